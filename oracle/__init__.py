@@ -1,0 +1,19 @@
+"""CPU oracle of the MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its Python
+binding) never imports it and shares no code with it.
+"""
+from .oracle import (  # noqa: F401
+    ORC_BF16,
+    ORC_F32,
+    ORC_FP8,
+    build,
+    e4m3_decode,
+    e4m3_encode,
+    fp8_quant_rows,
+    forward,
+    permute,
+    round_bf16,
+    route,
+)

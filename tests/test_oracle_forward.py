@@ -1,0 +1,203 @@
+"""Pins of the oracle's whole-layer forward: dense brute force over every
+expert (numpy/torch matmuls), textbook special cases (E=1 k=1 is a dense
+SwiGLU FFN; identical experts; k=E soft mixture; zero input) and the
+tolerance budget of the GPU-like fp32 pipeline."""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import ORC_BF16, ORC_F32, ORC_FP8
+
+
+def _bf16(a):
+    t = torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16), t.double().numpy()
+
+
+def _silu(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def _round_bf16_np(h):
+    """float64 -> nearest bf16 (ties to even), via frexp + numpy's
+    half-to-even rounding: independent of the oracle's C routine."""
+    m, e = np.frexp(h)  # h = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def _fp8_codes_torch(v32):
+    return torch.from_numpy(np.asarray(v32, np.float32)).clamp(-448, 448).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _fp8_vals(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _quant_rows_torch(v):
+    """1x128 groups: s = amax/448 (fp32), codes = e4m3(v/s) via torch; returns
+    the dequantised fp64 values."""
+    v = np.asarray(v, np.float32)
+    out = np.empty(v.shape, np.float64)
+    for g in range(v.shape[-1] // 128):
+        blk = v[..., g * 128:(g + 1) * 128]
+        amax = np.abs(blk).max(axis=-1, keepdims=True)
+        s = np.where(amax == 0, np.float32(1), (amax / np.float32(448)).astype(np.float32))
+        q = _fp8_codes_torch((blk / s).astype(np.float32))
+        out[..., g * 128:(g + 1) * 128] = _fp8_vals(q) * s.astype(np.float64)
+    return out
+
+
+def _make(T, d, f, E, k, act, wdt, seed, same_experts=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    gw = (rng.standard_normal((d, E)) * 0.02).astype(np.float32)
+    W = {n: (rng.standard_normal((E, K, N)) * 0.02).astype(np.float32)
+         for n, (K, N) in (("W1", (d, f)), ("W3", (d, f)), ("W2", (f, d)))}
+    if same_experts:
+        for n in W:
+            W[n][:] = W[n][0]
+    inp = {"scales": {}}
+    if act == ORC_BF16:
+        inp["x"], inp["xv"] = _bf16(x)
+        inp["gw"], inp["gwv"] = _bf16(gw)
+    else:
+        inp["x"], inp["xv"] = x, x.astype(np.float64)
+        inp["gw"], inp["gwv"] = gw, gw.astype(np.float64)
+    for n, w in W.items():
+        if wdt == ORC_FP8:
+            E_, K, N = w.shape
+            blocks = w.reshape(E_, K // 128, 128, N // 128, 128)
+            amax = np.abs(blocks).max(axis=(2, 4))
+            s = np.where(amax == 0, 1, amax / 448.0).astype(np.float32)
+            codes = _fp8_codes_torch(blocks / s[:, :, None, :, None]).reshape(E_, K, N)
+            inp[n] = codes
+            inp["scales"][n] = s
+            inp[n + "v"] = (_fp8_vals(codes).reshape(E_, K // 128, 128, N // 128, 128)
+                            * s[:, :, None, :, None]).reshape(E_, K, N)
+        elif wdt == ORC_BF16:
+            inp[n], inp[n + "v"] = _bf16(w)
+        else:
+            inp[n], inp[n + "v"] = w, w.astype(np.float64)
+    return inp
+
+
+def _run_oracle(inp, k, act, wdt, bias=None, tokens=None):
+    E = inp["W1"].shape[0]
+    sc = inp["scales"]
+    return oracle.forward(inp["x"], inp["gw"], bias, list(inp["W1"]), list(inp["W3"]),
+                          list(inp["W2"]), k, act, wdt, tokens=tokens,
+                          W1s=[sc["W1"][e] for e in range(E)] if sc else None,
+                          W3s=[sc["W3"][e] for e in range(E)] if sc else None,
+                          W2s=[sc["W2"][e] for e in range(E)] if sc else None)
+
+
+def _dense_experts(inp, act, wdt):
+    """y[e] for every token and expert, fp64 matmuls with the h rounding of
+    the layer's activation format applied by independent code."""
+    x = inp["xv"]
+    if wdt == ORC_FP8:
+        x = _quant_rows_torch(x.astype(np.float32))
+    ys = []
+    for e in range(inp["W1"].shape[0]):
+        h = _silu(x @ inp["W1v"][e]) * (x @ inp["W3v"][e])
+        if wdt == ORC_FP8:
+            h = _quant_rows_torch(h.astype(np.float32))
+        elif act == ORC_BF16:
+            h = _round_bf16_np(h)
+        else:
+            h = h.astype(np.float32).astype(np.float64)
+        ys.append(h @ inp["W2v"][e])
+    return np.stack(ys)  # [E][T][d]
+
+
+@pytest.mark.parametrize("act,wdt,d,f", [(ORC_F32, ORC_F32, 32, 48),
+                                         (ORC_BF16, ORC_BF16, 64, 64),
+                                         (ORC_BF16, ORC_FP8, 256, 128)])
+def test_forward_matches_dense_brute_force(act, wdt, d, f):
+    T, E, k = 24, 6, 2
+    inp = _make(T, d, f, E, k, act, wdt, seed=20 + act + wdt)
+    out, ids, w = _run_oracle(inp, k, act, wdt)
+    ys = _dense_experts(inp, act, wdt)
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            ref[t] += float(w[t, j]) * ys[ids[t, j], t]
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    assert np.abs(out - ref).max() <= 1e-9 * rms
+
+
+def test_e1_k1_is_dense_swiglu_ffn():
+    T, d, f = 16, 32, 64
+    inp = _make(T, d, f, 1, 1, ORC_F32, ORC_F32, seed=30)
+    out, ids, w = _run_oracle(inp, 1, ORC_F32, ORC_F32)
+    assert (ids == 0).all() and (w == 1.0).all()
+    x = torch.from_numpy(inp["xv"])
+    W1, W3, W2 = (torch.from_numpy(inp[n + "v"][0]) for n in ("W1", "W3", "W2"))
+    h = torch.nn.functional.silu(x @ W1) * (x @ W3)
+    ref = (h.float().double() @ W2).numpy()
+    assert np.abs(out - ref).max() <= 1e-12 * math.sqrt(float(np.mean(ref ** 2)))
+
+
+def test_identical_experts_give_the_ffn_for_any_routing():
+    T, d, f, E, k = 20, 32, 32, 5, 3
+    inp = _make(T, d, f, E, k, ORC_F32, ORC_F32, seed=31, same_experts=True)
+    out, _, _ = _run_oracle(inp, k, ORC_F32, ORC_F32)
+    x = inp["xv"]
+    h = (_silu(x @ inp["W1v"][0]) * (x @ inp["W3v"][0])).astype(np.float32).astype(np.float64)
+    ref = h @ inp["W2v"][0]
+    # the only difference is sum(g) = 1 up to fp32 rounding of each g
+    assert np.abs(out - ref).max() <= 4e-7 * np.abs(ref).max()
+
+
+def test_k_equals_E_is_full_softmax_mixture():
+    T, d, f, E = 12, 32, 32, 4
+    inp = _make(T, d, f, E, E, ORC_F32, ORC_F32, seed=32)
+    out, _, _ = _run_oracle(inp, E, ORC_F32, ORC_F32)
+    logits, _, _ = oracle.route(inp["x"], inp["gw"], None, E, ORC_F32)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    ys = _dense_experts(inp, ORC_F32, ORC_F32)
+    ref = np.einsum("te,etd->td", p, ys)
+    assert np.abs(out - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_zero_input_gives_zero_output():
+    T, d, f, E, k = 8, 64, 64, 4, 2
+    inp = _make(T, d, f, E, k, ORC_BF16, ORC_BF16, seed=33)
+    inp["x"][:] = 0
+    out, ids, w = _run_oracle(inp, k, ORC_BF16, ORC_BF16)
+    assert not out.any() and (ids == [0, 1]).all() and (w == 0.5).all()
+
+
+def test_token_subset_equals_full_run():
+    T, d, f, E, k = 30, 64, 64, 8, 2
+    inp = _make(T, d, f, E, k, ORC_BF16, ORC_BF16, seed=34)
+    full, ids, _ = _run_oracle(inp, k, ORC_BF16, ORC_BF16)
+    sub = np.array([29, 3, 3, 17], np.int64)
+    part, ids2, _ = _run_oracle(inp, k, ORC_BF16, ORC_BF16, tokens=sub)
+    assert np.array_equal(part, full[sub]) and np.array_equal(ids2, ids[sub])
+
+
+def test_tolerance_budget_of_fp32_accumulation_pipeline():
+    # A GPU-like pipeline (fp32 accumulation, h rounded to bf16, fp32 y,
+    # fp32 combine) stays well inside the 1e-2 x RMS bar against the oracle,
+    # while skipping the h rounding in the reference would cost about 1e-2.
+    T, d, f, E, k = 128, 512, 512, 4, 2
+    inp = _make(T, d, f, E, k, ORC_BF16, ORC_BF16, seed=35)
+    out, ids, w = _run_oracle(inp, k, ORC_BF16, ORC_BF16)
+    x = torch.from_numpy(inp["xv"]).float()
+    gpu = torch.zeros(T, d)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            a = x[t] @ torch.from_numpy(inp["W1v"][e]).float()
+            b = x[t] @ torch.from_numpy(inp["W3v"][e]).float()
+            h = (torch.nn.functional.silu(a) * b).bfloat16().float()
+            gpu[t] += float(w[t, j]) * (h @ torch.from_numpy(inp["W2v"][e]).float())
+    rms = math.sqrt(float(np.mean(out ** 2)))
+    err = float(np.abs(gpu.double().numpy() - out).max()) / rms
+    assert err < 5e-3
