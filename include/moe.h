@@ -1,0 +1,200 @@
+/*
+ * moe.h -- C ABI of the MI355X MoE layer forward library (libmoe.so).
+ *
+ * One GPU runs a whole Mixture-of-Experts layer forward:
+ *   softmax gate + top-k routing -> expert histogram and prefix-sum
+ *   permutation -> grouped SwiGLU expert GEMMs -> gate-weighted combine.
+ * The stage list is the one the FlashMoE Kernel page gives in its opening
+ * paragraph (gate -> dispatch -> expert FFN -> combine), run here inside one
+ * GPU with no exchange between devices.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises the host inside a call, except
+ *    where an entry point says otherwise.
+ *  - Every call enqueues its kernels on `stream` (NULL = the default stream)
+ *    and returns immediately; outputs are valid once the caller synchronises
+ *    the stream.
+ *  - Arguments are checked before anything is enqueued.  On any error nothing
+ *    is launched and no output is touched.  No C++ exception crosses the ABI.
+ *  - Matrices are row-major and contiguous.  bf16 is IEEE bfloat16 storage
+ *    (the upper half of an fp32); FP8 is OCP E4M3FN (max 448, no infinity).
+ *  - No entry point reads a size back from the device, so a call can be
+ *    captured into a HIP graph (the reason given on the FlashMoE Kernel page,
+ *    "Problem" section, for why launch storms cannot simply be graphed is a
+ *    host-sized pipeline; this one is device-sized).
+ *  - Calls sharing one workspace must not overlap in time.
+ *
+ * Numerics (each choice is a reading where the pages are silent):
+ *  - Router logits are fp32: acc = +0.0f, acc = fmaf(x[t][i], gate_w[i][e],
+ *    acc) for i = 0 .. d-1 ascending, then acc + bias[e] as one fp32 add.
+ *  - Top-k is taken on the logits; order is descending logit, equal logits
+ *    ranked by lower expert index.  Weights are the softmax over the k
+ *    selected logits (the renormalised full softmax), computed in fp64 and
+ *    stored fp32.
+ *  - Slots are ordered by expert, and inside an expert by q = t*k + j.
+ *  - SwiGLU expert: h = SiLU(x W1) * (x W3), SiLU(a) = a / (1 + e^-a),
+ *    y = h W2, fp32 accumulation; h is rounded to the activation format
+ *    (fp32, bf16 RNE, or FP8 1x128 groups) before W2; y stays fp32.
+ *  - FP8 groups: activations per 1x128 group along the contraction axis with
+ *    scale s = amax / 448 (1 when amax == 0) and code e4m3_rne_sat(v / s)
+ *    (both quotients fp32 IEEE); weights per 128x128 (K, N) block.
+ *  - Combine: out[t] = sum_{j = 0 .. k-1} w[t][j] * y[slot(t, j)], fp32, in j
+ *    order, then rounded (RNE) to out_dtype.  No floating-point atomics are
+ *    used anywhere, so every output is bitwise reproducible run to run.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,          /* null pointer, bad size, bad dtype   */
+    MOE_ERR_UNSUPPORTED = 2,          /* valid but not implemented shape     */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes < moe_workspace_size()     */
+    MOE_ERR_HIP = 4                   /* a HIP launch/runtime call failed    */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_FP8_E4M3 = 2
+} moe_dtype;
+
+/* Problem description.  Sizes: T tokens, hidden d, expert intermediate f,
+ * E experts, top_k experts per token (1 <= top_k <= E <= 1024).
+ *   act_dtype: x and gate_w -- MOE_F32 or MOE_BF16.
+ *   w_dtype:   W1, W3, W2   -- MOE_F32 (needs act_dtype F32), MOE_BF16 (needs
+ *              act_dtype BF16) or MOE_FP8_E4M3 (needs act_dtype BF16, d and f
+ *              multiples of 128).
+ *   out_dtype: MOE_F32 or MOE_BF16.
+ *   block_m:   rows per expert tile of the grouped GEMMs; 0 picks it from the
+ *              expected tokens per expert T*top_k/E (the serving-regime choice
+ *              of the MegaMoE-vs-MoE-systems page, section 2.5, re-tuned for
+ *              MFMA tiles).  Otherwise one of 16, 32, 64, 128.
+ * bf16/FP8 layers need d % 64 == 0 and f % 64 == 0; fp32 layers need
+ * d % 16 == 0 and f % 16 == 0. */
+typedef struct {
+    int64_t T, d, f;
+    int32_t E, top_k;
+    int32_t act_dtype;
+    int32_t w_dtype;
+    int32_t out_dtype;
+    int32_t block_m;
+} moe_problem;
+
+/* Optional device outputs filled from inside moe_forward, so that the routing
+ * the fused call actually used can be compared with moe_route/moe_permute.
+ * Any pointer may be NULL.  Sizes as in moe_route / moe_permute.
+ * stage_events: caller-created HIP events (or NULL); event i is recorded on
+ * the call's stream at stage boundary i: 0 start, 1 after the gate, 2 after
+ * the FP8 quantisation of x, 3 after histogram/scan/scatter, 4 after the
+ * W1/W3 GEMM, 5 after the W2 GEMM, 6 after the combine.  Used to time each
+ * kernel inside the whole-layer call. */
+#define MOE_NUM_STAGE_EVENTS 7
+typedef struct {
+    int32_t *topk_ids;    /* [T*k]  */
+    float *topk_w;        /* [T*k]  */
+    int32_t *counts;      /* [E]    */
+    int32_t *offsets;     /* [E+1]  */
+    int32_t *slot_token;  /* [T*k]  */
+    int32_t *slot_k;      /* [T*k]  */
+    int32_t *token_slot;  /* [T*k]  */
+    hipEvent_t stage_events[MOE_NUM_STAGE_EVENTS];
+} moe_debug;
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_status_string(moe_status s);
+
+/* The HIP error code behind the last MOE_ERR_HIP on the calling thread. */
+int moe_last_hip_error(void);
+
+/* Bytes of device workspace that moe_route (when logits == NULL),
+ * moe_permute and moe_forward need for this problem.  A pure function of the
+ * problem, never of the routing: the dropless worst case of T*k slot rows
+ * (the worst-case pool of the MegaMoE-vs-MoE-systems page, section 2.6, with
+ * one rank), plus tables, tile maps and FP8 scales. */
+moe_status moe_workspace_size(const moe_problem *p, size_t *bytes);
+
+/* Gate (FlashMoE Kernel page, opening paragraph: the first stage).
+ *   x        [T][d]   act_dtype
+ *   gate_w   [d][E]   act_dtype
+ *   bias     [E]      fp32, or NULL (added to every logit of expert e)
+ *   logits   [T][E]   fp32 output, or NULL (then kept in the workspace)
+ *   topk_ids [T][k]   int32 output, descending logit, ties to lower index
+ *   topk_w   [T][k]   fp32 output, renormalised softmax weights
+ *   ws/ws_bytes       workspace; may be NULL/0 when logits != NULL. */
+moe_status moe_route(const moe_problem *p, const void *x, const void *gate_w,
+                     const float *bias, float *logits, int32_t *topk_ids,
+                     float *topk_w, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Dispatch bookkeeping: atomic-free expert histogram, exclusive scan and
+ * stable scatter (slot order by expert, then q = t*k + j).  The per-slot
+ * source record (token, k-slot) is the one-GPU form of the source metadata
+ * of the MegaMoE-vs-MoE-systems page, section 2.4.
+ *   topk_ids   [T*k] int32 input, each in [0, E)  (out-of-range ids are
+ *              undefined behaviour on the device; they are not detected)
+ *   counts     [E]   rows per expert
+ *   offsets    [E+1] exclusive scan of counts (offsets[E] == T*k)
+ *   slot_token [T*k] source token of each slot
+ *   slot_k     [T*k] source top-k index of each slot
+ *   token_slot [T*k] inverse: slot of (t, j) at index t*k + j
+ *   ws/ws_bytes workspace of at least moe_workspace_size(). */
+moe_status moe_permute(const moe_problem *p, const int32_t *topk_ids,
+                       int32_t *counts, int32_t *offsets, int32_t *slot_token,
+                       int32_t *slot_k, int32_t *token_slot, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* FP8 1x128 group quantisation of a bf16 [rows][cols] matrix (cols % 128 ==
+ * 0): q [rows][cols] E4M3FN codes, s [rows][cols/128] fp32 scales, as the FP8
+ * layer applies it to x before the expert GEMMs. */
+moe_status moe_quantize_fp8(int64_t rows, int64_t cols, const void *x_bf16,
+                            uint8_t *q, float *s, hipStream_t stream);
+
+/* Bytes of each expert-weight tensor in the layout moe_forward reads
+ * (element size of w_dtype times E*d*f). */
+moe_status moe_weight_bytes(const moe_problem *p, size_t *bytes);
+
+/* One-time weight re-layout (untimed, done when weights are loaded): each
+ * expert matrix given as [K][N] (W1, W3: [d][f]; W2: [f][d], the stated
+ * layouts) is written as its transpose [N][K], so that the contraction axis
+ * is contiguous for the MFMA operand loads.  src and dst must not overlap.
+ * elem_bytes is 4 (fp32), 2 (bf16) or 1 (FP8 codes); E matrices of K x N. */
+moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
+                           const void *src, void *dst, hipStream_t stream);
+
+/* Whole layer forward.
+ *   x       [T][d]       act_dtype
+ *   gate_w  [d][E]       act_dtype
+ *   bias    [E]          fp32 or NULL
+ *   W1t,W3t [E][f][d]    w_dtype, packed by moe_pack_weight (gate, up)
+ *   W2t     [E][d][f]    w_dtype, packed by moe_pack_weight (down)
+ *   W1s,W3s [E][d/128][f/128] fp32 block scales (FP8 only, else NULL)
+ *   W2s     [E][f/128][d/128] fp32 block scales (FP8 only, else NULL)
+ *   out     [T][d]       out_dtype
+ *   ws/ws_bytes          workspace of at least moe_workspace_size()
+ *   dbg                  NULL, or device buffers receiving the routing used.
+ * Kernels enqueued: route (logits, top-k), FP8 quantisation of x (FP8 only),
+ * histogram, scan + tile map, scatter, grouped W1/W3 GEMM + SwiGLU, grouped
+ * W2 GEMM, combine. */
+moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
+                       const float *bias, const void *W1t, const void *W3t,
+                       const void *W2t, const float *W1s, const float *W3s,
+                       const float *W2s, void *out, void *ws, size_t ws_bytes,
+                       const moe_debug *dbg, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,209 @@
+"""ctypes binding of libmoe.so -- argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, passes their
+device pointers and the current HIP stream to the C ABI of include/moe.h, and
+raises on a non-OK status.  Nothing here computes any part of the layer; if
+libmoe.so is missing the import fails loudly (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+
+EXPORTS = ["moe_status_string", "moe_last_hip_error", "moe_workspace_size", "moe_route",
+           "moe_permute", "moe_quantize_fp8", "moe_weight_bytes", "moe_pack_weight",
+           "moe_forward"]
+
+
+class MoEProblem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64),
+                ("E", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("block_m", ctypes.c_int32)]
+
+
+NUM_STAGE_EVENTS = 7
+DEBUG_BUFFERS = ("topk_ids", "topk_w", "counts", "offsets", "slot_token", "slot_k",
+                 "token_slot")
+
+
+class MoEDebug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in DEBUG_BUFFERS] + [
+        ("stage_events", ctypes.c_void_p * NUM_STAGE_EVENTS)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn, code, hip):
+        self.code = code
+        self.hip = hip
+        super().__init__(f"{fn} -> {STATUS.get(code, code)}"
+                         + (f" (hip error {hip})" if code == 4 else ""))
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoe.so (built in-tree by build()); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run __graft_entry__.build() or "
+                          "python -m mixture_experts_layer_softmax_amd.build")
+    lib = ctypes.CDLL(path)
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    PP = ctypes.POINTER(MoEProblem)
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_hip_error.restype = ctypes.c_int
+    lib.moe_workspace_size.argtypes = [PP, ctypes.POINTER(S)]
+    lib.moe_weight_bytes.argtypes = [PP, ctypes.POINTER(S)]
+    lib.moe_route.argtypes = [PP, P, P, P, P, P, P, P, S, P]
+    lib.moe_permute.argtypes = [PP, P, P, P, P, P, P, P, S, P]
+    lib.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, P, P, P, P]
+    lib.moe_pack_weight.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int32, P, P, P]
+    lib.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, S,
+                                ctypes.POINTER(MoEDebug), P]
+    for fn in EXPORTS:
+        if fn not in ("moe_status_string", "moe_last_hip_error"):
+            getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise MoEError(fn, rc, load().moe_last_hip_error())
+
+
+def problem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m=0) -> MoEProblem:
+    return MoEProblem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m)
+
+
+def problem_of(cfg, T=None, block_m=0, out_dtype=None) -> MoEProblem:
+    return problem(cfg.T if T is None else T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act_dtype,
+                   cfg.w_dtype, cfg.out_dtype if out_dtype is None else out_dtype, block_m)
+
+
+def workspace_size(p: MoEProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_size", load().moe_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def weight_bytes(p: MoEProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_weight_bytes", load().moe_weight_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(p: MoEProblem, device="cuda") -> torch.Tensor:
+    return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def moe_route(p, x, gate_w, bias, logits, topk_ids, topk_w, ws=None, stream=None):
+    rc = load().moe_route(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(logits),
+                          _p(topk_ids), _p(topk_w), _p(ws),
+                          0 if ws is None else ws.numel(), _stream(stream))
+    _check("moe_route", rc)
+
+
+def moe_permute(p, topk_ids, counts, offsets, slot_token, slot_k, token_slot, ws,
+                stream=None):
+    rc = load().moe_permute(ctypes.byref(p), _p(topk_ids), _p(counts), _p(offsets),
+                            _p(slot_token), _p(slot_k), _p(token_slot), _p(ws), ws.numel(),
+                            _stream(stream))
+    _check("moe_permute", rc)
+
+
+def moe_quantize_fp8(x_bf16, q, s, stream=None):
+    rows, cols = x_bf16.shape
+    rc = load().moe_quantize_fp8(rows, cols, _p(x_bf16), _p(q), _p(s), _stream(stream))
+    _check("moe_quantize_fp8", rc)
+
+
+def moe_pack_weight(src, dst, stream=None):
+    """src [E][K][N] -> dst [E][N][K] (any 1/2/4-byte element type)."""
+    E, K, N = src.shape
+    rc = load().moe_pack_weight(E, K, N, src.element_size(), _p(src), _p(dst),
+                                _stream(stream))
+    _check("moe_pack_weight", rc)
+
+
+def moe_forward(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, dbg=None,
+                stream=None):
+    dbg_s = None
+    if dbg is not None:
+        dbg_s = MoEDebug(*[None if dbg.get(n) is None else dbg[n].data_ptr()
+                           for n in DEBUG_BUFFERS])
+        for i, ev in enumerate(dbg.get("stage_events") or []):
+            dbg_s.stage_events[i] = ev
+    rc = load().moe_forward(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(W1t), _p(W3t),
+                            _p(W2t), _p(W1s), _p(W3s), _p(W2s), _p(out), _p(ws), ws.numel(),
+                            None if dbg_s is None else ctypes.byref(dbg_s), _stream(stream))
+    _check("moe_forward", rc)
+
+
+# ---------------------------------------------------------------------------
+# convenience wrappers over the calls above (tensor allocation + marshalling)
+# ---------------------------------------------------------------------------
+
+def pack_weights(inp: dict, stream=None) -> dict:
+    """One-time re-layout of W1/W3/W2 ([E][K][N] -> [E][N][K]) on the GPU."""
+    out = {}
+    for name in ("W1", "W3", "W2"):
+        w = inp[name]
+        E, K, N = w.shape
+        dst = torch.empty((E, N, K), dtype=w.dtype, device=w.device)
+        moe_pack_weight(w, dst, stream)
+        out[name + "t"] = dst
+    for name in ("W1s", "W3s", "W2s"):
+        out[name] = inp.get(name)
+    return out
+
+
+def out_tensor(cfg, T=None, device="cuda", out_dtype=None):
+    od = cfg.out_dtype if out_dtype is None else out_dtype
+    return torch.empty((cfg.T if T is None else T, cfg.d),
+                       dtype=torch.float32 if od == MOE_F32 else torch.bfloat16, device=device)
+
+
+def forward(cfg, inp: dict, packed: dict, out=None, ws=None, dbg=None, out_dtype=None,
+            block_m=0, stream=None):
+    """Whole-layer forward of cfg on resident inputs; returns the output tensor."""
+    T = inp["x"].shape[0]
+    p = problem_of(cfg, T=T, block_m=block_m, out_dtype=out_dtype)
+    if out is None:
+        out = out_tensor(cfg, T=T, device=inp["x"].device, out_dtype=out_dtype)
+    if ws is None:
+        ws = alloc_workspace(p, inp["x"].device)
+    moe_forward(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"], packed["W3t"],
+                packed["W2t"], packed.get("W1s"), packed.get("W3s"), packed.get("W2s"), out,
+                ws, dbg=dbg, stream=stream)
+    return out

@@ -1,0 +1,335 @@
+// api.cpp -- the C ABI of libmoe.so: argument checks, workspace layout and
+// the launch sequence of the layer forward.  See include/moe.h for the
+// contract of every entry point.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int esize(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
+
+// Tile height from the expected rows per expert, T*k/E: the serving-regime
+// choice of the MegaMoE-vs-MoE-systems page (section 2.5), re-tuned for
+// 16-row MFMA fragments and four 64-wide waves per workgroup.
+int pick_bm(const moe_problem& p) {
+  if (p.block_m) return p.block_m;
+  const double r = static_cast<double>(p.T) * p.top_k / p.E;
+  if (r <= 24.0) return 16;
+  if (r <= 48.0) return 32;
+  if (r <= 160.0) return 64;
+  return 128;
+}
+
+bool valid_problem(const moe_problem* p) {
+  if (!p) return false;
+  if (p->T < 0 || p->d <= 0 || p->f <= 0) return false;
+  if (p->E < 1 || p->E > 1024 || p->top_k < 1 || p->top_k > p->E) return false;
+  if (p->T > (1ll << 31) / 1024 || p->T * p->top_k > (1ll << 30)) return false;
+  const bool ok_types = (p->act_dtype == MOE_F32 && p->w_dtype == MOE_F32) ||
+                        (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_BF16) ||
+                        (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_FP8_E4M3);
+  if (!ok_types) return false;
+  if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return false;
+  if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
+      p->block_m != 128)
+    return false;
+  return true;
+}
+
+// Shapes the kernels support (valid but unsupported -> MOE_ERR_UNSUPPORTED).
+bool supported_shape(const moe_problem* p) {
+  const int64_t m = p->w_dtype == MOE_F32 ? 32 : (p->w_dtype == MOE_BF16 ? 64 : 128);
+  return p->d % m == 0 && p->f % m == 0 && p->d <= (1ll << 20) && p->f <= (1ll << 20);
+}
+
+struct Layout {
+  size_t logits, ids, w, table, counts, offsets, slot_token, slot_k, token_slot;
+  size_t tm_e, tm_row0, tm_rows, tm_misc;
+  size_t xq, sx, hs, h, y;
+  size_t total;
+  int bm;
+  int64_t max_mtiles;
+};
+
+Layout make_layout(const moe_problem& p) {
+  Layout L{};
+  const int64_t n = p.T * p.top_k;
+  const int64_t nchunk = ceil_div(n, moe::kPermuteChunk);
+  L.bm = pick_bm(p);
+  L.max_mtiles = (n + static_cast<int64_t>(p.E) * (L.bm - 1)) / L.bm + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + std::max<size_t>(bytes, 1));
+    return at;
+  };
+  L.logits = take(sizeof(float) * p.T * p.E);
+  L.ids = take(sizeof(int32_t) * n);
+  L.w = take(sizeof(float) * n);
+  L.table = take(sizeof(int32_t) * nchunk * p.E);
+  L.counts = take(sizeof(int32_t) * p.E);
+  L.offsets = take(sizeof(int32_t) * (p.E + 1));
+  L.slot_token = take(sizeof(int32_t) * n);
+  L.slot_k = take(sizeof(int32_t) * n);
+  L.token_slot = take(sizeof(int32_t) * n);
+  L.tm_e = take(sizeof(int32_t) * L.max_mtiles);
+  L.tm_row0 = take(sizeof(int32_t) * L.max_mtiles);
+  L.tm_rows = take(sizeof(int32_t) * L.max_mtiles);
+  L.tm_misc = take(sizeof(int32_t) * 4);
+  const bool fp8 = p.w_dtype == MOE_FP8_E4M3;
+  L.xq = take(fp8 ? static_cast<size_t>(p.T) * p.d : 0);
+  L.sx = take(fp8 ? sizeof(float) * p.T * (p.d / 128) : 0);
+  L.hs = take(fp8 ? sizeof(float) * n * (p.f / 128) : 0);
+  L.h = take(static_cast<size_t>(n) * p.f * esize(p.w_dtype == MOE_FP8_E4M3 ? MOE_FP8_E4M3 : p.act_dtype));
+  L.y = take(sizeof(float) * n * p.d);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+moe::TileMap tile_map(void* ws, const Layout& L) {
+  moe::TileMap tm;
+  tm.e = at<int32_t>(ws, L.tm_e);
+  tm.row0 = at<int32_t>(ws, L.tm_row0);
+  tm.rows = at<int32_t>(ws, L.tm_rows);
+  tm.n_mtiles = at<int32_t>(ws, L.tm_misc);
+  tm.queue = at<int32_t>(ws, L.tm_misc) + 1;
+  return tm;
+}
+
+moe_status hip_status() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip = static_cast<int>(e);
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status from_code(int code) {
+  if (code != 0) {
+    g_last_hip = code;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or type combination";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int moe_last_hip_error(void) { return g_last_hip; }
+
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  if (!valid_problem(p) || !bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = make_layout(*p).total;
+  return MOE_OK;
+}
+
+moe_status moe_weight_bytes(const moe_problem* p, size_t* bytes) {
+  if (!valid_problem(p) || !bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = static_cast<size_t>(p->E) * p->d * p->f * esize(p->w_dtype);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_problem* p, const void* x, const void* gate_w, const float* bias,
+                     float* logits, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
+  if (p->T == 0) return MOE_OK;
+  if (!x || !gate_w || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  float* lg = logits;
+  if (!lg) {
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(*p);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    lg = at<float>(ws, L.logits);
+  }
+  (void)hipGetLastError();
+  moe::launch_logits(x, gate_w, bias, lg, static_cast<int>(p->T), static_cast<int>(p->d), p->E,
+                     p->act_dtype == MOE_BF16, stream);
+  moe::launch_topk(lg, topk_ids, topk_w, static_cast<int>(p->T), p->E, p->top_k, stream);
+  return hip_status();
+}
+
+moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* slot_token, int32_t* slot_k,
+                       int32_t* token_slot, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
+  if (!counts || !offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!topk_ids || !slot_token || !slot_k || !token_slot))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*p);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  (void)hipGetLastError();
+  moe::launch_permute(topk_ids, static_cast<int>(p->T), p->top_k, p->E, L.bm,
+                      at<int32_t>(ws, L.table), counts, offsets, slot_token, slot_k, token_slot,
+                      tile_map(ws, L), stream);
+  return hip_status();
+}
+
+moe_status moe_quantize_fp8(int64_t rows, int64_t cols, const void* x_bf16, uint8_t* q,
+                            float* s, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x_bf16 || !q || !s) return MOE_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  moe::launch_quant_fp8(static_cast<const uint16_t*>(x_bf16), rows, cols, q, s, stream);
+  return hip_status();
+}
+
+moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes, const void* src,
+                           void* dst, hipStream_t stream) {
+  if (E < 1 || K < 1 || N < 1 || !src || !dst) return MOE_ERR_INVALID_ARG;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return MOE_ERR_INVALID_ARG;
+  if (K > (1ll << 24) || N > (1ll << 24)) return MOE_ERR_UNSUPPORTED;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t len = static_cast<uintptr_t>(E) * K * N * elem_bytes;
+  if (a < b + len && b < a + len) return MOE_ERR_INVALID_ARG;  // overlap
+  (void)hipGetLastError();
+  moe::launch_pack(E, K, N, elem_bytes, src, dst, stream);
+  return hip_status();
+}
+
+moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, const float* bias,
+                       const void* W1t, const void* W3t, const void* W2t, const float* W1s,
+                       const float* W3s, const float* W2s, void* out, void* ws, size_t ws_bytes,
+                       const moe_debug* dbg, hipStream_t stream) {
+  if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
+  if (!supported_shape(p)) return MOE_ERR_UNSUPPORTED;
+  if (p->T == 0) return MOE_OK;
+  if (!x || !gate_w || !W1t || !W3t || !W2t || !out || !ws) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = p->w_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!W1s || !W3s || !W2s)) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*p);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  const int T = static_cast<int>(p->T), d = static_cast<int>(p->d);
+  const int E = p->E, k = p->top_k;
+  const int n = T * k;
+  float* logits = at<float>(ws, L.logits);
+  int32_t* ids = at<int32_t>(ws, L.ids);
+  float* w = at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* slot_token = at<int32_t>(ws, L.slot_token);
+  int32_t* slot_k = at<int32_t>(ws, L.slot_k);
+  int32_t* token_slot = at<int32_t>(ws, L.token_slot);
+  const moe::TileMap tm = tile_map(ws, L);
+  const int hdt = fp8 ? moe::kFP8 : (p->act_dtype == MOE_BF16 ? moe::kBF16 : moe::kF32);
+  const int gdt = hdt;
+
+  auto mark = [&](int i) {
+    if (dbg && dbg->stage_events[i]) (void)hipEventRecord(dbg->stage_events[i], stream);
+  };
+  (void)hipGetLastError();
+  mark(0);
+  // 1. gate
+  moe::launch_logits(x, gate_w, bias, logits, T, d, E, p->act_dtype == MOE_BF16, stream);
+  moe::launch_topk(logits, ids, w, T, E, k, stream);
+  mark(1);
+  // 2. FP8 activations
+  if (fp8)
+    moe::launch_quant_fp8(static_cast<const uint16_t*>(x), p->T, p->d, at<uint8_t>(ws, L.xq),
+                          at<float>(ws, L.sx), stream);
+  mark(2);
+  // 3. histogram, scan + tile map, scatter
+  moe::launch_permute(ids, T, k, E, L.bm, at<int32_t>(ws, L.table), counts, offsets, slot_token,
+                      slot_k, token_slot, tm, stream);
+  mark(3);
+  moe_status st = hip_status();
+  if (st != MOE_OK) return st;
+
+  // 4. W1/W3 + SwiGLU
+  moe::GemmArgs g1{};
+  g1.A = fp8 ? at<uint8_t>(ws, L.xq) : static_cast<const uint8_t*>(x);
+  g1.a_row_bytes = p->d * esize(fp8 ? MOE_FP8_E4M3 : p->act_dtype);
+  g1.gather = slot_token;
+  g1.sa = fp8 ? at<float>(ws, L.sx) : nullptr;
+  g1.B0 = static_cast<const uint8_t*>(W1t);
+  g1.B1 = static_cast<const uint8_t*>(W3t);
+  g1.sb0 = W1s;
+  g1.sb1 = W3s;
+  g1.K = p->d;
+  g1.N = p->f;
+  g1.C = at<uint8_t>(ws, L.h);
+  g1.sc = fp8 ? at<float>(ws, L.hs) : nullptr;
+  g1.tm = tm;
+  g1.n_tiles_n = static_cast<int>(ceil_div(2 * p->f, moe::gemm_tile_n(1, gdt, L.bm)));
+  g1.queue_idx = 0;
+  st = from_code(moe::launch_gemm(1, gdt, L.bm, g1, stream));
+  if (st != MOE_OK) return st;
+  mark(4);
+
+  // 5. W2
+  moe::GemmArgs g2{};
+  g2.A = at<uint8_t>(ws, L.h);
+  g2.a_row_bytes = p->f * esize(fp8 ? MOE_FP8_E4M3 : p->act_dtype);
+  g2.gather = nullptr;
+  g2.sa = fp8 ? at<float>(ws, L.hs) : nullptr;
+  g2.B0 = static_cast<const uint8_t*>(W2t);
+  g2.B1 = nullptr;
+  g2.sb0 = W2s;
+  g2.sb1 = nullptr;
+  g2.K = p->f;
+  g2.N = p->d;
+  g2.C = at<uint8_t>(ws, L.y);
+  g2.sc = nullptr;
+  g2.tm = tm;
+  g2.n_tiles_n = static_cast<int>(ceil_div(p->d, moe::gemm_tile_n(2, gdt, L.bm)));
+  g2.queue_idx = 1;
+  st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));
+  if (st != MOE_OK) return st;
+  mark(5);
+
+  // 6. combine
+  moe::launch_combine(at<float>(ws, L.y), w, token_slot, out, T, d, k,
+                      p->out_dtype == MOE_BF16, stream);
+  mark(6);
+
+  if (dbg) {
+    auto cp = [&](void* dst, const void* src, size_t bytes) {
+      if (dst) (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream);
+    };
+    cp(dbg->topk_ids, ids, sizeof(int32_t) * n);
+    cp(dbg->topk_w, w, sizeof(float) * n);
+    cp(dbg->counts, counts, sizeof(int32_t) * E);
+    cp(dbg->offsets, offsets, sizeof(int32_t) * (E + 1));
+    cp(dbg->slot_token, slot_token, sizeof(int32_t) * n);
+    cp(dbg->slot_k, slot_k, sizeof(int32_t) * n);
+    cp(dbg->token_slot, token_slot, sizeof(int32_t) * n);
+  }
+  return hip_status();
+}
+
+}  // extern "C"

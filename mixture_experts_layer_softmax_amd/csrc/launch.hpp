@@ -1,0 +1,65 @@
+// launch.hpp -- host-side launch wrappers of the HIP kernels and the small
+// structs they share with api.cpp.  Internal to libmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kPermuteChunk = 4096;  // (token, k) pairs per histogram chunk
+
+// Expert m-tile map written by the scan kernel: tile i covers slots
+// [row0[i], row0[i] + rows[i]) of expert e[i].  n_mtiles is the number of
+// valid entries; queue[2] are the work-queue counters of the two GEMMs.
+struct TileMap {
+  int32_t* e;
+  int32_t* row0;
+  int32_t* rows;
+  int32_t* n_mtiles;
+  int32_t* queue;
+};
+
+// dtype codes (same values as moe_dtype)
+constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2;
+
+struct GemmArgs {
+  // activation operand: rows of K elements
+  const uint8_t* A;
+  int64_t a_row_bytes;
+  const int32_t* gather;  // row index table (slot -> token), or null (row = slot)
+  const float* sa;        // FP8: [rows][K/128] scales of A rows
+  // weight operand(s): [E][N][K] (contraction axis contiguous)
+  const uint8_t* B0;      // W1t (phase 1) or W2t (phase 2)
+  const uint8_t* B1;      // W3t (phase 1)
+  const float* sb0;       // FP8: [E][K/128][N/128]
+  const float* sb1;
+  int64_t K;              // contraction length (elements)
+  int64_t N;              // output columns: f (phase 1) or d (phase 2)
+  // outputs
+  uint8_t* C;             // h [slots][f] (phase 1) or Y fp32 [slots][d] (phase 2)
+  float* sc;              // FP8 phase 1: [slots][f/128] scales of h
+  TileMap tm;
+  int n_tiles_n;          // column tiles per m-tile
+  int queue_idx;
+};
+
+void launch_logits(const void* x, const void* gate_w, const float* bias, float* logits,
+                   int T, int d, int E, bool bf16, hipStream_t s);
+void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
+                 hipStream_t s);
+void launch_permute(const int32_t* ids, int T, int k, int E, int bm, int32_t* table,
+                    int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_k,
+                    int32_t* token_slot, TileMap tm, hipStream_t s);
+void launch_quant_fp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
+                      hipStream_t st);
+// Grouped GEMMs.  bm = tile height; returns a hipError_t.
+int launch_gemm(int phase, int dtype, int bm, const GemmArgs& a, hipStream_t s);
+// Column tiles per m-tile for a phase (depends on the kernel variant).
+int gemm_tile_n(int phase, int dtype, int bm);
+void launch_combine(const float* Y, const float* w, const int32_t* token_slot, void* out,
+                    int T, int d, int k, bool out_bf16, hipStream_t s);
+void launch_pack(int E, int64_t K, int64_t N, int elem_bytes, const void* src, void* dst,
+                 hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,155 @@
+// permute.hip -- dispatch bookkeeping inside one GPU: expert histogram,
+// exclusive scan, stable scatter of (token, k-slot) pairs to expert-ordered
+// slots, and the expert tile map of the grouped GEMMs.
+//
+// The per-slot (token, k-slot) record is the one-device form of the source
+// metadata every pool slot carries on the MegaMoE-vs-MoE-systems page
+// (section 2.4); the layer stays dropless (section 2.6): every pair gets a
+// slot and padding exists only in the tile map, never in memory (the local
+// "in-place padding" idea of the FlashMoE Kernel page, Communication section).
+//
+// No global atomics: each chunk of kChunk consecutive pairs is counted by one
+// wavefront into a [chunks x E] table; one workgroup scans it in (expert,
+// chunk) order; the scatter wavefront of each chunk re-ranks its pairs with
+// ballots so equal experts keep increasing q = t*k + j order.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+// 64-bit mask of lanes in this wave holding the same value of `e` (bits 0..nb-1).
+__device__ __forceinline__ uint64_t match_lanes(int e, int nbits, bool active) {
+  uint64_t m = __ballot(active);
+  for (int b = 0; b < nbits; ++b) {
+    uint64_t ones = __ballot(active && ((e >> b) & 1));
+    m &= ((e >> b) & 1) ? ones : ~ones;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(64) void hist_kernel(const int32_t* __restrict__ ids, int n,
+                                                  int E, int32_t* __restrict__ table) {
+  extern __shared__ int32_t cnt[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __syncthreads();
+  const int q0 = blockIdx.x * kPermuteChunk;
+  const int q1 = min(n, q0 + kPermuteChunk);
+  for (int q = q0 + lane; q < q1; q += 64) atomicAdd(&cnt[ids[q]], 1);  // LDS integer add
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) table[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads.  table [nchunk x E] in, becomes the base slot
+// of each (chunk, expert).  Also writes counts/offsets, the m-tile map for
+// tile height bm and zeroes the GEMM work-queue counters.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table, int nchunk,
+                                                    int E, int bm, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    TileMap tm) {
+  __shared__ int32_t s_cnt[1024];
+  __shared__ int32_t s_tiles[1024];
+  const int tid = threadIdx.x;
+  int total = 0;
+  if (tid < E) {
+    // running sum down this expert's column; loads go out 8 at a time
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = (c0 + u < nchunk) ? table[static_cast<size_t>(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < nchunk) table[static_cast<size_t>(c0 + u) * E + tid] = total;
+        total += v[u];
+      }
+    }
+  }
+  const int tiles = (tid < E) ? (total + bm - 1) / bm : 0;
+  s_cnt[tid] = (tid < E) ? total : 0;
+  s_tiles[tid] = tiles;
+  __syncthreads();
+  // exclusive scans of counts and tiles over experts (E <= 1024); one
+  // thread walks the experts in order -- at most 1024 steps
+  if (tid == 0) {
+    int acc_c = 0, acc_t = 0;
+    for (int e = 0; e < E; ++e) {
+      int c = s_cnt[e], t = s_tiles[e];
+      s_cnt[e] = acc_c;
+      s_tiles[e] = acc_t;
+      acc_c += c;
+      acc_t += t;
+    }
+    offsets[E] = acc_c;
+    *tm.n_mtiles = acc_t;
+    tm.queue[0] = 0;
+    tm.queue[1] = 0;
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int off = s_cnt[tid];
+    counts[tid] = total;
+    offsets[tid] = off;
+    for (int c = 0; c < nchunk; ++c) table[static_cast<size_t>(c) * E + tid] += off;
+    const int t0 = s_tiles[tid];
+    for (int m = 0; m < tiles; ++m) {
+      tm.e[t0 + m] = tid;
+      tm.row0[t0 + m] = off + m * bm;
+      tm.rows[t0 + m] = min(bm, total - m * bm);
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int n,
+                                                     int k, int E, int nbits,
+                                                     const int32_t* __restrict__ table,
+                                                     int32_t* __restrict__ slot_token,
+                                                     int32_t* __restrict__ slot_k,
+                                                     int32_t* __restrict__ token_slot) {
+  extern __shared__ int32_t base[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) base[e] = table[static_cast<size_t>(blockIdx.x) * E + e];
+  __syncthreads();
+  const int q0 = blockIdx.x * kPermuteChunk;
+  const int q1 = min(n, q0 + kPermuteChunk);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int qb = q0; qb < q1; qb += 64) {
+    const int q = qb + lane;
+    const bool active = q < q1;
+    const int e = active ? ids[q] : 0;
+    const uint64_t peers = match_lanes(e, nbits, active);
+    const int rank = __popcll(peers & below);
+    const int cnt = __popcll(peers);
+    int slot = 0;
+    if (active) slot = base[e] + rank;
+    __syncthreads();  // every lane has read base[] before it moves
+    if (active && rank == cnt - 1) base[e] += cnt;
+    __syncthreads();
+    if (active) {
+      slot_token[slot] = q / k;
+      slot_k[slot] = q % k;
+      token_slot[q] = slot;
+    }
+  }
+}
+
+}  // namespace
+
+void launch_permute(const int32_t* ids, int T, int k, int E, int bm, int32_t* table,
+                    int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_k,
+                    int32_t* token_slot, TileMap tm, hipStream_t s) {
+  const int n = T * k;
+  const int nchunk = (n + kPermuteChunk - 1) / kPermuteChunk;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const size_t lds = sizeof(int32_t) * static_cast<size_t>(E);
+  if (nchunk > 0) hist_kernel<<<nchunk, 64, lds, s>>>(ids, n, E, table);
+  scan_kernel<<<1, 1024, 0, s>>>(table, nchunk, E, bm, counts, offsets, tm);
+  if (nchunk > 0)
+    scatter_kernel<<<nchunk, 64, lds, s>>>(ids, n, k, E, nbits, table, slot_token, slot_k,
+                                           token_slot);
+}
+
+}  // namespace moe
