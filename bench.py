@@ -1,0 +1,267 @@
+#!/usr/bin/env python
+"""Benchmark of the one-GPU MoE layer forward on MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one whole-layer moe_forward (gate, FP8 quantisation of x when
+the layer is FP8, histogram/scan/scatter, W1/W3 + SwiGLU GEMM, W2 GEMM,
+combine) on inputs already resident in HBM, weights packed once before the
+timed region.  Prints ONE JSON line: tokens/s of the whole layer, the
+roofline of the dominant kernel timed live with HIP events recorded inside
+the call, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {0: 157.3, 1: 2516.6, 2: 5033.2}  # dense MFMA: fp32, bf16, fp8
+PEAK_HBM_GBPS = 8000.0
+STAGES = ["gate", "quant_x", "permute", "gemm_w13_swiglu", "gemm_w2", "combine"]
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _events(hip, n):
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    return evs
+
+
+def _elapsed(hip, a, b):
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return ms.value
+
+
+def _src_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc"))):
+        with open(os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload, kernel):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, valid
+    only while the kernel sources are the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_hash") != _src_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _stage_work(cfg, counts):
+    """Algorithmic work per launch of each GEMM stage: FLOPs, and HBM bytes
+    (weights of the experts that receive a token, activations in, outputs)."""
+    import numpy as np
+    es = {0: 4, 1: 2, 2: 1}[cfg.w_dtype]
+    ae = {0: 4, 1: 2}[cfg.act_dtype] if cfg.w_dtype != 2 else 1
+    he = {0: 4, 1: 2, 2: 1}[cfg.w_dtype]
+    hit = int(np.count_nonzero(counts))
+    n = cfg.T * cfg.k
+    w13 = dict(flops=4.0 * n * cfg.d * cfg.f,
+               bytes=hit * 2.0 * cfg.d * cfg.f * es + cfg.T * cfg.d * ae + n * cfg.f * he)
+    w2 = dict(flops=2.0 * n * cfg.d * cfg.f,
+              bytes=hit * 1.0 * cfg.d * cfg.f * es + n * cfg.f * he + n * cfg.d * 4.0)
+    return {"gemm_w13_swiglu": w13, "gemm_w2": w2, "hit_experts": hit}
+
+
+def _cpu_baseline(cfg, inp, out_gpu, target_s):
+    """The CPU oracle as it stands, timed on a bounded token sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from mixture_experts_layer_softmax_amd.inputs import host_arrays
+
+    orc = {0: oracle.ORC_F32, 1: oracle.ORC_BF16, 2: oracle.ORC_FP8}
+    gw = host_arrays(inp["gate_w"])
+    bias = None if inp.get("bias") is None else inp["bias"].cpu().numpy()
+    host_w = {}
+
+    def run(rows):
+        x = host_arrays(inp["x"][torch.as_tensor(rows, device=inp["x"].device)])
+        _, ids, _ = oracle.route(x, gw, bias, cfg.k, orc[cfg.act_dtype])
+        for e in sorted(set(int(v) for v in ids.reshape(-1))):
+            if e not in host_w:
+                host_w[e] = {n: host_arrays(inp[n][e]) for n in ("W1", "W3", "W2")}
+                if cfg.w_dtype == 2:
+                    host_w[e].update({n + "s": inp[n + "s"][e].cpu().numpy()
+                                      for n in ("W1", "W3", "W2")})
+        W = {n: [host_w.get(e, {}).get(n) for e in range(cfg.E)]
+             for n in ("W1", "W3", "W2", "W1s", "W3s", "W2s")}
+        fp8 = cfg.w_dtype == 2
+        t0 = time.perf_counter()
+        out, _, _ = oracle.forward(x, gw, bias, W["W1"], W["W3"], W["W2"], cfg.k,
+                                   orc[cfg.act_dtype], orc[cfg.w_dtype],
+                                   W1s=W["W1s"] if fp8 else None,
+                                   W3s=W["W3s"] if fp8 else None,
+                                   W2s=W["W2s"] if fp8 else None)
+        return out, time.perf_counter() - t0
+
+    rng = np.random.default_rng(0)
+    n0 = min(cfg.T, 8)
+    rows0 = np.sort(rng.choice(cfg.T, size=n0, replace=False))
+    _, t_probe = run(rows0)
+    n = int(min(cfg.T, max(n0, n0 * target_s / max(t_probe, 1e-3))))
+    rows = np.sort(rng.choice(cfg.T, size=n, replace=False))
+    ref, secs = run(rows)
+    got = out_gpu[torch.as_tensor(rows, device=out_gpu.device)].double().cpu().numpy()
+    rms = math.sqrt(float(np.mean(ref ** 2))) or 1.0
+    err = float(np.abs(got - ref).max()) / rms
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    return {"value": n / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {cfg.T} tokens (seeded random rows), full layer forward per "
+                      f"token, {secs:.1f} s", "seconds": secs}, err
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-m", type=int, default=0, help="expert tile height (0 = auto)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_softmax_amd import binding as B
+    from mixture_experts_layer_softmax_amd.configs import CONFIGS
+    from mixture_experts_layer_softmax_amd.inputs import make_inputs
+
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    B.load()
+    inp = make_inputs(cfg, device="cuda")
+    packed = B.pack_weights(inp)
+    p = B.problem_of(cfg, block_m=args.block_m)
+    ws = B.alloc_workspace(p)
+    out = B.out_tensor(cfg)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    hip = _hip()
+    nev = B.NUM_STAGE_EVENTS
+    evs = [_events(hip, nev) for _ in range(args.steps)]
+
+    def step(dbg=None):
+        B.moe_forward(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"],
+                      packed["W3t"], packed["W2t"], packed.get("W1s"), packed.get("W3s"),
+                      packed.get("W2s"), out, ws, dbg=dbg, stream=stream)
+
+    for _ in range(args.warmup):
+        step({"counts": counts})
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step({"stage_events": evs[i]})
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    hip.hipEventSynchronize(evs[-1][-1])
+    stage_ms = {}
+    for s, name in enumerate(STAGES, start=1):
+        stage_ms[name] = float(np.mean([_elapsed(hip, e[s - 1], e[s]) for e in evs]))
+    gpu_ms = _elapsed(hip, evs[0][0], evs[-1][-1]) / args.steps
+    for e in evs:
+        for v in e:
+            hip.hipEventDestroy(v)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.T * args.steps / elapsed
+    work = _stage_work(cfg, counts.cpu().numpy())
+    dom = max(("gemm_w13_swiglu", "gemm_w2"), key=lambda k: stage_ms[k])
+    dom_s = stage_ms[dom] * 1e-3
+    decode = cfg.T * cfg.k / cfg.E < 16
+    if decode:
+        achieved = work[dom]["bytes"] / dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBPS}
+    else:
+        achieved = work[dom]["flops"] / dom_s / 1e12
+        peak = PEAK_TFLOPS[cfg.w_dtype]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof["kernel"] = dom
+    roof["traffic"] = _traffic(cfg.name, dom)
+    layer_flops = cfg.expert_flops
+    layer = {
+        "expert_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
+        "mfma_frac_of_peak": layer_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_TFLOPS[cfg.w_dtype],
+        "alg_hbm_GBps": (work["gemm_w13_swiglu"]["bytes"] + work["gemm_w2"]["bytes"])
+        / (ms_per_step * 1e-3) / 1e9,
+        "hit_experts": work["hit_experts"],
+        "gpu_event_ms_per_step": gpu_ms,
+    }
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = _cpu_baseline(cfg, inp, out, args.cpu_seconds)
+
+    dtype = {0: "f32", 1: "bf16", 2: "fp8e4m3"}[cfg.w_dtype]
+    line = {
+        "metric": "MoE-layer tokens/s on 1 MI355X; MFMA % peak (prefill), HBM GB/s (decode)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
+                   "top_k": cfg.k, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages_ms": stage_ms,
+        "layer": layer,
+        "parity_sample_err_rms": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

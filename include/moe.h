@@ -80,7 +80,7 @@ typedef enum {
  *   block_m:   rows per expert tile of the grouped GEMMs; 0 picks it from the
  *              expected tokens per expert T*top_k/E (the serving-regime choice
  *              of the MegaMoE-vs-MoE-systems page, section 2.5, re-tuned for
- *              MFMA tiles).  Otherwise one of 16, 32, 64, 128.
+ *              MFMA tiles).  Otherwise one of 16, 32, 64, 128, 256.
  * bf16/FP8 layers need d % 64 == 0 and f % 64 == 0; fp32 layers need
  * d % 16 == 0 and f % 16 == 0. */
 typedef struct {

@@ -32,7 +32,8 @@ int pick_bm(const moe_problem& p) {
   if (r <= 24.0) return 16;
   if (r <= 48.0) return 32;
   if (r <= 160.0) return 64;
-  return 128;
+  if (r < 384.0) return 128;
+  return 256;
 }
 
 bool valid_problem(const moe_problem* p) {
@@ -46,15 +47,20 @@ bool valid_problem(const moe_problem* p) {
   if (!ok_types) return false;
   if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return false;
   if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
-      p->block_m != 128)
+      p->block_m != 128 && p->block_m != 256)
     return false;
   return true;
 }
 
-// Shapes the kernels support (valid but unsupported -> MOE_ERR_UNSUPPORTED).
+// Shapes the kernels support (valid but unsupported -> MOE_ERR_UNSUPPORTED):
+// contraction rows of 128 bytes, and every GEMM operand addressable with
+// 32-bit byte offsets (x or its FP8 codes, h, one expert's weight matrix).
 bool supported_shape(const moe_problem* p) {
   const int64_t m = p->w_dtype == MOE_F32 ? 32 : (p->w_dtype == MOE_BF16 ? 64 : 128);
-  return p->d % m == 0 && p->f % m == 0 && p->d <= (1ll << 20) && p->f <= (1ll << 20);
+  if (p->d % m != 0 || p->f % m != 0) return false;
+  const int64_t es = p->w_dtype == MOE_F32 ? 4 : (p->w_dtype == MOE_BF16 ? 2 : 1);
+  const int64_t lim = 1ll << 31;
+  return p->T * p->d * es < lim && p->T * p->top_k * p->f * es < lim && p->d * p->f * es < lim;
 }
 
 struct Layout {
@@ -90,7 +96,7 @@ Layout make_layout(const moe_problem& p) {
   L.tm_e = take(sizeof(int32_t) * L.max_mtiles);
   L.tm_row0 = take(sizeof(int32_t) * L.max_mtiles);
   L.tm_rows = take(sizeof(int32_t) * L.max_mtiles);
-  L.tm_misc = take(sizeof(int32_t) * 4);
+  L.tm_misc = take(sizeof(int32_t) * (1 + moe::kQueueWords));
   const bool fp8 = p.w_dtype == MOE_FP8_E4M3;
   L.xq = take(fp8 ? static_cast<size_t>(p.T) * p.d : 0);
   L.sx = take(fp8 ? sizeof(float) * p.T * (p.d / 128) : 0);

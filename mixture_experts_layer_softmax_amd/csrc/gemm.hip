@@ -30,6 +30,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <cstdlib>
 #include <mutex>
 
 namespace moe {
@@ -37,7 +38,6 @@ namespace moe {
 namespace {
 
 constexpr int kRowBytes = 128;
-constexpr int kThreads = 256;
 
 template <int DT>
 struct ESize;
@@ -54,23 +54,35 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
+// Bytes of LDS shared by the main-loop stages and the epilogue staging.
+template <int DT, int PHASE, int BM, int BN, int WM>
+struct StageBytes {
+  static constexpr int main_loop = 2 * (BM + BN) * kRowBytes;
+  static constexpr int epilogue = (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) *
+                                  ((PHASE == 1) ? ESize<DT>::v : 4);
+  static constexpr int v = main_loop > epilogue ? main_loop : epilogue;
+};
+
 template <int DT, int PHASE, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
+  constexpr int kThreads = WM * WN * 64;
   constexpr int ES = ESize<DT>::v;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   constexpr int ACH = BM * 8, BCH = BN * 8;  // 16-byte chunks per K-step
   constexpr int RA = (ACH + kThreads - 1) / kThreads;
   constexpr int RB = (BCH + kThreads - 1) / kThreads;
-  static_assert(WM * WN == 4, "four waves");
+  static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(PHASE == 2 || TN % 2 == 0, "gate/up pairs");
   static_assert(!(DT == kFP8 && PHASE == 1) || BN == 256, "FP8 h groups of 128 f");
 
+  // LDS: the two K-step stages of A and B, reused by the epilogue staging,
+  // then (FP8 phase 1) the per-wave row maxima
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t* As = lds;                                  // [2][BM][128]
   uint8_t* Bs = lds + 2 * BM * kRowBytes;             // [2][BN][128]
-  float* red = reinterpret_cast<float*>(Bs + 2 * BN * kRowBytes);  // [WN][BM]
+  float* red = reinterpret_cast<float*>(lds + StageBytes<DT, PHASE, BM, BN, WM>::v);  // [WN][BM]
   __shared__ int s_task;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -80,80 +92,119 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   const int ksteps = static_cast<int>(K * ES / kRowBytes);
   const int kblocks = static_cast<int>(K / 128);  // FP8 scale blocks along K
   const int nblocks = static_cast<int>(N / 128);
-  const int total = *g.tm.n_mtiles * g.n_tiles_n;
+  // XCD-aware work queue.  Workgroups of a persistent launch are dealt to the
+  // eight XCDs round-robin, so workgroup b runs on XCD b % 8 and shares that
+  // XCD's L2 with the others there.  The m-tiles are cut into chunks of kGM
+  // consecutive m-tiles; chunk c belongs to XCD c % 8, whose workgroups take
+  // its tasks n-tile by n-tile (kGM m-tiles x n-tiles in flight per XCD:
+  // activation rows reused across n-tiles and weight rows across m-tiles in
+  // one L2).  A drained XCD queue makes its workgroups steal from the others,
+  // so the queue stays work-conserving under routing skew.
+  constexpr int kXcd = 8, kGM = 4;
+  const int M = *g.tm.n_mtiles, NT = g.n_tiles_n;
+  const int nchunks = (M + kGM - 1) / kGM;
+  const int chunk_tasks = kGM * NT;
+  const int xcd = static_cast<int>(blockIdx.x) % kXcd;
+  int* queue = g.tm.queue + kXcd * g.queue_idx;
 
   for (;;) {
-    if (tid == 0) s_task = atomicAdd(&g.tm.queue[g.queue_idx], 1);
+    if (tid == 0) {
+      int task = -1;
+      for (int s = 0; s < kXcd && task < 0; ++s) {
+        const int y = (xcd + s) % kXcd;
+        const int owned = nchunks > y ? (nchunks - y + kXcd - 1) / kXcd : 0;
+        const int limit = owned * chunk_tasks;
+        for (;;) {
+          if (__hip_atomic_load(&queue[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= limit)
+            break;
+          const int v = atomicAdd(&queue[y], 1);
+          if (v >= limit) break;
+          const int p = v % chunk_tasks;
+          const int mt = (y + kXcd * (v / chunk_tasks)) * kGM + p % kGM;
+          if (mt < M) {  // the last chunk may hold fewer than kGM m-tiles
+            task = mt * NT + p / kGM;
+            break;
+          }
+        }
+      }
+      s_task = task;
+    }
     __syncthreads();
     const int task = s_task;
-    if (task >= total) break;
+    if (task < 0) break;
     const int mt = task / g.n_tiles_n;
     const int nt = task - mt * g.n_tiles_n;
     const int e = g.tm.e[mt], row0 = g.tm.row0[mt], rows = g.tm.rows[mt];
     const int64_t n0 = static_cast<int64_t>(nt) * BN;
 
-    // ---- global source of every 16-byte chunk this thread stages ----
-    const uint8_t* pa[RA];
-    const uint8_t* pb[RB];
+    // ---- source of every 16-byte chunk this thread stages: 32-bit byte
+    // offsets from wave-uniform bases (the host checks that every operand
+    // spans less than 2^31 bytes per expert) ----
+    const int64_t w_bytes = N * K * ES;  // one expert's weight matrix
+    const uint8_t* b0 = g.B0 + static_cast<int64_t>(e) * w_bytes;
+    const uint8_t* b1 = (PHASE == 1) ? g.B1 + static_cast<int64_t>(e) * w_bytes : b0;
+    uint32_t oa[RA], ob[RB];
+    uint32_t up_mask = 0;  // bit j: chunk j of B comes from the up (W3) matrix
 #pragma unroll
     for (int j = 0; j < RA; ++j) {
       const int ci = tid + kThreads * j;
       const int r = min(ci >> 3, rows - 1);  // padding rows re-read a valid row
       const int64_t src = g.gather ? g.gather[row0 + r] : static_cast<int64_t>(row0 + r);
-      pa[j] = g.A + src * g.a_row_bytes + (ci & 7) * 16;
+      oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + (ci & 7) * 16);
     }
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int ci = tid + kThreads * j;
       const int64_t n = n0 + (ci >> 3);
       int64_t col;
-      const uint8_t* base;
       if (PHASE == 1) {  // combined rows: 16 gate rows, then 16 up rows, per f block
         col = (n >> 5) * 16 + (n & 15);
-        base = (n & 16) ? g.B1 : g.B0;
+        if (n & 16) up_mask |= 1u << j;
       } else {
         col = n;
-        base = g.B0;
       }
       col = min(col, N - 1);
-      pb[j] = base + (static_cast<int64_t>(e) * N + col) * K * ES + (ci & 7) * 16;
+      ob[j] = static_cast<uint32_t>(col * K * ES + (ci & 7) * 16);
     }
 
-    uint4 ra[RA], rb[RB];
-    auto gload = [&](int ks) {
-      const int64_t off = static_cast<int64_t>(ks) * kRowBytes;
-#pragma unroll
-      for (int j = 0; j < RA; ++j)
-        if (ACH % kThreads == 0 || tid + kThreads * j < ACH)
-          ra[j] = *reinterpret_cast<const uint4*>(pa[j] + off);
-#pragma unroll
-      for (int j = 0; j < RB; ++j)
-        if (BCH % kThreads == 0 || tid + kThreads * j < BCH)
-          rb[j] = *reinterpret_cast<const uint4*>(pb[j] + off);
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < RA; ++j) {
-        const int ci = tid + kThreads * j;
-        if (ACH % kThreads == 0 || ci < ACH)
-          *reinterpret_cast<uint4*>(As + buf * BM * kRowBytes + swz(ci >> 3, ci & 7)) = ra[j];
-      }
-#pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        const int ci = tid + kThreads * j;
-        if (BCH % kThreads == 0 || ci < BCH)
-          *reinterpret_cast<uint4*>(Bs + buf * BN * kRowBytes + swz(ci >> 3, ci & 7)) = rb[j];
-      }
-    };
+    // Prefetch registers of the next K-step.  Written with plain loops (no
+    // lambdas capturing the arrays by reference), so they stay in VGPRs.
+    u32x4 ra[RA], rb[RB];
+#define MOE_GLOAD(KS)                                                                   \
+  do {                                                                                  \
+    const uint32_t off_ = static_cast<uint32_t>(KS) * kRowBytes;                        \
+    _Pragma("unroll") for (int j = 0; j < RA; ++j) if (ACH % kThreads == 0 ||            \
+                                                        tid + kThreads * j < ACH)       \
+        ra[j] = *reinterpret_cast<const u32x4*>(g.A + (oa[j] + off_));                  \
+    _Pragma("unroll") for (int j = 0; j < RB; ++j) if (BCH % kThreads == 0 ||            \
+                                                        tid + kThreads * j < BCH)       \
+        rb[j] = *reinterpret_cast<const u32x4*>(((up_mask >> j) & 1u ? b1 : b0) +       \
+                                                (ob[j] + off_));                        \
+  } while (0)
+#define MOE_LSTORE(BUF)                                                                 \
+  do {                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < RA; ++j) {                                    \
+      const int ci = tid + kThreads * j;                                                \
+      if (ACH % kThreads == 0 || ci < ACH)                                              \
+        *reinterpret_cast<u32x4*>(As + (BUF) * BM * kRowBytes + swz(ci >> 3, ci & 7)) = \
+            ra[j];                                                                      \
+    }                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < RB; ++j) {                                    \
+      const int ci = tid + kThreads * j;                                                \
+      if (BCH % kThreads == 0 || ci < BCH)                                              \
+        *reinterpret_cast<u32x4*>(Bs + (BUF) * BN * kRowBytes + swz(ci >> 3, ci & 7)) = \
+            rb[j];                                                                      \
+    }                                                                                   \
+  } while (0)
 
-    // FP8: per token fragment i, the A-scale row of the lane's slot column
-    const float* sa_row[TM];
+    // FP8: per token fragment i, the A-scale row offset of the lane's slot
+    uint32_t sa_off[TM];
     if constexpr (DT == kFP8) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = min(wm * WTM + 16 * i + l16, rows - 1);
         const int64_t src = g.gather ? g.gather[row0 + r] : static_cast<int64_t>(row0 + r);
-        sa_row[i] = g.sa + src * kblocks;
+        sa_off[i] = static_cast<uint32_t>(src * kblocks);
       }
     }
 
@@ -163,62 +214,57 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    gload(0);
-    lstore(0);
+    MOE_GLOAD(0);
+    MOE_LSTORE(0);
     __syncthreads();
     for (int ks = 0; ks < ksteps; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < ksteps) gload(ks + 1);
+      if (ks + 1 < ksteps) MOE_GLOAD(ks + 1);
       const uint8_t* Ab = As + cur * BM * kRowBytes;
       const uint8_t* Bb = Bs + cur * BN * kRowBytes;
       if constexpr (DT == kBF16) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          bf16x8 xf[TM], wf[TN];
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-            xf[i] = *reinterpret_cast<const bf16x8*>(Ab + swz(wm * WTM + 16 * i + l16, kk * 4 + lg));
+          bf16x8 wf[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             wf[j] = *reinterpret_cast<const bf16x8*>(Bb + swz(wn * WTN + 16 * j + l16, kk * 4 + lg));
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
+          for (int i = 0; i < TM; ++i) {
+            if (wm * WTM + 16 * i >= rows) break;  // padding rows only: wave-uniform
+            const bf16x8 xf =
+                *reinterpret_cast<const bf16x8*>(Ab + swz(wm * WTM + 16 * i + l16, kk * 4 + lg));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf, acc[i][j], 0, 0, 0);
+          }
         }
       } else if constexpr (DT == kF32) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          f32x4 xf[TM], wf[TN];
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-            xf[i] = *reinterpret_cast<const f32x4*>(Ab + swz(wm * WTM + 16 * i + l16, kk * 4 + lg));
+          f32x4 wf[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz(wn * WTN + 16 * j + l16, kk * 4 + lg));
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int i = 0; i < TM; ++i) {
+            if (wm * WTM + 16 * i >= rows) break;
+            const f32x4 xf =
+                *reinterpret_cast<const f32x4*>(Ab + swz(wm * WTM + 16 * i + l16, kk * 4 + lg));
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
               for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[i][u], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[u], acc[i][j], 0, 0, 0);
+          }
         }
       } else {  // FP8: one 16x16x128 MFMA per fragment pair and K block
-        i32x8 xf[TM], wf[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = wm * WTM + 16 * i + l16;
-          i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz(r, 2 * lg));
-          i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz(r, 2 * lg + 1));
-          xf[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
+        i32x8 wf[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int r = wn * WTN + 16 * j + l16;
-          i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz(r, 2 * lg));
-          i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz(r, 2 * lg + 1));
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz(r, 2 * lg));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz(r, 2 * lg + 1));
           wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
         float s_b0, s_b1 = 0.f;
@@ -232,64 +278,50 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const float s_a = sa_row[i][ks];
+          if (wm * WTM + 16 * i >= rows) break;  // padding rows only: wave-uniform
+          const int r = wm * WTM + 16 * i + l16;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz(r, 2 * lg));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz(r, 2 * lg + 1));
+          const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const float s_a = g.sa[sa_off[i] + ks];
+          const float sg = s_a * s_b0, su = s_a * s_b1;
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], z, 0, 0,
-                                                                        0, 127, 0, 127);
-            const float s = s_a * ((PHASE == 1 && (j & 1)) ? s_b1 : s_b0);
+            const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0,
+                                                                              0, 127, 0, 127);
+            const float sc = (PHASE == 1 && (j & 1)) ? su : sg;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], s, acc[i][j][r]);
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(p[q], sc, acc[i][j][q]);
           }
         }
       }
-      if (ks + 1 < ksteps) lstore(cur ^ 1);
+      if (ks + 1 < ksteps) MOE_LSTORE(cur ^ 1);
       __syncthreads();
     }
 
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+
     // ---------------- epilogue ----------------
-    if constexpr (PHASE == 2) {
-      float* Y = reinterpret_cast<float*>(g.C);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int lr = wm * WTM + 16 * i + l16;
-        if (lr >= rows) continue;
-        const int64_t slot = row0 + lr;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t col = n0 + wn * WTN + 16 * j + 4 * lg;
-          if (col < N) *reinterpret_cast<f32x4*>(Y + slot * N + col) = acc[i][j];
-        }
-      }
-    } else if constexpr (DT != kFP8) {
-      const int64_t fbase = ((n0 + wn * WTN) >> 1) + 4 * lg;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int lr = wm * WTM + 16 * i + l16;
-        if (lr >= rows) continue;
-        const int64_t slot = row0 + lr;
-#pragma unroll
-        for (int p = 0; p < TN / 2; ++p) {
-          const int64_t col = fbase + 16 * p;
-          if (col >= N) continue;
-          float h[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
-          if constexpr (DT == kBF16) {
-            uint2 v;
-            v.x = f32_to_bf16_rne(h[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[1])) << 16);
-            v.y = f32_to_bf16_rne(h[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[3])) << 16);
-            *reinterpret_cast<uint2*>(g.C + (slot * N + col) * 2) = v;
-          } else {
-            *reinterpret_cast<f32x4*>(g.C + (slot * N + col) * 4) = f32x4{h[0], h[1], h[2], h[3]};
-          }
-        }
-      }
-    } else {
-      // FP8 h: SwiGLU in fp32, then one scale per (slot, 128 f columns) --
-      // the whole workgroup tile -- and E4M3 codes.
-      float h[TM][TN / 2][4];
+    // Output values are staged in LDS (free after the main loop's last
+    // barrier) so that every global store is a 16-byte piece of a contiguous
+    // row segment; one pass per wave row wm.  Staged rows are XOR-swizzled by
+    // 16-byte chunk to keep the fragment writes off a single bank group.
+    constexpr int OUT_COLS = (PHASE == 1) ? BN / 2 : BN;
+    constexpr int OUT_ES = (PHASE == 1) ? ES : 4;
+    constexpr int ROWB = OUT_COLS * OUT_ES;
+    constexpr int CPR = ROWB / 16;
+    constexpr int XM = (CPR >= 16 ? 16 : CPR) - 1;
+    uint8_t* stage = lds;
+    auto st_off = [&](int r, int cbyte) {
+      return r * ROWB + ((((cbyte >> 4) ^ (r & XM)) << 4) | (cbyte & 15));
+    };
+    const int64_t col0 = (PHASE == 1) ? n0 / 2 : n0;
+
+    if constexpr (PHASE == 1 && DT == kFP8) {
+      // h = SiLU(gate) * up in fp32 (in place), then the row amax over the
+      // tile's 128 f columns: lanes, then the WN waves through LDS
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         float m = 0.f;
@@ -297,50 +329,89 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
         for (int p = 0; p < TN / 2; ++p)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            h[i][p][r] = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
-            m = fmaxf(m, fabsf(h[i][p][r]));
+            acc[i][2 * p][r] = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
+            m = fmaxf(m, fabsf(acc[i][2 * p][r]));
           }
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
         if (lg == 0) red[wn * BM + wm * WTM + 16 * i + l16] = m;
       }
       __syncthreads();
-      const int64_t fbase = ((n0 + wn * WTN) >> 1) + 4 * lg;
-      const int fgroup = static_cast<int>(n0 / 256);
+    }
+
+    for (int pass = 0; pass < WM; ++pass) {
+      if (wm == pass) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int lr = wm * WTM + 16 * i + l16;
-        float amax = 0.f;
+        for (int i = 0; i < TM; ++i) {
+          const int r = 16 * i + l16;  // row within this pass
+          if constexpr (PHASE == 2) {
 #pragma unroll
-        for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + lr]);
-        if (lr >= rows) continue;
-        const float s = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
-        const int64_t slot = row0 + lr;
+            for (int j = 0; j < TN; ++j)
+              *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
+                  acc[i][j];
+          } else if constexpr (DT == kFP8) {
+            const int lr = pass * WTM + r;
+            float amax = 0.f;
 #pragma unroll
-        for (int p = 0; p < TN / 2; ++p) {
-          uint32_t packed = 0;
+            for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + lr]);
+            const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) packed |= f32_to_e4m3(__fdiv_rn(h[i][p][r], s)) << (8 * r);
-          *reinterpret_cast<uint32_t*>(g.C + slot * N + fbase + 16 * p) = packed;
+            for (int p = 0; p < TN / 2; ++p) {
+              uint32_t packed = 0;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                packed |= f32_to_e4m3(__fdiv_rn(acc[i][2 * p][q], sc)) << (8 * q);
+              *reinterpret_cast<uint32_t*>(stage + st_off(r, wn * (WTN / 2) + 16 * p + 4 * lg)) =
+                  packed;
+            }
+            if (wn == 0 && lg == 0 && lr < rows)
+              g.sc[static_cast<int64_t>(row0 + lr) * (N / 128) + n0 / 256] = sc;
+          } else {
+#pragma unroll
+            for (int p = 0; p < TN / 2; ++p) {
+              float h[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) h[q] = silu(acc[i][2 * p][q]) * acc[i][2 * p + 1][q];
+              const int cb = (wn * (WTN / 2) + 16 * p + 4 * lg) * ES;
+              if constexpr (DT == kBF16) {
+                u32x2 v;
+                v.x = f32_to_bf16_rne(h[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[1])) << 16);
+                v.y = f32_to_bf16_rne(h[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[3])) << 16);
+                *reinterpret_cast<u32x2*>(stage + st_off(r, cb)) = v;
+              } else {
+                *reinterpret_cast<f32x4*>(stage + st_off(r, cb)) = f32x4{h[0], h[1], h[2], h[3]};
+              }
+            }
+          }
         }
-        if (wn == 0 && lg == 0) g.sc[slot * (N / 128) + fgroup] = s;
       }
+      __syncthreads();
+      for (int idx = tid; idx < WTM * CPR; idx += kThreads) {
+        const int r = idx / CPR, c = idx - r * CPR;
+        const int lr = pass * WTM + r;
+        const int64_t col = col0 + c * (16 / OUT_ES);
+        if (lr < rows && col < N)
+          *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(row0 + lr) * N + col) * OUT_ES) =
+              *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
+      }
+      __syncthreads();
     }
   }
 }
 
 template <int DT, int PHASE, int BM, int BN, int WM, int WN>
 struct Variant {
+  static constexpr int kThreads = WM * WN * 64;
   static constexpr int lds_bytes() {
-    return 2 * (BM + BN) * kRowBytes + ((DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0);
+    return StageBytes<DT, PHASE, BM, BN, WM>::v + ((DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0);
   }
   static int launch(const GemmArgs& a, hipStream_t s) {
     auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN>;
     static int grid = 0;
     static std::once_flag once;
     std::call_once(once, [&] {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes());
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes());
       int dev = 0, cus = 0, per_cu = 0;
       (void)hipGetDevice(&dev);
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -353,37 +424,69 @@ struct Variant {
   static constexpr int tile_n() { return BN; }
 };
 
-// Kernel variant per (dtype, phase, tile height).
+// Tuning selector: MOE_GEMM_VARIANT picks an alternative tile shape for the
+// tile heights that have one (read once; 0 = default).
+int variant_choice() {
+  static int v = [] {
+    const char* e = getenv("MOE_GEMM_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+// Kernel variant per (dtype, phase, tile height, tuning variant).
 template <typename F>
-int dispatch(int phase, int dtype, int bm, F&& f) {
-#define MOE_V(DT, P, BM_, BN_, WM_, WN_) \
-  if (dtype == DT && phase == P && bm == BM_) return f(Variant<DT, P, BM_, BN_, WM_, WN_>{});
-  MOE_V(kBF16, 1, 128, 128, 2, 2)
-  MOE_V(kBF16, 2, 128, 128, 2, 2)
-  MOE_V(kBF16, 1, 64, 128, 1, 4)
-  MOE_V(kBF16, 2, 64, 128, 1, 4)
-  MOE_V(kBF16, 1, 32, 128, 1, 4)
-  MOE_V(kBF16, 2, 32, 128, 1, 4)
-  MOE_V(kBF16, 1, 16, 256, 1, 4)
-  MOE_V(kBF16, 2, 16, 256, 1, 4)
-  MOE_V(kFP8, 1, 128, 256, 2, 2)
-  MOE_V(kFP8, 2, 128, 128, 2, 2)
-  MOE_V(kFP8, 1, 64, 256, 1, 4)
-  MOE_V(kFP8, 2, 64, 128, 1, 4)
-  MOE_V(kFP8, 1, 32, 256, 2, 2)
-  MOE_V(kFP8, 2, 32, 128, 1, 4)
-  MOE_V(kFP8, 1, 16, 256, 1, 4)
-  MOE_V(kFP8, 2, 16, 128, 1, 4)
-  MOE_V(kF32, 1, 128, 128, 2, 2)
-  MOE_V(kF32, 2, 128, 128, 2, 2)
-  MOE_V(kF32, 1, 64, 128, 1, 4)
-  MOE_V(kF32, 2, 64, 128, 1, 4)
-  MOE_V(kF32, 1, 32, 128, 1, 4)
-  MOE_V(kF32, 2, 32, 128, 1, 4)
-  MOE_V(kF32, 1, 16, 128, 1, 4)
-  MOE_V(kF32, 2, 16, 128, 1, 4)
+int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
+#define MOE_V(DT, P, BM_, VAR, BN_, WM_, WN_)                     \
+  if (dtype == DT && phase == P && bm == BM_ && var == VAR)        \
+    return f(Variant<DT, P, BM_, BN_, WM_, WN_>{});
+  MOE_V(kBF16, 1, 256, 0, 256, 2, 4)
+  MOE_V(kBF16, 2, 256, 0, 256, 2, 4)
+  MOE_V(kBF16, 1, 256, 1, 256, 2, 2)
+  MOE_V(kBF16, 2, 256, 1, 256, 2, 2)
+  MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
+  MOE_V(kBF16, 2, 128, 0, 128, 2, 2)
+  MOE_V(kBF16, 1, 128, 1, 256, 1, 4)
+  MOE_V(kBF16, 2, 128, 1, 256, 1, 4)
+  MOE_V(kBF16, 1, 128, 2, 256, 2, 4)
+  MOE_V(kBF16, 2, 128, 2, 256, 2, 4)
+  MOE_V(kBF16, 1, 64, 0, 128, 1, 4)
+  MOE_V(kBF16, 2, 64, 0, 128, 1, 4)
+  MOE_V(kBF16, 1, 32, 0, 128, 1, 4)
+  MOE_V(kBF16, 2, 32, 0, 128, 1, 4)
+  MOE_V(kBF16, 1, 16, 0, 256, 1, 4)
+  MOE_V(kBF16, 2, 16, 0, 256, 1, 4)
+  MOE_V(kFP8, 1, 256, 0, 256, 2, 2)
+  MOE_V(kFP8, 2, 256, 0, 256, 2, 2)
+  MOE_V(kFP8, 1, 128, 0, 256, 2, 2)
+  MOE_V(kFP8, 2, 128, 0, 128, 2, 2)
+  MOE_V(kFP8, 1, 128, 1, 256, 2, 4)
+  MOE_V(kFP8, 2, 128, 1, 256, 2, 4)
+  MOE_V(kFP8, 1, 64, 0, 256, 1, 4)
+  MOE_V(kFP8, 2, 64, 0, 128, 1, 4)
+  MOE_V(kFP8, 1, 32, 0, 256, 2, 2)
+  MOE_V(kFP8, 2, 32, 0, 128, 1, 4)
+  MOE_V(kFP8, 1, 16, 0, 256, 1, 4)
+  MOE_V(kFP8, 2, 16, 0, 128, 1, 4)
+  MOE_V(kF32, 1, 256, 0, 128, 2, 2)
+  MOE_V(kF32, 2, 256, 0, 128, 2, 2)
+  MOE_V(kF32, 1, 128, 0, 128, 2, 2)
+  MOE_V(kF32, 2, 128, 0, 128, 2, 2)
+  MOE_V(kF32, 1, 64, 0, 128, 1, 4)
+  MOE_V(kF32, 2, 64, 0, 128, 1, 4)
+  MOE_V(kF32, 1, 32, 0, 128, 1, 4)
+  MOE_V(kF32, 2, 32, 0, 128, 1, 4)
+  MOE_V(kF32, 1, 16, 0, 128, 1, 4)
+  MOE_V(kF32, 2, 16, 0, 128, 1, 4)
 #undef MOE_V
   return -1;
+}
+
+template <typename F>
+int dispatch(int phase, int dtype, int bm, F&& f) {
+  int r = dispatch_var(phase, dtype, bm, variant_choice(), f);
+  if (r == -1 && variant_choice() != 0) r = dispatch_var(phase, dtype, bm, 0, f);
+  return r;
 }
 
 }  // namespace

@@ -9,9 +9,12 @@ namespace moe {
 
 constexpr int kPermuteChunk = 4096;  // (token, k) pairs per histogram chunk
 
+constexpr int kQueueWords = 16;  // 8 per-XCD work-queue counters per GEMM
+
 // Expert m-tile map written by the scan kernel: tile i covers slots
 // [row0[i], row0[i] + rows[i]) of expert e[i].  n_mtiles is the number of
-// valid entries; queue[2] are the work-queue counters of the two GEMMs.
+// valid entries; queue[kQueueWords] are the per-XCD work-queue counters of
+// the two GEMMs (zeroed by the scan kernel).
 struct TileMap {
   int32_t* e;
   int32_t* row0;

@@ -84,8 +84,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
     }
     offsets[E] = acc_c;
     *tm.n_mtiles = acc_t;
-    tm.queue[0] = 0;
-    tm.queue[1] = 0;
+    for (int q = 0; q < kQueueWords; ++q) tm.queue[q] = 0;
   }
   __syncthreads();
   if (tid < E) {

@@ -80,7 +80,7 @@ def test_forward_parity_reduced(name):
     _outputs_ok(cfg, out, ref, "native out")
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16_r", "prefill_fp8_r"])
 def test_forward_every_tile_height(name, block_m):
     cfg = REDUCED[name]
