@@ -33,7 +33,9 @@ int pick_bm(const moe_problem& p) {
   if (r <= 48.0) return 32;
   if (r <= 160.0) return 64;
   if (r < 384.0) return 128;
-  return 256;
+  // FP8 256-row tiles would need more than 256 VGPRs per lane at two waves
+  // per SIMD (32-byte operand fragments plus per-row scales)
+  return p.w_dtype == MOE_FP8_E4M3 ? 128 : 256;
 }
 
 bool valid_problem(const moe_problem* p) {
@@ -75,7 +77,7 @@ struct Layout {
 Layout make_layout(const moe_problem& p) {
   Layout L{};
   const int64_t n = p.T * p.top_k;
-  const int64_t nchunk = ceil_div(n, moe::kPermuteChunk);
+  const int64_t nchunk = ceil_div(n, moe::permute_chunk(n));
   L.bm = pick_bm(p);
   L.max_mtiles = (n + static_cast<int64_t>(p.E) * (L.bm - 1)) / L.bm + 1;
   size_t off = 0;

@@ -294,6 +294,9 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(p[q], sc, acc[i][j][q]);
           }
+          // keep each fragment's MFMAs next to their rescale: hoisting all of
+          // them would hold TM x TN fresh results live and spill
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (ks + 1 < ksteps) MOE_LSTORE(cur ^ 1);
@@ -456,12 +459,14 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kBF16, 2, 32, 0, 128, 1, 4)
   MOE_V(kBF16, 1, 16, 0, 256, 1, 4)
   MOE_V(kBF16, 2, 16, 0, 256, 1, 4)
-  MOE_V(kFP8, 1, 256, 0, 256, 2, 2)
-  MOE_V(kFP8, 2, 256, 0, 256, 2, 2)
-  MOE_V(kFP8, 1, 128, 0, 256, 2, 2)
-  MOE_V(kFP8, 2, 128, 0, 128, 2, 2)
-  MOE_V(kFP8, 1, 128, 1, 256, 2, 4)
-  MOE_V(kFP8, 2, 128, 1, 256, 2, 4)
+  MOE_V(kFP8, 1, 256, 0, 256, 2, 4)
+  MOE_V(kFP8, 2, 256, 0, 256, 2, 4)
+  MOE_V(kFP8, 1, 256, 1, 256, 2, 2)
+  MOE_V(kFP8, 2, 256, 1, 256, 2, 2)
+  MOE_V(kFP8, 1, 128, 0, 256, 2, 4)
+  MOE_V(kFP8, 2, 128, 0, 256, 2, 4)
+  MOE_V(kFP8, 1, 128, 1, 256, 2, 2)
+  MOE_V(kFP8, 2, 128, 1, 128, 2, 2)
   MOE_V(kFP8, 1, 64, 0, 256, 1, 4)
   MOE_V(kFP8, 2, 64, 0, 128, 1, 4)
   MOE_V(kFP8, 1, 32, 0, 256, 2, 2)

@@ -7,7 +7,15 @@
 
 namespace moe {
 
-constexpr int kPermuteChunk = 4096;  // (token, k) pairs per histogram chunk
+// (token, k) pairs per histogram/scatter chunk: enough chunks to spread the
+// scatter over many wavefronts, few enough for the single-workgroup scan.
+constexpr int kPermuteMinChunk = 512;
+constexpr int kPermuteMaxChunks = 128;
+inline int permute_chunk(long long n) {
+  long long c = (n + kPermuteMaxChunks - 1) / kPermuteMaxChunks;
+  c = (c + 63) / 64 * 64;
+  return static_cast<int>(c < kPermuteMinChunk ? kPermuteMinChunk : c);
+}
 
 constexpr int kQueueWords = 16;  // 8 per-XCD work-queue counters per GEMM
 

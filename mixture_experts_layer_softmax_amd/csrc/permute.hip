@@ -8,7 +8,7 @@
 // slot and padding exists only in the tile map, never in memory (the local
 // "in-place padding" idea of the FlashMoE Kernel page, Communication section).
 //
-// No global atomics: each chunk of kChunk consecutive pairs is counted by one
+// No global atomics: each chunk of consecutive pairs is counted by one
 // wavefront into a [chunks x E] table; one workgroup scans it in (expert,
 // chunk) order; the scatter wavefront of each chunk re-ranks its pairs with
 // ballots so equal experts keep increasing q = t*k + j order.
@@ -30,13 +30,13 @@ __device__ __forceinline__ uint64_t match_lanes(int e, int nbits, bool active) {
 }
 
 __global__ __launch_bounds__(64) void hist_kernel(const int32_t* __restrict__ ids, int n,
-                                                  int E, int32_t* __restrict__ table) {
+                                                  int E, int chunk, int32_t* __restrict__ table) {
   extern __shared__ int32_t cnt[];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   __syncthreads();
-  const int q0 = blockIdx.x * kPermuteChunk;
-  const int q1 = min(n, q0 + kPermuteChunk);
+  const int q0 = blockIdx.x * chunk;
+  const int q1 = min(n, q0 + chunk);
   for (int q = q0 + lane; q < q1; q += 64) atomicAdd(&cnt[ids[q]], 1);  // LDS integer add
   __syncthreads();
   for (int e = lane; e < E; e += 64) table[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
 }
 
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int n,
-                                                     int k, int E, int nbits,
+                                                     int k, int E, int nbits, int chunk,
                                                      const int32_t* __restrict__ table,
                                                      int32_t* __restrict__ slot_token,
                                                      int32_t* __restrict__ slot_k,
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) base[e] = table[static_cast<size_t>(blockIdx.x) * E + e];
   __syncthreads();
-  const int q0 = blockIdx.x * kPermuteChunk;
-  const int q1 = min(n, q0 + kPermuteChunk);
+  const int q0 = blockIdx.x * chunk;
+  const int q1 = min(n, q0 + chunk);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int qb = q0; qb < q1; qb += 64) {
     const int q = qb + lane;
@@ -140,15 +140,16 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int bm, int32_t* ta
                     int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_k,
                     int32_t* token_slot, TileMap tm, hipStream_t s) {
   const int n = T * k;
-  const int nchunk = (n + kPermuteChunk - 1) / kPermuteChunk;
+  const int chunk = permute_chunk(n);
+  const int nchunk = (n + chunk - 1) / chunk;
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   const size_t lds = sizeof(int32_t) * static_cast<size_t>(E);
-  if (nchunk > 0) hist_kernel<<<nchunk, 64, lds, s>>>(ids, n, E, table);
+  if (nchunk > 0) hist_kernel<<<nchunk, 64, lds, s>>>(ids, n, E, chunk, table);
   scan_kernel<<<1, 1024, 0, s>>>(table, nchunk, E, bm, counts, offsets, tm);
   if (nchunk > 0)
-    scatter_kernel<<<nchunk, 64, lds, s>>>(ids, n, k, E, nbits, table, slot_token, slot_k,
-                                           token_slot);
+    scatter_kernel<<<nchunk, 64, lds, s>>>(ids, n, k, E, nbits, chunk, table, slot_token,
+                                           slot_k, token_slot);
 }
 
 }  // namespace moe

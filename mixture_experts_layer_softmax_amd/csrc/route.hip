@@ -15,19 +15,26 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouteKB = 32;  // hidden-dim chunk staged per LDS tile
+constexpr int kRoutePad = 4;  // floats of padding per LDS row (keeps float4 alignment)
 
-// Block of 256 threads = 16 x 16 lanes; lane (ty, tx) owns tokens
-// t0 + ty + 16 a (a < RT) and experts e0 + tx + 16 b (b < RE).
-template <int RT, int RE, bool BF16>
+// Block of 256 threads = TYL x TXL lanes; lane (ty, tx) owns tokens
+// t0 + ty * RT + a (a < RT) and experts e0 + tx * RE + b (b < RE).  LDS holds
+// x[t][i] and gate_w[i][e] of the chunk already widened to fp32, both with the
+// hidden index contiguous, so a lane reads four consecutive i of one row with
+// one float4 load and then runs its RT x RE chains four FMA steps, i
+// ascending -- the fixed summation order is untouched by the blocking.
+template <int RT, int RE, int TYL, int TXL, int kRouteKB, bool BF16>
 __global__ __launch_bounds__(256) void logits_kernel(
     const void* __restrict__ xv, const void* __restrict__ wv,
     const float* __restrict__ bias, float* __restrict__ logits, int T, int d,
     int E) {
-  constexpr int TT = 16 * RT, TE = 16 * RE;
-  __shared__ float xs[kRouteKB][TT + 1];  // [i][token]
-  __shared__ float ws[kRouteKB][TE + 1];  // [i][expert]
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  static_assert(TYL * TXL == 256, "256 threads");
+  constexpr int TT = TYL * RT, TE = TXL * RE;
+  constexpr int LD = kRouteKB + kRoutePad;
+  constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte global load
+  __shared__ __attribute__((aligned(16))) float xs[TT][LD];  // [token][i]
+  __shared__ __attribute__((aligned(16))) float ws[TE][LD];  // [expert][i]
+  const int tid = threadIdx.x, tx = tid % TXL, ty = tid / TXL;
   const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
   float acc[RT][RE];
 #pragma unroll
@@ -36,51 +43,93 @@ __global__ __launch_bounds__(256) void logits_kernel(
     for (int b = 0; b < RE; ++b) acc[a][b] = 0.0f;
 
   for (int i0 = 0; i0 < d; i0 += kRouteKB) {
-    // stage x[t0 .. t0+TT)[i0 .. i0+KB) transposed, and w[i0 ..][e0 ..)
-    for (int idx = tid; idx < TT * kRouteKB; idx += 256) {
-      int tl = idx / kRouteKB, il = idx % kRouteKB;
-      int t = t0 + tl, i = i0 + il;
-      float v = 0.0f;
+    // x chunk: TT rows of KB elements, 16-byte loads along i
+    for (int idx = tid; idx < TT * (kRouteKB / EPC); idx += 256) {
+      const int tl = idx / (kRouteKB / EPC), il = (idx % (kRouteKB / EPC)) * EPC;
+      const int t = t0 + tl, i = i0 + il;
+      float v[EPC];
       if (t < T && i < d) {
-        size_t o = static_cast<size_t>(t) * d + i;
-        v = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[o])
-                 : static_cast<const float*>(xv)[o];
+        const size_t o = static_cast<size_t>(t) * d + i;
+        if (BF16) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xv) + o);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __uint_as_float(raw[q] << 16);
+            v[2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
+          }
+        } else {
+          const f32x4 raw = *reinterpret_cast<const f32x4*>(static_cast<const float*>(xv) + o);
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) v[q] = raw[q];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) v[q] = 0.0f;
       }
-      xs[il][tl] = v;
+#pragma unroll
+      for (int q = 0; q < EPC; q += 4)
+        *reinterpret_cast<f32x4*>(&xs[tl][il + q]) = f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
     }
-    for (int idx = tid; idx < TE * kRouteKB; idx += 256) {
-      int il = idx / TE, el = idx % TE;
-      int e = e0 + el, i = i0 + il;
-      float v = 0.0f;
-      if (e < E && i < d) {
-        size_t o = static_cast<size_t>(i) * E + e;
-        v = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])
-                 : static_cast<const float*>(wv)[o];
+    // gate_w chunk: KB rows of TE experts (expert index contiguous in
+    // memory), stored transposed so the hidden index is contiguous in LDS
+    for (int idx = tid; idx < kRouteKB * (TE / EPC); idx += 256) {
+      const int il = idx / (TE / EPC), el = (idx % (TE / EPC)) * EPC;
+      const int e = e0 + el, i = i0 + il;
+      float v[EPC];
+      if (i < d && E % EPC == 0 && e + EPC <= E) {  // aligned 16-byte load
+        const size_t o = static_cast<size_t>(i) * E + e;
+        if (BF16) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wv) + o);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __uint_as_float(raw[q] << 16);
+            v[2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
+          }
+        } else {
+          const f32x4 raw = *reinterpret_cast<const f32x4*>(static_cast<const float*>(wv) + o);
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) v[q] = raw[q];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) {
+          const int eq = e + q;
+          float val = 0.0f;
+          if (i < d && eq < E) {
+            const size_t o = static_cast<size_t>(i) * E + eq;
+            val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])
+                       : static_cast<const float*>(wv)[o];
+          }
+          v[q] = val;
+        }
       }
-      ws[il][el] = v;
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) ws[el + q][il] = v[q];
     }
     __syncthreads();
-    const int iend = min(kRouteKB, d - i0);
-    for (int il = 0; il < iend; ++il) {
-      float xr[RT], wr[RE];
+    const int iend = min(kRouteKB, d - i0);  // d % 8 == 0, so iend % 4 == 0
+    for (int il = 0; il < iend; il += 4) {
+      f32x4 xr[RT], wr[RE];
 #pragma unroll
-      for (int a = 0; a < RT; ++a) xr[a] = xs[il][ty + 16 * a];
+      for (int a = 0; a < RT; ++a) xr[a] = *reinterpret_cast<const f32x4*>(&xs[ty * RT + a][il]);
 #pragma unroll
-      for (int b = 0; b < RE; ++b) wr[b] = ws[il][tx + 16 * b];
+      for (int b = 0; b < RE; ++b) wr[b] = *reinterpret_cast<const f32x4*>(&ws[tx * RE + b][il]);
 #pragma unroll
-      for (int a = 0; a < RT; ++a)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int b = 0; b < RE; ++b) acc[a][b] = __builtin_fmaf(xr[a], wr[b], acc[a][b]);
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+          for (int b = 0; b < RE; ++b) acc[a][b] = __builtin_fmaf(xr[a][u], wr[b][u], acc[a][b]);
     }
     __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < RT; ++a) {
-    int t = t0 + ty + 16 * a;
+    const int t = t0 + ty * RT + a;
     if (t >= T) continue;
 #pragma unroll
     for (int b = 0; b < RE; ++b) {
-      int e = e0 + tx + 16 * b;
+      const int e = e0 + tx * RE + b;
       if (e >= E) continue;
       float l = acc[a][b];
       if (bias) l = l + bias[e];
@@ -164,27 +213,44 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 void launch_logits(const void* x, const void* gate_w, const float* bias, float* logits,
                    int T, int d, int E, bool bf16, hipStream_t s) {
-  // Enough blocks to fill the chip first, then the largest register blocking.
-  auto go = [&](auto rt, auto re) {
-    constexpr int RT = decltype(rt)::value, RE = decltype(re)::value;
-    dim3 grid((T + 16 * RT - 1) / (16 * RT), (E + 16 * RE - 1) / (16 * RE));
-    if (bf16)
-      logits_kernel<RT, RE, true><<<grid, 256, 0, s>>>(x, gate_w, bias, logits, T, d, E);
-    else
-      logits_kernel<RT, RE, false><<<grid, 256, 0, s>>>(x, gate_w, bias, logits, T, d, E);
+  // Largest register blocking that still gives the chip >= 256 workgroups
+  // and does not leave most expert lanes idle.
+  struct Cfg {
+    int rt, re, tyl, txl;
   };
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I4 = std::integral_constant<int, 4>;
-  const long long big = static_cast<long long>(T) * E;
-  if (big >= (1ll << 22) && E >= 64)
-    go(I4{}, I4{});
-  else if (big >= (1ll << 20))
-    go(I4{}, I2{});
-  else if (big >= (1ll << 17))
-    go(I2{}, I1{});
-  else
-    go(I1{}, I1{});
+  // KB (hidden chunk per LDS tile) is 32 for the blocked shapes and 128 for
+  // the one-output-per-lane shapes of small T, where per-chunk latency
+  // dominates.
+  static constexpr Cfg cfgs[] = {{8, 4, 16, 16}, {4, 4, 16, 16}, {2, 4, 32, 8},
+                                 {2, 2, 16, 16}, {1, 2, 32, 8},  {1, 1, 16, 16}};
+  int pick = 5;
+  for (int c = 0; c < 5; ++c) {
+    const int TT = cfgs[c].tyl * cfgs[c].rt, TE = cfgs[c].txl * cfgs[c].re;
+    const long long wgs = static_cast<long long>((T + TT - 1) / TT) * ((E + TE - 1) / TE);
+    if (TE <= E && wgs >= 512) {  // two or more workgroups per CU
+      pick = c;
+      break;
+    }
+  }
+  auto go = [&](auto kern, int TT, int TE) {
+    dim3 grid((T + TT - 1) / TT, (E + TE - 1) / TE);
+    kern<<<grid, 256, 0, s>>>(x, gate_w, bias, logits, T, d, E);
+  };
+#define MOE_L(C, RT, RE, TYL, TXL, KB)                                                    \
+  if (pick == C) {                                                                        \
+    if (bf16)                                                                             \
+      go(logits_kernel<RT, RE, TYL, TXL, KB, true>, TYL * RT, TXL * RE);                  \
+    else                                                                                  \
+      go(logits_kernel<RT, RE, TYL, TXL, KB, false>, TYL * RT, TXL * RE);                 \
+    return;                                                                               \
+  }
+  MOE_L(0, 8, 4, 16, 16, 32)
+  MOE_L(1, 4, 4, 16, 16, 32)
+  MOE_L(2, 2, 4, 32, 8, 32)
+  MOE_L(3, 2, 2, 16, 16, 32)
+  MOE_L(4, 1, 2, 32, 8, 128)
+  MOE_L(5, 1, 1, 16, 16, 128)
+#undef MOE_L
 }
 
 void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
