@@ -12,7 +12,7 @@
 // Phase 2 (W2): h rows of an m-tile times the expert's down weights, fp32 Y.
 //
 // Scheduling: a persistent grid sized from occupancy pulls (m-tile, n-tile)
-// tasks from an integer atomic counter -- a work-conserving device-side tile
+// tasks from integer atomic counters -- a work-conserving device-side tile
 // queue (FlashMoE Kernel page, Architecture: the scheduler hands out work by
 // readiness; MegaMoE-vs-MoE-systems page, section 2.7: a global atomic task
 // counter).  Skewed experts simply own more tasks; idle CUs keep pulling.
@@ -20,13 +20,20 @@
 // stored (FlashMoE Kernel page, Communication: padding is local, just before
 // compute).
 //
+// Operand pipeline: an NS-stage LDS ring.  Each stage holds KRB bytes of the
+// contraction axis for the BM activation rows and the BN weight rows, filled
+// by direct global->LDS loads (global_load_lds_dwordx4: lane L of a wave
+// writes 16 bytes at the wave's LDS base + 16 L) issued NS-1 stages ahead, so
+// up to (NS-1) stages of both operands are in flight per CU without passing
+// through VGPRs.  Each wave waits only for its own loads of the stage it is
+// about to use (vmcnt), then one barrier publishes the stage.  The source
+// address of each lane is chosen so that rows land XOR-swizzled by 16-byte
+// chunk, which keeps the MFMA fragment reads free of LDS bank conflicts.
+//
 // MFMA mapping: the weight fragment is the MFMA "A" operand and the token
 // fragment the "B" operand, so the 16x16 result tile is D[n][slot]: lane l
 // holds n = 4*(l/16) + r (r = 0..3) of slot l%16 -- four consecutive output
-// columns of one row, which makes every epilogue store a 8- or 16-byte
-// vector and puts gate/up pairs in the same lane.
-// LDS rows are 128 bytes of K (64 bf16, 32 fp32 or 128 fp8) split in eight
-// 16-byte chunks stored XOR-swizzled by (row & 7).
+// columns of one row, which puts gate/up pairs in the same lane.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -37,8 +44,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kRowBytes = 128;
-
 template <int DT>
 struct ESize;
 template <>
@@ -48,53 +53,116 @@ struct ESize<kBF16> { static constexpr int v = 2; };
 template <>
 struct ESize<kFP8> { static constexpr int v = 1; };
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
+
+// Compile-time geometry of one kernel variant.
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_ = (DT == kF32 ? 64 : 128)>
+struct Geo {
+  static constexpr int NW = WM * WN;
+  static constexpr int kThreads = NW * 64;
+  static constexpr int ES = ESize<DT>::v;
+  // contraction bytes per LDS row and stage: two 16x16x32 bf16 MFMA steps,
+  // four 16x16x4 fp32 steps, or one 16x16x128 FP8 step.  128-byte rows keep
+  // every DMA request a whole cache line and halve the barriers per MFMA.
+  static constexpr int KRB = KRB_;
+  static constexpr int ROWS_PER_DMA = 1024 / KRB;  // rows one wave-wide DMA load fills
+  static constexpr int ABLK = BM / ROWS_PER_DMA, BBLK = BN / ROWS_PER_DMA;
+  static constexpr int AW = (ABLK + NW - 1) / NW, BW = (BBLK + NW - 1) / NW;
+  static constexpr int SA_DMA = (DT == kFP8) ? (BM + 63) / 64 : 0;  // A-scale dword DMAs
+  static constexpr int SCALE_BYTES = SA_DMA * 256;                    // per stage
+  static constexpr int STAGE = (BM + BN) * KRB + SCALE_BYTES;
+  static constexpr int RED = (DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0;
+  static constexpr int NS0 = (kLdsBytes - RED) / STAGE;
+  static constexpr int NS = NS0 > 4 ? 4 : NS0;
+  static constexpr int EPI =
+      (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : 4);
+  static constexpr int RING = NS * STAGE;
+  static constexpr int LDS = (RING > EPI ? RING : EPI) + RED;
+  static_assert(NS >= 2, "at least two LDS stages");
+  static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMA == 0, "whole DMA blocks");
+};
+
+// LDS byte offset of 16-byte chunk c of row r in a tile of KRB-byte rows.
+// The XOR key makes the 16 rows read by one quarter-wave ds_read_b128 hit
+// 16 distinct 4-bank groups (64 banks of 4 bytes).
+template <int KRB>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (KRB == 64)
+    return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+  else
+    return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// s_waitcnt vmcnt(n) that leaves expcnt and lgkmcnt alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define MOE_W(N)                                                                        \
+  case N:                                                                               \
+    __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)); \
+    break;
+  switch (n) {
+    MOE_W(0) MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7)
+    MOE_W(8) MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15)
+    MOE_W(16) MOE_W(17) MOE_W(18) MOE_W(19) MOE_W(20) MOE_W(21) MOE_W(22) MOE_W(23)
+    MOE_W(24) MOE_W(25) MOE_W(26) MOE_W(27) MOE_W(28) MOE_W(29) MOE_W(30) MOE_W(31)
+    default:
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      break;
+  }
+#undef MOE_W
+}
+
+// Direct global -> LDS loads; the LDS pointer must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
 }
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
-// Bytes of LDS shared by the main-loop stages and the epilogue staging.
-template <int DT, int PHASE, int BM, int BN, int WM>
-struct StageBytes {
-  static constexpr int main_loop = 2 * (BM + BN) * kRowBytes;
-  static constexpr int epilogue = (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) *
-                                  ((PHASE == 1) ? ESize<DT>::v : 4);
-  static constexpr int v = main_loop > epilogue ? main_loop : epilogue;
-};
+// Workgroup barrier for the DMA ring.  __syncthreads() also emits a release
+// fence whose s_waitcnt vmcnt(0) would drain every stage in flight; LDS needs
+// no cache maintenance, each wave has already waited for its own loads of the
+// stage (vmcnt) and for its LDS reads of the slot being refilled (their
+// results fed the MFMAs), so a bare s_barrier suffices.  The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int DT, int PHASE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
-  constexpr int kThreads = WM * WN * 64;
-  constexpr int ES = ESize<DT>::v;
+  using G = Geo<DT, PHASE, BM, BN, WM, WN>;
+  constexpr int kThreads = G::kThreads, ES = G::ES, KRB = G::KRB, NS = G::NS;
+  constexpr int NW = G::NW, RPD = G::ROWS_PER_DMA;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int ACH = BM * 8, BCH = BN * 8;  // 16-byte chunks per K-step
-  constexpr int RA = (ACH + kThreads - 1) / kThreads;
-  constexpr int RB = (BCH + kThreads - 1) / kThreads;
-  static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(PHASE == 2 || TN % 2 == 0, "gate/up pairs");
   static_assert(!(DT == kFP8 && PHASE == 1) || BN == 256, "FP8 h groups of 128 f");
 
-  // LDS: the two K-step stages of A and B, reused by the epilogue staging,
-  // then (FP8 phase 1) the per-wave row maxima
+  // LDS: NS stages of [BM rows A | BN rows B | BM A-scales (FP8)], reused by
+  // the epilogue staging; then (FP8 phase 1) the per-wave row maxima.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* As = lds;                                  // [2][BM][128]
-  uint8_t* Bs = lds + 2 * BM * kRowBytes;             // [2][BN][128]
-  float* red = reinterpret_cast<float*>(lds + StageBytes<DT, PHASE, BM, BN, WM>::v);  // [WN][BM]
+  float* red = reinterpret_cast<float*>(lds + (G::RING > G::EPI ? G::RING : G::EPI));
   __shared__ int s_task;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, lg = lane >> 4;
   const int64_t K = g.K, N = g.N;
-  const int ksteps = static_cast<int>(K * ES / kRowBytes);
+  const int ksteps = static_cast<int>(K * ES / KRB);
   const int kblocks = static_cast<int>(K / 128);  // FP8 scale blocks along K
   const int nblocks = static_cast<int>(N / 128);
-  // XCD-aware work queue.  Workgroups of a persistent launch are dealt to the
-  // eight XCDs round-robin, so workgroup b runs on XCD b % 8 and shares that
-  // XCD's L2 with the others there.  The m-tiles are cut into chunks of kGM
+
+  // XCD-aware work queue.  Each workgroup reads the XCD it runs on from the
+  // XCC_ID hardware register and shares that XCD's L2 with the workgroups
+  // there.  The m-tiles are cut into chunks of kGM
   // consecutive m-tiles; chunk c belongs to XCD c % 8, whose workgroups take
   // its tasks n-tile by n-tile (kGM m-tiles x n-tiles in flight per XCD:
   // activation rows reused across n-tiles and weight rows across m-tiles in
@@ -104,7 +172,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
   const int M = *g.tm.n_mtiles, NT = g.n_tiles_n;
   const int nchunks = (M + kGM - 1) / kGM;
   const int chunk_tasks = kGM * NT;
-  const int xcd = static_cast<int>(blockIdx.x) % kXcd;
+  // s_getreg_b32 hwreg(HW_REG_XCC_ID, 0, 4): id of this XCD
+  const int xcd = __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kXcd - 1);
   int* queue = g.tm.queue + kXcd * g.queue_idx;
 
   for (;;) {
@@ -130,32 +199,44 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       s_task = task;
     }
     __syncthreads();
-    const int task = s_task;
+    const int task = __builtin_amdgcn_readfirstlane(s_task);
     if (task < 0) break;
-    const int mt = task / g.n_tiles_n;
-    const int nt = task - mt * g.n_tiles_n;
-    const int e = g.tm.e[mt], row0 = g.tm.row0[mt], rows = g.tm.rows[mt];
+    const int mt = task / NT;
+    const int nt = task - mt * NT;
+    const int e = __builtin_amdgcn_readfirstlane(g.tm.e[mt]);
+    const int row0 = __builtin_amdgcn_readfirstlane(g.tm.row0[mt]);
+    const int rows = __builtin_amdgcn_readfirstlane(g.tm.rows[mt]);
     const int64_t n0 = static_cast<int64_t>(nt) * BN;
 
-    // ---- source of every 16-byte chunk this thread stages: 32-bit byte
-    // offsets from wave-uniform bases (the host checks that every operand
-    // spans less than 2^31 bytes per expert) ----
-    const int64_t w_bytes = N * K * ES;  // one expert's weight matrix
+    // ---- DMA sources of this lane: 32-bit byte offsets from wave-uniform
+    // bases (the host checks that x, h and one expert's weight matrix each
+    // span less than 2^31 bytes).  A wave-wide DMA fills RPD rows of KRB
+    // bytes; lane L fills row L / (KRB/16), physical chunk L % (KRB/16), so it
+    // loads the logical chunk that the swizzle maps there. ----
+    const int64_t w_bytes = N * K * ES;
     const uint8_t* b0 = g.B0 + static_cast<int64_t>(e) * w_bytes;
     const uint8_t* b1 = (PHASE == 1) ? g.B1 + static_cast<int64_t>(e) * w_bytes : b0;
-    uint32_t oa[RA], ob[RB];
-    uint32_t up_mask = 0;  // bit j: chunk j of B comes from the up (W3) matrix
+    constexpr int CPRK = KRB / 16;  // 16-byte chunks per LDS row
+    const int lrow = lane / CPRK, lphys = lane % CPRK;
+    uint32_t oa[G::AW], ob[G::BW];
+    uint32_t up_mask = 0;  // bit j: B block j of this wave comes from W3 (up)
+    int my_loads = 0;      // DMA instructions this wave issues per stage
 #pragma unroll
-    for (int j = 0; j < RA; ++j) {
-      const int ci = tid + kThreads * j;
-      const int r = min(ci >> 3, rows - 1);  // padding rows re-read a valid row
-      const int64_t src = g.gather ? g.gather[row0 + r] : static_cast<int64_t>(row0 + r);
-      oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + (ci & 7) * 16);
+    for (int j = 0; j < G::AW; ++j) {
+      const int q = wave + NW * j;
+      const int r = q * RPD + lrow;
+      const int logical = lphys ^ ((KRB == 64) ? ((r >> 2) & 3) : ((r >> 1) & 7));
+      const int rr = min(r, rows - 1);  // padding rows re-read a valid row
+      const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
+      oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + logical * 16);
+      if (q < G::ABLK) ++my_loads;
     }
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int ci = tid + kThreads * j;
-      const int64_t n = n0 + (ci >> 3);
+    for (int j = 0; j < G::BW; ++j) {
+      const int q = wave + NW * j;
+      const int r = q * RPD + lrow;
+      const int logical = lphys ^ ((KRB == 64) ? ((r >> 2) & 3) : ((r >> 1) & 7));
+      const int64_t n = n0 + r;
       int64_t col;
       if (PHASE == 1) {  // combined rows: 16 gate rows, then 16 up rows, per f block
         col = (n >> 5) * 16 + (n & 15);
@@ -164,49 +245,33 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
         col = n;
       }
       col = min(col, N - 1);
-      ob[j] = static_cast<uint32_t>(col * K * ES + (ci & 7) * 16);
+      ob[j] = static_cast<uint32_t>(col * K * ES + logical * 16);
+      if (q < G::BBLK) ++my_loads;
     }
-
-    // Prefetch registers of the next K-step.  Written with plain loops (no
-    // lambdas capturing the arrays by reference), so they stay in VGPRs.
-    u32x4 ra[RA], rb[RB];
-#define MOE_GLOAD(KS)                                                                   \
-  do {                                                                                  \
-    const uint32_t off_ = static_cast<uint32_t>(KS) * kRowBytes;                        \
-    _Pragma("unroll") for (int j = 0; j < RA; ++j) if (ACH % kThreads == 0 ||            \
-                                                        tid + kThreads * j < ACH)       \
-        ra[j] = *reinterpret_cast<const u32x4*>(g.A + (oa[j] + off_));                  \
-    _Pragma("unroll") for (int j = 0; j < RB; ++j) if (BCH % kThreads == 0 ||            \
-                                                        tid + kThreads * j < BCH)       \
-        rb[j] = *reinterpret_cast<const u32x4*>(((up_mask >> j) & 1u ? b1 : b0) +       \
-                                                (ob[j] + off_));                        \
-  } while (0)
-#define MOE_LSTORE(BUF)                                                                 \
-  do {                                                                                  \
-    _Pragma("unroll") for (int j = 0; j < RA; ++j) {                                    \
-      const int ci = tid + kThreads * j;                                                \
-      if (ACH % kThreads == 0 || ci < ACH)                                              \
-        *reinterpret_cast<u32x4*>(As + (BUF) * BM * kRowBytes + swz(ci >> 3, ci & 7)) = \
-            ra[j];                                                                      \
-    }                                                                                   \
-    _Pragma("unroll") for (int j = 0; j < RB; ++j) {                                    \
-      const int ci = tid + kThreads * j;                                                \
-      if (BCH % kThreads == 0 || ci < BCH)                                              \
-        *reinterpret_cast<u32x4*>(Bs + (BUF) * BN * kRowBytes + swz(ci >> 3, ci & 7)) = \
-            rb[j];                                                                      \
-    }                                                                                   \
-  } while (0)
-
-    // FP8: per token fragment i, the A-scale row offset of the lane's slot
-    uint32_t sa_off[TM];
+    const float* sa_src = g.sa;  // FP8: this lane's A-row scale row
     if constexpr (DT == kFP8) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = min(wm * WTM + 16 * i + l16, rows - 1);
-        const int64_t src = g.gather ? g.gather[row0 + r] : static_cast<int64_t>(row0 + r);
-        sa_off[i] = static_cast<uint32_t>(src * kblocks);
-      }
+      const int rr = min(wave * 64 + lane, rows - 1);
+      const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
+      sa_src = g.sa + src * kblocks;
+      if (wave < G::SA_DMA) ++my_loads;
     }
+
+#define MOE_ISSUE(KS)                                                                    \
+  do {                                                                                   \
+    uint8_t* st_ = lds + ((KS) % NS) * G::STAGE;                                         \
+    const uint32_t ko_ = static_cast<uint32_t>(KS) * KRB;                                \
+    _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                  \
+      const int q = wave + NW * j;                                                       \
+      if (q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024);                       \
+    }                                                                                    \
+    _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                  \
+      const int q = wave + NW * j;                                                       \
+      if (q < G::BBLK)                                                                   \
+        dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + ko_), st_ + BM * KRB + q * 1024); \
+    }                                                                                    \
+    if (DT == kFP8 && wave < G::SA_DMA)                                                  \
+      dma4(sa_src + (KS), st_ + (BM + BN) * KRB + wave * 256);                           \
+  } while (0)
 
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -214,59 +279,74 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    MOE_GLOAD(0);
-    MOE_LSTORE(0);
-    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < ksteps) MOE_ISSUE(p);
+
     for (int ks = 0; ks < ksteps; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < ksteps) MOE_GLOAD(ks + 1);
-      const uint8_t* Ab = As + cur * BM * kRowBytes;
-      const uint8_t* Bb = Bs + cur * BN * kRowBytes;
+      // my loads of stage ks have landed once at most `ahead` later stages
+      // are still in flight; the barrier then publishes everyone's loads and
+      // guarantees every wave is done with the slot reloaded below
+      const int ahead = min(NS - 2, ksteps - 1 - ks);
+      wait_vmcnt(ahead * my_loads);
+      ring_barrier();
+      if (ks + NS - 1 < ksteps) MOE_ISSUE(ks + NS - 1);
+      const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
+      const uint8_t* Bb = Ab + BM * KRB;
+      // A wave whose rows are all padding skips the step; a partly valid
+      // wave computes its padding rows too (their results are never stored),
+      // which keeps the fragment loop free of branches.
+      if (wm * WTM >= rows) continue;
       if constexpr (DT == kBF16) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < KRB / 64; ++kk) {
           bf16x8 wf[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            wf[j] = *reinterpret_cast<const bf16x8*>(Bb + swz(wn * WTN + 16 * j + l16, kk * 4 + lg));
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            if (wm * WTM + 16 * i >= rows) break;  // padding rows only: wave-uniform
-            const bf16x8 xf =
-                *reinterpret_cast<const bf16x8*>(Ab + swz(wm * WTM + 16 * i + l16, kk * 4 + lg));
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf, acc[i][j], 0, 0, 0);
-          }
+            wf[j] = *reinterpret_cast<const bf16x8*>(
+                Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
+#define MOE_BF16_ROWS(SKIP)                                                               \
+  bf16x8 xf[TM];                                                                          \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>( \
+      Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));                               \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+    if (SKIP) break;                                                                      \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0); \
+  }                                                                                       \
+  /* issue every fragment read of the step before the MFMAs (LDS latency  */              \
+  /* then overlaps the MFMAs instead of stalling each pair of fragments)  */              \
+  __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                                \
+  __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+          MOE_BF16_ROWS(false)
+#undef MOE_BF16_ROWS
         }
       } else if constexpr (DT == kF32) {
+        f32x4 wf[TN];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          f32x4 wf[TN];
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz(wn * WTN + 16 * j + l16, kk * 4 + lg));
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            if (wm * WTM + 16 * i >= rows) break;
-            const f32x4 xf =
-                *reinterpret_cast<const f32x4*>(Ab + swz(wm * WTM + 16 * i + l16, kk * 4 + lg));
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-              for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[u], acc[i][j], 0, 0, 0);
-          }
-        }
-      } else {  // FP8: one 16x16x128 MFMA per fragment pair and K block
+        for (int j = 0; j < TN; ++j)
+          wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz<KRB>(wn * WTN + 16 * j + l16, lg));
+#define MOE_F32_ROWS(SKIP)                                                                \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+    if (SKIP) break;                                                                      \
+    const f32x4 xf =                                                                      \
+        *reinterpret_cast<const f32x4*>(Ab + swz<KRB>(wm * WTM + 16 * i + l16, lg));      \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                         \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[u], acc[i][j], 0, 0, 0); \
+  }
+        MOE_F32_ROWS(false)
+#undef MOE_F32_ROWS
+      } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
         i32x8 wf[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int r = wn * WTN + 16 * j + l16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz(r, 2 * lg));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz(r, 2 * lg + 1));
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
           wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
+        const float* sa_st = reinterpret_cast<const float*>(Bb + BN * KRB);
         float s_b0, s_b1 = 0.f;
         if (PHASE == 1) {
           const int fb = static_cast<int>(n0 / 256);  // 128 f columns per workgroup tile
@@ -276,35 +356,30 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
           const int nb = static_cast<int>((n0 + wn * WTN) / 128);
           s_b0 = g.sb0[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + nb];
         }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          if (wm * WTM + 16 * i >= rows) break;  // padding rows only: wave-uniform
-          const int r = wm * WTM + 16 * i + l16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz(r, 2 * lg));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz(r, 2 * lg + 1));
-          const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const float s_a = g.sa[sa_off[i] + ks];
-          const float sg = s_a * s_b0, su = s_a * s_b1;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0,
-                                                                              0, 127, 0, 127);
-            const float sc = (PHASE == 1 && (j & 1)) ? su : sg;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(p[q], sc, acc[i][j][q]);
-          }
-          // keep each fragment's MFMAs next to their rescale: hoisting all of
-          // them would hold TM x TN fresh results live and spill
-          __builtin_amdgcn_sched_barrier(0);
-        }
+#define MOE_FP8_ROWS(SKIP)                                                                \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+    if (SKIP) break;                                                                      \
+    const int r = wm * WTM + 16 * i + l16;                                                \
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));           \
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));       \
+    const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};       \
+    const float s_a = sa_st[r];                                                           \
+    const float sg = s_a * s_b0, su = s_a * s_b1;                                         \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                      \
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};                                               \
+      const f32x4 p =                                                                     \
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 127, 0, 127); \
+      const float sc = (PHASE == 1 && (j & 1)) ? su : sg;                                 \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) acc[i][j][q] =                        \
+          __builtin_fmaf(p[q], sc, acc[i][j][q]);                                         \
+    }                                                                                     \
+  }
+        MOE_FP8_ROWS(false)
+#undef MOE_FP8_ROWS
       }
-      if (ks + 1 < ksteps) MOE_LSTORE(cur ^ 1);
-      __syncthreads();
     }
-
-#undef MOE_GLOAD
-#undef MOE_LSTORE
+#undef MOE_ISSUE
+    __syncthreads();  // every wave is done with the ring before the epilogue reuses it
 
     // ---------------- epilogue ----------------
     // Output values are staged in LDS (free after the main loop's last
@@ -405,9 +480,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 template <int DT, int PHASE, int BM, int BN, int WM, int WN>
 struct Variant {
   static constexpr int kThreads = WM * WN * 64;
-  static constexpr int lds_bytes() {
-    return StageBytes<DT, PHASE, BM, BN, WM>::v + ((DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0);
-  }
+  static constexpr int lds_bytes() { return Geo<DT, PHASE, BM, BN, WM, WN>::LDS; }
   static int launch(const GemmArgs& a, hipStream_t s) {
     auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN>;
     static int grid = 0;
