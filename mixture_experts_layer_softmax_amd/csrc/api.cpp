@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "launch.hpp"
@@ -33,9 +34,21 @@ int pick_bm(const moe_problem& p) {
   if (r <= 48.0) return 32;
   if (r <= 160.0) return 64;
   if (r < 384.0) return 128;
-  // FP8 256-row tiles would need more than 256 VGPRs per lane at two waves
-  // per SIMD (32-byte operand fragments plus per-row scales)
-  return p.w_dtype == MOE_FP8_E4M3 ? 128 : 256;
+  return 256;
+}
+
+// m-tiles per XCD work chunk: about the m-tiles one expert fills (so the
+// expert's weight tiles are reused by all of them at once), between 1 and 8;
+// MOE_GROUP_M overrides it for tuning.
+int group_m(const moe_problem& p, int bm) {
+  static const int forced = [] {
+    const char* e = getenv("MOE_GROUP_M");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced > 0) return std::min(forced, 8);
+  const double r = static_cast<double>(p.T) * p.top_k / p.E / bm;
+  const int gm = static_cast<int>(r + 0.999);
+  return std::max(1, std::min(8, gm));
 }
 
 bool valid_problem(const moe_problem* p) {
@@ -295,6 +308,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   g1.tm = tm;
   g1.n_tiles_n = static_cast<int>(ceil_div(2 * p->f, moe::gemm_tile_n(1, gdt, L.bm)));
   g1.queue_idx = 0;
+  g1.group_m = group_m(*p, L.bm);
   st = from_code(moe::launch_gemm(1, gdt, L.bm, g1, stream));
   if (st != MOE_OK) return st;
   mark(4);
@@ -316,6 +330,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   g2.tm = tm;
   g2.n_tiles_n = static_cast<int>(ceil_div(p->d, moe::gemm_tile_n(2, gdt, L.bm)));
   g2.queue_idx = 1;
+  g2.group_m = g1.group_m;
   st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));
   if (st != MOE_OK) return st;
   mark(5);

@@ -162,13 +162,15 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 
   // XCD-aware work queue.  Each workgroup reads the XCD it runs on from the
   // XCC_ID hardware register and shares that XCD's L2 with the workgroups
-  // there.  The m-tiles are cut into chunks of kGM
-  // consecutive m-tiles; chunk c belongs to XCD c % 8, whose workgroups take
-  // its tasks n-tile by n-tile (kGM m-tiles x n-tiles in flight per XCD:
-  // activation rows reused across n-tiles and weight rows across m-tiles in
-  // one L2).  A drained XCD queue makes its workgroups steal from the others,
-  // so the queue stays work-conserving under routing skew.
-  constexpr int kXcd = 8, kGM = 4;
+  // there.  The m-tiles are cut into chunks of kGM consecutive m-tiles (kGM
+  // from the host: about the m-tiles of one expert, at most 8); chunk c
+  // belongs to XCD c % 8, whose workgroups take its tasks n-tile by n-tile,
+  // so the weight rows of an n-tile are shared by kGM concurrent m-tiles and
+  // the activation rows of an m-tile by the n-tiles in flight -- in one L2.
+  // A drained XCD queue makes its workgroups steal from the others, so the
+  // queue stays work-conserving under routing skew.
+  constexpr int kXcd = 8;
+  const int kGM = g.group_m;
   const int M = *g.tm.n_mtiles, NT = g.n_tiles_n;
   const int nchunks = (M + kGM - 1) / kGM;
   const int chunk_tasks = kGM * NT;

@@ -53,6 +53,7 @@ struct GemmArgs {
   TileMap tm;
   int n_tiles_n;          // column tiles per m-tile
   int queue_idx;
+  int group_m;            // m-tiles per XCD work chunk (1..8)
 };
 
 void launch_logits(const void* x, const void* gate_w, const float* bias, float* logits,
