@@ -19,21 +19,25 @@ constexpr int kRoutePad = 4;  // floats of padding per LDS row (keeps float4 ali
 
 // Block of 256 threads = TYL x TXL lanes; lane (ty, tx) owns tokens
 // t0 + ty * RT + a (a < RT) and experts e0 + tx * RE + b (b < RE).  LDS holds
-// x[t][i] and gate_w[i][e] of the chunk already widened to fp32, both with the
-// hidden index contiguous, so a lane reads four consecutive i of one row with
-// one float4 load and then runs its RT x RE chains four FMA steps, i
-// ascending -- the fixed summation order is untouched by the blocking.
-template <int RT, int RE, int TYL, int TXL, int kRouteKB, bool BF16>
+// x[t][i] and gate_w[i][e] of one hidden chunk already widened to fp32, both
+// with the hidden index contiguous, so a lane reads four consecutive i of one
+// row with one float4 load and then runs its RT x RE chains four FMA steps, i
+// ascending -- the fixed summation order is untouched by the blocking.  The
+// next chunk is loaded into registers while the current one is computed.
+template <int RT, int RE, int TYL, int TXL, int KB, bool BF16>
 __global__ __launch_bounds__(256) void logits_kernel(
     const void* __restrict__ xv, const void* __restrict__ wv,
     const float* __restrict__ bias, float* __restrict__ logits, int T, int d,
     int E) {
   static_assert(TYL * TXL == 256, "256 threads");
   constexpr int TT = TYL * RT, TE = TXL * RE;
-  constexpr int LD = kRouteKB + kRoutePad;
+  constexpr int LD = KB + kRoutePad;
   constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte global load
-  __shared__ __attribute__((aligned(16))) float xs[TT][LD];  // [token][i]
-  __shared__ __attribute__((aligned(16))) float ws[TE][LD];  // [expert][i]
+  constexpr int XCH = TT * (KB / EPC), WCH = KB * (TE / EPC);  // 16-byte chunks
+  constexpr int XR = (XCH + 255) / 256, WR = (WCH + 255) / 256;
+  extern __shared__ __attribute__((aligned(16))) float route_lds[];
+  float (*xs)[LD] = reinterpret_cast<float (*)[LD]>(route_lds);            // [TT][LD]
+  float (*ws)[LD] = reinterpret_cast<float (*)[LD]>(route_lds + TT * LD);  // [TE][LD]
   const int tid = threadIdx.x, tx = tid % TXL, ty = tid / TXL;
   const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
   float acc[RT][RE];
@@ -42,87 +46,110 @@ __global__ __launch_bounds__(256) void logits_kernel(
 #pragma unroll
     for (int b = 0; b < RE; ++b) acc[a][b] = 0.0f;
 
-  for (int i0 = 0; i0 < d; i0 += kRouteKB) {
-    // x chunk: TT rows of KB elements, 16-byte loads along i
-    for (int idx = tid; idx < TT * (kRouteKB / EPC); idx += 256) {
-      const int tl = idx / (kRouteKB / EPC), il = (idx % (kRouteKB / EPC)) * EPC;
-      const int t = t0 + tl, i = i0 + il;
-      float v[EPC];
-      if (t < T && i < d) {
-        const size_t o = static_cast<size_t>(t) * d + i;
-        if (BF16) {
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xv) + o);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[2 * q] = __uint_as_float(raw[q] << 16);
-            v[2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
-          }
-        } else {
-          const f32x4 raw = *reinterpret_cast<const f32x4*>(static_cast<const float*>(xv) + o);
-#pragma unroll
-          for (int q = 0; q < EPC; ++q) v[q] = raw[q];
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < EPC; ++q) v[q] = 0.0f;
-      }
-#pragma unroll
-      for (int q = 0; q < EPC; q += 4)
-        *reinterpret_cast<f32x4*>(&xs[tl][il + q]) = f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
-    }
-    // gate_w chunk: KB rows of TE experts (expert index contiguous in
-    // memory), stored transposed so the hidden index is contiguous in LDS
-    for (int idx = tid; idx < kRouteKB * (TE / EPC); idx += 256) {
-      const int il = idx / (TE / EPC), el = (idx % (TE / EPC)) * EPC;
-      const int e = e0 + el, i = i0 + il;
-      float v[EPC];
-      if (i < d && E % EPC == 0 && e + EPC <= E) {  // aligned 16-byte load
-        const size_t o = static_cast<size_t>(i) * E + e;
-        if (BF16) {
-          const u32x4 raw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wv) + o);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[2 * q] = __uint_as_float(raw[q] << 16);
-            v[2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
-          }
-        } else {
-          const f32x4 raw = *reinterpret_cast<const f32x4*>(static_cast<const float*>(wv) + o);
-#pragma unroll
-          for (int q = 0; q < EPC; ++q) v[q] = raw[q];
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < EPC; ++q) {
-          const int eq = e + q;
-          float val = 0.0f;
-          if (i < d && eq < E) {
-            const size_t o = static_cast<size_t>(i) * E + eq;
-            val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])
-                       : static_cast<const float*>(wv)[o];
-          }
-          v[q] = val;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < EPC; ++q) ws[el + q][il] = v[q];
-    }
+  // prefetch registers: raw 16-byte pieces of the next chunk (widened when
+  // stored to LDS); out-of-range pieces are zero
+  u32x4 xr[XR], wr[WR];
+  bool wvec[WR];  // piece loaded as one aligned 16-byte vector
+#define MOE_RLOAD(I0)                                                                    \
+  do {                                                                                   \
+    _Pragma("unroll") for (int r = 0; r < XR; ++r) {                                     \
+      const int idx = tid + 256 * r;                                                     \
+      const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;                    \
+      const int t = t0 + tl, i = (I0) + il;                                              \
+      xr[r] = u32x4{0u, 0u, 0u, 0u};                                                     \
+      if (idx < XCH && t < T && i < d) {                                                 \
+        const size_t o = static_cast<size_t>(t) * d + i;                                 \
+        xr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xv) + o) \
+                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(xv) + o); \
+      }                                                                                  \
+    }                                                                                    \
+    _Pragma("unroll") for (int r = 0; r < WR; ++r) {                                     \
+      const int idx = tid + 256 * r;                                                     \
+      const int il = idx / (TE / EPC), el = (idx % (TE / EPC)) * EPC;                    \
+      const int e = e0 + el, i = (I0) + il;                                              \
+      wr[r] = u32x4{0u, 0u, 0u, 0u};                                                     \
+      wvec[r] = idx < WCH && i < d && E % EPC == 0 && e + EPC <= E;                      \
+      if (wvec[r]) {                                                                     \
+        const size_t o = static_cast<size_t>(i) * E + e;                                 \
+        wr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wv) + o) \
+                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(wv) + o); \
+      }                                                                                  \
+    }                                                                                    \
+  } while (0)
+#define MOE_RSTORE(I0)                                                                   \
+  do {                                                                                   \
+    _Pragma("unroll") for (int r = 0; r < XR; ++r) {                                     \
+      const int idx = tid + 256 * r;                                                     \
+      if (idx < XCH) {                                                                   \
+        const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;                  \
+        float v[EPC];                                                                    \
+        if (BF16) {                                                                      \
+          _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
+            v[2 * q] = __uint_as_float(xr[r][q] << 16);                                  \
+            v[2 * q + 1] = __uint_as_float(xr[r][q] & 0xffff0000u);                      \
+          }                                                                              \
+        } else {                                                                         \
+          _Pragma("unroll") for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(xr[r][q]); \
+        }                                                                                \
+        _Pragma("unroll") for (int q = 0; q < EPC; q += 4) *reinterpret_cast<f32x4*>(    \
+            &xs[tl][il + q]) = f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};                \
+      }                                                                                  \
+    }                                                                                    \
+    _Pragma("unroll") for (int r = 0; r < WR; ++r) {                                     \
+      const int idx = tid + 256 * r;                                                     \
+      if (idx < WCH) {                                                                   \
+        const int il = idx / (TE / EPC), el = (idx % (TE / EPC)) * EPC;                  \
+        const int i = (I0) + il;                                                         \
+        float v[EPC];                                                                    \
+        if (wvec[r]) {                                                                   \
+          if (BF16) {                                                                    \
+            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                              \
+              v[2 * q] = __uint_as_float(wr[r][q] << 16);                                \
+              v[2 * q + 1] = __uint_as_float(wr[r][q] & 0xffff0000u);                    \
+            }                                                                            \
+          } else {                                                                       \
+            _Pragma("unroll") for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(wr[r][q]); \
+          }                                                                              \
+        } else {                                                                         \
+          _Pragma("unroll") for (int q = 0; q < EPC; ++q) {                              \
+            const int eq = e0 + el + q;                                                  \
+            float val = 0.0f;                                                            \
+            if (i < d && eq < E) {                                                       \
+              const size_t o = static_cast<size_t>(i) * E + eq;                          \
+              val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])              \
+                         : static_cast<const float*>(wv)[o];                             \
+            }                                                                            \
+            v[q] = val;                                                                  \
+          }                                                                              \
+        }                                                                                \
+        _Pragma("unroll") for (int q = 0; q < EPC; ++q) ws[el + q][il] = v[q];           \
+      }                                                                                  \
+    }                                                                                    \
+  } while (0)
+
+  MOE_RLOAD(0);
+  for (int i0 = 0; i0 < d; i0 += KB) {
+    MOE_RSTORE(i0);
     __syncthreads();
-    const int iend = min(kRouteKB, d - i0);  // d % 8 == 0, so iend % 4 == 0
+    if (i0 + KB < d) MOE_RLOAD(i0 + KB);  // in flight during this chunk's FMAs
+    const int iend = min(KB, d - i0);     // d % 8 == 0, so iend % 4 == 0
     for (int il = 0; il < iend; il += 4) {
-      f32x4 xr[RT], wr[RE];
+      f32x4 xv4[RT], wv4[RE];
 #pragma unroll
-      for (int a = 0; a < RT; ++a) xr[a] = *reinterpret_cast<const f32x4*>(&xs[ty * RT + a][il]);
+      for (int a = 0; a < RT; ++a) xv4[a] = *reinterpret_cast<const f32x4*>(&xs[ty * RT + a][il]);
 #pragma unroll
-      for (int b = 0; b < RE; ++b) wr[b] = *reinterpret_cast<const f32x4*>(&ws[tx * RE + b][il]);
+      for (int b = 0; b < RE; ++b) wv4[b] = *reinterpret_cast<const f32x4*>(&ws[tx * RE + b][il]);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll
-          for (int b = 0; b < RE; ++b) acc[a][b] = __builtin_fmaf(xr[a][u], wr[b][u], acc[a][b]);
+          for (int b = 0; b < RE; ++b) acc[a][b] = __builtin_fmaf(xv4[a][u], wv4[b][u], acc[a][b]);
     }
     __syncthreads();
   }
+#undef MOE_RLOAD
+#undef MOE_RSTORE
 #pragma unroll
   for (int a = 0; a < RT; ++a) {
     const int t = t0 + ty * RT + a;
@@ -218,9 +245,9 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
   struct Cfg {
     int rt, re, tyl, txl;
   };
-  // KB (hidden chunk per LDS tile) is 32 for the blocked shapes and 128 for
-  // the one-output-per-lane shapes of small T, where per-chunk latency
-  // dominates.
+  // KB (hidden chunk per LDS tile) is 64 for the most blocked shapes (more
+  // FMAs per chunk) and 128 otherwise, so a chunk's FMAs cover the global
+  // load latency of the next one.
   static constexpr Cfg cfgs[] = {{8, 4, 16, 16}, {4, 4, 16, 16}, {2, 4, 32, 8},
                                  {2, 2, 16, 16}, {1, 2, 32, 8},  {1, 1, 16, 16}};
   int pick = 5;
@@ -232,22 +259,23 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
       break;
     }
   }
-  auto go = [&](auto kern, int TT, int TE) {
+  auto go = [&](auto kern, int TT, int TE, int KB) {
     dim3 grid((T + TT - 1) / TT, (E + TE - 1) / TE);
-    kern<<<grid, 256, 0, s>>>(x, gate_w, bias, logits, T, d, E);
+    const size_t lds = sizeof(float) * static_cast<size_t>(TT + TE) * (KB + kRoutePad);
+    kern<<<grid, 256, lds, s>>>(x, gate_w, bias, logits, T, d, E);
   };
 #define MOE_L(C, RT, RE, TYL, TXL, KB)                                                    \
   if (pick == C) {                                                                        \
     if (bf16)                                                                             \
-      go(logits_kernel<RT, RE, TYL, TXL, KB, true>, TYL * RT, TXL * RE);                  \
+      go(logits_kernel<RT, RE, TYL, TXL, KB, true>, TYL * RT, TXL * RE, KB);              \
     else                                                                                  \
-      go(logits_kernel<RT, RE, TYL, TXL, KB, false>, TYL * RT, TXL * RE);                 \
+      go(logits_kernel<RT, RE, TYL, TXL, KB, false>, TYL * RT, TXL * RE, KB);             \
     return;                                                                               \
   }
-  MOE_L(0, 8, 4, 16, 16, 32)
-  MOE_L(1, 4, 4, 16, 16, 32)
-  MOE_L(2, 2, 4, 32, 8, 32)
-  MOE_L(3, 2, 2, 16, 16, 32)
+  MOE_L(0, 8, 4, 16, 16, 64)
+  MOE_L(1, 4, 4, 16, 16, 64)
+  MOE_L(2, 2, 4, 32, 8, 128)
+  MOE_L(3, 2, 2, 16, 16, 128)
   MOE_L(4, 1, 2, 32, 8, 128)
   MOE_L(5, 1, 1, 16, 16, 128)
 #undef MOE_L
