@@ -25,11 +25,15 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# per-source additions: the GEMM's work-queue atomic is issued by one lane
+# and its result consumed a whole tile later, so the wave-aggregating atomic
+# rewrite (which waits for the result at once) is switched off there
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *COMMON]
+    cmd = ["hipcc", *COMMON, *EXTRA.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -56,7 +56,7 @@ struct ESize<kFP8> { static constexpr int v = 1; };
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 
 // Compile-time geometry of one kernel variant.
-template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_ = (DT == kF32 ? 64 : 128)>
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_>
 struct Geo {
   static constexpr int NW = WM * WN;
   static constexpr int kThreads = NW * 64;
@@ -73,40 +73,51 @@ struct Geo {
   static constexpr int STAGE = (BM + BN) * KRB + SCALE_BYTES;
   static constexpr int RED = (DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0;
   static constexpr int NS0 = (kLdsBytes - RED) / STAGE;
-  static constexpr int NS = NS0 > 4 ? 4 : NS0;
-  static constexpr int EPI =
+  static constexpr int NS = NS0 > 6 ? 6 : NS0;
+  static constexpr int EPI =  // output staging, one pass per wave row
       (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : 4);
   static constexpr int RING = NS * STAGE;
   static constexpr int LDS = (RING > EPI ? RING : EPI) + RED;
   static_assert(NS >= 2, "at least two LDS stages");
+  static_assert(LDS <= kLdsBytes, "LDS budget");
   static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMA == 0, "whole DMA blocks");
 };
 
 // LDS byte offset of 16-byte chunk c of row r in a tile of KRB-byte rows.
-// The XOR key makes the 16 rows read by one quarter-wave ds_read_b128 hit
-// 16 distinct 4-bank groups (64 banks of 4 bytes).
+// The chunk index is XORed with bits 1.. of the row, which (measured on
+// gfx950) keeps the ds_read_b128 fragment reads -- 16 consecutive rows, one
+// chunk -- free of LDS bank conflicts for both 64- and 128-byte rows; keying
+// on bits 0-1 or 2-3 instead halves the read rate for 64-byte rows.
+template <int KRB>
+__device__ __forceinline__ int swz_key(int r) {
+  return (r >> 1) & (KRB / 16 - 1);
+}
 template <int KRB>
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (KRB == 64)
-    return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
-  else
-    return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+  return r * KRB + ((c ^ swz_key<KRB>(r)) << 4);
 }
 
-// s_waitcnt vmcnt(n) that leaves expcnt and lgkmcnt alone (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+// s_waitcnt vmcnt(n) that leaves expcnt alone, and lgkmcnt too unless
+// LGKM0 (then it also waits for every LDS access of the wave).  gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <bool LGKM0 = false>
 __device__ __forceinline__ void wait_vmcnt(int n) {
-#define MOE_W(N)                                                                        \
-  case N:                                                                               \
-    __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)); \
+  constexpr int kL = LGKM0 ? 0 : (15 << 8);
+#define MOE_W(N)                                                                         \
+  case N:                                                                                \
+    __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | kL | (((N) >> 4) << 14));         \
     break;
   switch (n) {
     MOE_W(0) MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7)
     MOE_W(8) MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15)
     MOE_W(16) MOE_W(17) MOE_W(18) MOE_W(19) MOE_W(20) MOE_W(21) MOE_W(22) MOE_W(23)
     MOE_W(24) MOE_W(25) MOE_W(26) MOE_W(27) MOE_W(28) MOE_W(29) MOE_W(30) MOE_W(31)
+    MOE_W(32) MOE_W(33) MOE_W(34) MOE_W(35) MOE_W(36) MOE_W(37) MOE_W(38) MOE_W(39)
+    MOE_W(40) MOE_W(41) MOE_W(42) MOE_W(43) MOE_W(44) MOE_W(45) MOE_W(46) MOE_W(47)
+    MOE_W(48) MOE_W(49) MOE_W(50) MOE_W(51) MOE_W(52) MOE_W(53) MOE_W(54) MOE_W(55)
+    MOE_W(56) MOE_W(57) MOE_W(58) MOE_W(59) MOE_W(60) MOE_W(61) MOE_W(62)
     default:
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | kL);
       break;
   }
 #undef MOE_W
@@ -120,7 +131,11 @@ __device__ __forceinline__ void dma4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+// SiLU with the hardware exponential and reciprocal (about 2 ulp in fp32;
+// h is rounded to the activation format right after).
+__device__ __forceinline__ float silu(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 // Workgroup barrier for the DMA ring.  __syncthreads() also emits a release
 // fence whose s_waitcnt vmcnt(0) would drain every stage in flight; LDS needs
@@ -134,9 +149,49 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int DT, int PHASE, int BM, int BN, int WM, int WN>
+constexpr int kXcd = 8;  // XCDs (L2 domains) of the chip
+
+// Per-XCD task queues of one grouped GEMM (see the kernel).  Task ids are
+// m-tile * NT + n-tile; queue y hands out the tasks of chunks y, y+8, ...
+// (chunk = GM consecutive m-tiles), n-tile-major inside a chunk.
+struct TaskQueue {
+  int* counters;  // [kXcd] integer pull counters, zeroed by the scan kernel
+  int M, NT, GM, nchunks, xcd;
+
+  __device__ int limit(int y) const {
+    const int owned = nchunks > y ? (nchunks - y + kXcd - 1) / kXcd : 0;
+    return owned * GM * NT;
+  }
+  // task of pull number v of queue y, or -1 (the last chunk may hold fewer
+  // than GM m-tiles)
+  __device__ int decode(int v, int y) const {
+    const int per_chunk = GM * NT;
+    const int p = v % per_chunk;
+    const int mt = (y + kXcd * (v / per_chunk)) * GM + p % GM;
+    return mt < M ? mt * NT + p / GM : -1;
+  }
+  // pull from the own queue (s0 = 0) or start with the next XCD's (s0 = 1),
+  // moving on while queues are drained; -1 once every queue is.
+  __device__ int pull(int s0) const {
+    for (int s = s0; s < kXcd; ++s) {
+      const int y = (xcd + s) % kXcd;
+      const int lim = limit(y);
+      for (;;) {
+        if (__hip_atomic_load(&counters[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= lim)
+          break;
+        const int v = atomicAdd(&counters[y], 1);
+        if (v >= lim) break;
+        const int t = decode(v, y);
+        if (t >= 0) return t;
+      }
+    }
+    return -1;
+  }
+};
+
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
-  using G = Geo<DT, PHASE, BM, BN, WM, WN>;
+  using G = Geo<DT, PHASE, BM, BN, WM, WN, KRB_>;
   constexpr int kThreads = G::kThreads, ES = G::ES, KRB = G::KRB, NS = G::NS;
   constexpr int NW = G::NW, RPD = G::ROWS_PER_DMA;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -149,7 +204,10 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
   // the epilogue staging; then (FP8 phase 1) the per-wave row maxima.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds + (G::RING > G::EPI ? G::RING : G::EPI));
-  __shared__ int s_task;
+  // the task hand-over slot lives in the last bytes of the ring: it is
+  // written after every wave is done with the ring and read before the
+  // first DMA of the task can reach that stage slot
+  int& s_task = *reinterpret_cast<int*>(lds + G::RING - 16);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,47 +220,34 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 
   // XCD-aware work queue.  Each workgroup reads the XCD it runs on from the
   // XCC_ID hardware register and shares that XCD's L2 with the workgroups
-  // there.  The m-tiles are cut into chunks of kGM consecutive m-tiles (kGM
-  // from the host: about the m-tiles of one expert, at most 8); chunk c
+  // there.  The m-tiles are cut into chunks of group_m consecutive m-tiles
+  // (from the host: about the m-tiles of one expert, at most 8); chunk c
   // belongs to XCD c % 8, whose workgroups take its tasks n-tile by n-tile,
-  // so the weight rows of an n-tile are shared by kGM concurrent m-tiles and
-  // the activation rows of an m-tile by the n-tiles in flight -- in one L2.
-  // A drained XCD queue makes its workgroups steal from the others, so the
-  // queue stays work-conserving under routing skew.
-  constexpr int kXcd = 8;
-  const int kGM = g.group_m;
-  const int M = *g.tm.n_mtiles, NT = g.n_tiles_n;
-  const int nchunks = (M + kGM - 1) / kGM;
-  const int chunk_tasks = kGM * NT;
-  // s_getreg_b32 hwreg(HW_REG_XCC_ID, 0, 4): id of this XCD
-  const int xcd = __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kXcd - 1);
-  int* queue = g.tm.queue + kXcd * g.queue_idx;
+  // so the weight rows of an n-tile are shared by the concurrent m-tiles of
+  // the chunk and the activation rows of an m-tile by the n-tiles in flight
+  // -- in one L2.  A drained XCD queue makes its workgroups steal from the
+  // others, so the queue stays work-conserving under routing skew.
+  const TaskQueue q{g.tm.queue + kXcd * g.queue_idx, *g.tm.n_mtiles, g.n_tiles_n, g.group_m,
+                    (*g.tm.n_mtiles + g.group_m - 1) / g.group_m,
+                    // s_getreg_b32 hwreg(HW_REG_XCC_ID, 0, 4): id of this XCD
+                    static_cast<int>(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) &
+                                     (kXcd - 1))};
+  const int NT = q.NT;
+  const int own_limit = q.limit(q.xcd);
+  bool own_open = true;  // (thread 0) the own XCD queue may still hold tasks
 
+  if (tid == 0) s_task = q.pull(0);
+  __syncthreads();
   for (;;) {
-    if (tid == 0) {
-      int task = -1;
-      for (int s = 0; s < kXcd && task < 0; ++s) {
-        const int y = (xcd + s) % kXcd;
-        const int owned = nchunks > y ? (nchunks - y + kXcd - 1) / kXcd : 0;
-        const int limit = owned * chunk_tasks;
-        for (;;) {
-          if (__hip_atomic_load(&queue[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= limit)
-            break;
-          const int v = atomicAdd(&queue[y], 1);
-          if (v >= limit) break;
-          const int p = v % chunk_tasks;
-          const int mt = (y + kXcd * (v / chunk_tasks)) * kGM + p % kGM;
-          if (mt < M) {  // the last chunk may hold fewer than kGM m-tiles
-            task = mt * NT + p / kGM;
-            break;
-          }
-        }
-      }
-      s_task = task;
-    }
-    __syncthreads();
     const int task = __builtin_amdgcn_readfirstlane(s_task);
     if (task < 0) break;
+    // The next task is requested from the own XCD queue while this one runs:
+    // one atomic issued a few k-steps before the end, its result used after
+    // the epilogue.  That hides the queue round trip behind the tile's last
+    // k-steps while keeping the reservation short, so that the tail of the
+    // queue still spreads over all workgroups.
+    int next_v = -1;
+    const int k_pull = max(0, ksteps - 4);
     const int mt = task / NT;
     const int nt = task - mt * NT;
     const int e = __builtin_amdgcn_readfirstlane(g.tm.e[mt]);
@@ -227,7 +272,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     for (int j = 0; j < G::AW; ++j) {
       const int q = wave + NW * j;
       const int r = q * RPD + lrow;
-      const int logical = lphys ^ ((KRB == 64) ? ((r >> 2) & 3) : ((r >> 1) & 7));
+      const int logical = lphys ^ swz_key<KRB>(r);
       const int rr = min(r, rows - 1);  // padding rows re-read a valid row
       const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
       oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + logical * 16);
@@ -237,12 +282,15 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     for (int j = 0; j < G::BW; ++j) {
       const int q = wave + NW * j;
       const int r = q * RPD + lrow;
-      const int logical = lphys ^ ((KRB == 64) ? ((r >> 2) & 3) : ((r >> 1) & 7));
+      const int logical = lphys ^ swz_key<KRB>(r);
       const int64_t n = n0 + r;
       int64_t col;
       if (PHASE == 1) {  // combined rows: 16 gate rows, then 16 up rows, per f block
+        // the RPD rows of one DMA lie in one 16-row block (RPD divides 16 and
+        // n0 is a multiple of 32), so the gate/up choice is wave-uniform
+        static_assert(16 % RPD == 0, "DMA rows inside one gate/up block");
         col = (n >> 5) * 16 + (n & 15);
-        if (n & 16) up_mask |= 1u << j;
+        if ((q * RPD) & 16) up_mask |= 1u << j;
       } else {
         col = n;
       }
@@ -264,11 +312,11 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     const uint32_t ko_ = static_cast<uint32_t>(KS) * KRB;                                \
     _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                  \
       const int q = wave + NW * j;                                                       \
-      if (q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024);                       \
+      if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024);  \
     }                                                                                    \
     _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                  \
       const int q = wave + NW * j;                                                       \
-      if (q < G::BBLK)                                                                   \
+      if (G::BBLK % NW == 0 || q < G::BBLK)                                              \
         dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + ko_), st_ + BM * KRB + q * 1024); \
     }                                                                                    \
     if (DT == kFP8 && wave < G::SA_DMA)                                                  \
@@ -285,217 +333,291 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     for (int p = 0; p < NS - 1; ++p)
       if (p < ksteps) MOE_ISSUE(p);
 
-    for (int ks = 0; ks < ksteps; ++ks) {
-      // my loads of stage ks have landed once at most `ahead` later stages
-      // are still in flight; the barrier then publishes everyone's loads and
-      // guarantees every wave is done with the slot reloaded below
-      const int ahead = min(NS - 2, ksteps - 1 - ks);
-      wait_vmcnt(ahead * my_loads);
+    // bf16 with two MFMA k-steps per stage and one wave per SIMD: the
+    // fragment reads run one k-step ahead of the MFMAs, and the stage barrier
+    // sits between the two k-steps of a stage, so the MFMAs of the second
+    // k-step cover the LDS latency of the next stage's first reads.
+    constexpr bool kPipe = (DT == kBF16) && (KRB == 128) && (NW == 4);
+    if constexpr (kPipe) {
+      // (waves of padding rows compute too; their rows are never stored)
+      bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+#define MOE_RD(FA, FB, BASE, KK)                                                           \
+  do {                                                                                     \
+    const uint8_t* a_ = (BASE);                                                            \
+    const uint8_t* b_ = a_ + BM * KRB;                                                     \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) FB[j] = *reinterpret_cast<const bf16x8*>( \
+        b_ + swz<KRB>(wn * WTN + 16 * j + l16, (KK) * 4 + lg));                            \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) FA[i] = *reinterpret_cast<const bf16x8*>( \
+        a_ + swz<KRB>(wm * WTM + 16 * i + l16, (KK) * 4 + lg));                            \
+  } while (0)
+#define MOE_MM(FA, FB)                                                                     \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                         \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] =                             \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(FB[j], FA[i], acc[i][j], 0, 0, 0);         \
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                               \
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);                               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+  } while (0)
+      wait_vmcnt(min(NS - 2, ksteps - 1) * my_loads);  // stage 0 has landed
       ring_barrier();
-      if (ks + NS - 1 < ksteps) MOE_ISSUE(ks + NS - 1);
-      const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
-      const uint8_t* Bb = Ab + BM * KRB;
-      // A wave whose rows are all padding skips the step; a partly valid
-      // wave computes its padding rows too (their results are never stored),
-      // which keeps the fragment loop free of branches.
-      if (wm * WTM >= rows) continue;
-      if constexpr (DT == kBF16) {
-#pragma unroll
-        for (int kk = 0; kk < KRB / 64; ++kk) {
-          bf16x8 wf[TN];
-#pragma unroll
+      if (k_pull == 0 && tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
+      if (NS - 1 < ksteps) MOE_ISSUE(NS - 1);
+      MOE_RD(fa0, fb0, lds, 0);
+      for (int ks = 0; ks + 1 < ksteps; ++ks) {
+        MOE_RD(fa1, fb1, lds + (ks % NS) * G::STAGE, 1);
+        MOE_MM(fa0, fb0);
+        // my loads of stage ks+1 have landed and my reads of stage ks are
+        // done; after the barrier the slot of stage ks takes stage ks+NS
+        wait_vmcnt<true>(min(NS - 2, ksteps - 2 - ks) * my_loads);
+        ring_barrier();
+        if (ks + 1 == k_pull && tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
+        if (ks + NS < ksteps) MOE_ISSUE(ks + NS);
+        MOE_RD(fa0, fb0, lds + ((ks + 1) % NS) * G::STAGE, 0);
+        MOE_MM(fa1, fb1);
+      }
+      MOE_RD(fa1, fb1, lds + ((ksteps - 1) % NS) * G::STAGE, 1);
+      MOE_MM(fa0, fb0);
+      MOE_MM(fa1, fb1);
+#undef MOE_RD
+#undef MOE_MM
+    } else {
+      for (int ks = 0; ks < ksteps; ++ks) {
+        // my loads of stage ks have landed once at most `ahead` later stages
+        // are still in flight; the barrier then publishes everyone's loads and
+        // guarantees every wave is done with the slot reloaded below
+        const int ahead = min(NS - 2, ksteps - 1 - ks);
+        wait_vmcnt(ahead * my_loads);
+        ring_barrier();
+        if (ks == k_pull && tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
+        if (ks + NS - 1 < ksteps) MOE_ISSUE(ks + NS - 1);
+        const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
+        const uint8_t* Bb = Ab + BM * KRB;
+        // A wave whose rows are all padding skips the step; a partly valid
+        // wave computes its padding rows too (their results are never stored),
+        // which keeps the fragment loop free of branches.
+        if (wm * WTM >= rows) continue;
+        if constexpr (DT == kBF16) {
+  #pragma unroll
+          for (int kk = 0; kk < KRB / 64; ++kk) {
+            bf16x8 wf[TN];
+  #pragma unroll
+            for (int j = 0; j < TN; ++j)
+              wf[j] = *reinterpret_cast<const bf16x8*>(
+                  Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
+  #define MOE_BF16_ROWS(SKIP)                                                               \
+    bf16x8 xf[TM];                                                                          \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>( \
+        Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));                               \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+      if (SKIP) break;                                                                      \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0); \
+    }                                                                                       \
+    /* issue every fragment read of the step before the MFMAs (LDS latency  */              \
+    /* then overlaps the MFMAs instead of stalling each pair of fragments)  */              \
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                                \
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+            MOE_BF16_ROWS(false)
+  #undef MOE_BF16_ROWS
+          }
+        } else if constexpr (DT == kF32) {
+          f32x4 wf[TN];
+  #pragma unroll
           for (int j = 0; j < TN; ++j)
-            wf[j] = *reinterpret_cast<const bf16x8*>(
-                Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
-#define MOE_BF16_ROWS(SKIP)                                                               \
-  bf16x8 xf[TM];                                                                          \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>( \
-      Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));                               \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
-    if (SKIP) break;                                                                      \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0); \
-  }                                                                                       \
-  /* issue every fragment read of the step before the MFMAs (LDS latency  */              \
-  /* then overlaps the MFMAs instead of stalling each pair of fragments)  */              \
-  __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                                \
-  __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-          MOE_BF16_ROWS(false)
-#undef MOE_BF16_ROWS
+            wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz<KRB>(wn * WTN + 16 * j + l16, lg));
+  #define MOE_F32_ROWS(SKIP)                                                                \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+      if (SKIP) break;                                                                      \
+      const f32x4 xf =                                                                      \
+          *reinterpret_cast<const f32x4*>(Ab + swz<KRB>(wm * WTM + 16 * i + l16, lg));      \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u)                                         \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[u], acc[i][j], 0, 0, 0); \
+    }
+          MOE_F32_ROWS(false)
+  #undef MOE_F32_ROWS
+        } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
+          i32x8 wf[TN];
+  #pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int r = wn * WTN + 16 * j + l16;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
+            wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+          const float* sa_st = reinterpret_cast<const float*>(Bb + BN * KRB);
+          float s_b0, s_b1 = 0.f;
+          if (PHASE == 1) {
+            const int fb = static_cast<int>(n0 / 256);  // 128 f columns per workgroup tile
+            s_b0 = g.sb0[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + fb];
+            s_b1 = g.sb1[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + fb];
+          } else {
+            const int nb = static_cast<int>((n0 + wn * WTN) / 128);
+            s_b0 = g.sb0[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + nb];
+          }
+  #define MOE_FP8_ROWS(SKIP)                                                                \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+      if (SKIP) break;                                                                      \
+      const int r = wm * WTM + 16 * i + l16;                                                \
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));           \
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));       \
+      const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};       \
+      const float s_a = sa_st[r];                                                           \
+      const float sg = s_a * s_b0, su = s_a * s_b1;                                         \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                      \
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};                                               \
+        const f32x4 p =                                                                     \
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 127, 0, 127); \
+        const float sc = (PHASE == 1 && (j & 1)) ? su : sg;                                 \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) acc[i][j][q] =                        \
+            __builtin_fmaf(p[q], sc, acc[i][j][q]);                                         \
+      }                                                                                     \
+    }
+          MOE_FP8_ROWS(false)
+  #undef MOE_FP8_ROWS
         }
-      } else if constexpr (DT == kF32) {
-        f32x4 wf[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz<KRB>(wn * WTN + 16 * j + l16, lg));
-#define MOE_F32_ROWS(SKIP)                                                                \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
-    if (SKIP) break;                                                                      \
-    const f32x4 xf =                                                                      \
-        *reinterpret_cast<const f32x4*>(Ab + swz<KRB>(wm * WTM + 16 * i + l16, lg));      \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                         \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[u], acc[i][j], 0, 0, 0); \
-  }
-        MOE_F32_ROWS(false)
-#undef MOE_F32_ROWS
-      } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
-        i32x8 wf[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int r = wn * WTN + 16 * j + l16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
-          wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        const float* sa_st = reinterpret_cast<const float*>(Bb + BN * KRB);
-        float s_b0, s_b1 = 0.f;
-        if (PHASE == 1) {
-          const int fb = static_cast<int>(n0 / 256);  // 128 f columns per workgroup tile
-          s_b0 = g.sb0[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + fb];
-          s_b1 = g.sb1[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + fb];
-        } else {
-          const int nb = static_cast<int>((n0 + wn * WTN) / 128);
-          s_b0 = g.sb0[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + nb];
-        }
-#define MOE_FP8_ROWS(SKIP)                                                                \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
-    if (SKIP) break;                                                                      \
-    const int r = wm * WTM + 16 * i + l16;                                                \
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));           \
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));       \
-    const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};       \
-    const float s_a = sa_st[r];                                                           \
-    const float sg = s_a * s_b0, su = s_a * s_b1;                                         \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                      \
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};                                               \
-      const f32x4 p =                                                                     \
-          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 127, 0, 127); \
-      const float sc = (PHASE == 1 && (j & 1)) ? su : sg;                                 \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) acc[i][j][q] =                        \
-          __builtin_fmaf(p[q], sc, acc[i][j][q]);                                         \
-    }                                                                                     \
-  }
-        MOE_FP8_ROWS(false)
-#undef MOE_FP8_ROWS
       }
     }
 #undef MOE_ISSUE
-    __syncthreads();  // every wave is done with the ring before the epilogue reuses it
 
     // ---------------- epilogue ----------------
-    // Output values are staged in LDS (free after the main loop's last
+    // Output rows are staged in LDS (free after the main loop's last
     // barrier) so that every global store is a 16-byte piece of a contiguous
-    // row segment; one pass per wave row wm.  Staged rows are XOR-swizzled by
-    // 16-byte chunk to keep the fragment writes off a single bank group.
-    constexpr int OUT_COLS = (PHASE == 1) ? BN / 2 : BN;
-    constexpr int OUT_ES = (PHASE == 1) ? ES : 4;
-    constexpr int ROWB = OUT_COLS * OUT_ES;
-    constexpr int CPR = ROWB / 16;
-    constexpr int XM = (CPR >= 16 ? 16 : CPR) - 1;
-    uint8_t* stage = lds;
-    auto st_off = [&](int r, int cbyte) {
-      return r * ROWB + ((((cbyte >> 4) ^ (r & XM)) << 4) | (cbyte & 15));
-    };
-    const int64_t col0 = (PHASE == 1) ? n0 / 2 : n0;
+    // row segment: the whole tile in one pass when it fits in the ring, else
+    // one pass per wave row.  Staged rows are XOR-swizzled by 16-byte chunk to
+    // keep the fragment writes off a single bank group.
+    {
+      constexpr int OUT_COLS = (PHASE == 1) ? BN / 2 : BN;
+      constexpr int OUT_ES = (PHASE == 1) ? ES : 4;
+      constexpr int ROWB = OUT_COLS * OUT_ES;
+      constexpr int CPR = ROWB / 16;
+      constexpr int XM = (CPR >= 16 ? 16 : CPR) - 1;
+      constexpr int PASSES = (BM * ROWB <= G::RING - 16) ? 1 : WM;
+      constexpr int PROWS = BM / PASSES;  // rows per pass
+      static_assert(PROWS * ROWB <= (G::RING > G::EPI ? G::RING : G::EPI), "staging fits");
+      uint8_t* stage = lds;
+      auto st_off = [&](int r, int cbyte) {
+        return r * ROWB + ((((cbyte >> 4) ^ (r & XM)) << 4) | (cbyte & 15));
+      };
+      const int64_t col0 = (PHASE == 1) ? n0 / 2 : n0;
 
-    if constexpr (PHASE == 1 && DT == kFP8) {
-      // h = SiLU(gate) * up in fp32 (in place), then the row amax over the
-      // tile's 128 f columns: lanes, then the WN waves through LDS
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        float m = 0.f;
-#pragma unroll
-        for (int p = 0; p < TN / 2; ++p)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            acc[i][2 * p][r] = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
-            m = fmaxf(m, fabsf(acc[i][2 * p][r]));
-          }
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        if (lg == 0) red[wn * BM + wm * WTM + 16 * i + l16] = m;
-      }
-      __syncthreads();
-    }
-
-    for (int pass = 0; pass < WM; ++pass) {
-      if (wm == pass) {
+      if constexpr (PHASE == 1 && DT == kFP8) {
+        // h = SiLU(gate) * up in fp32 (in place), then the row amax over the
+        // tile's 128 f columns: lanes, then the WN waves through LDS
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const int r = 16 * i + l16;  // row within this pass
-          if constexpr (PHASE == 2) {
+          float m = 0.f;
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
-                  acc[i][j];
-          } else if constexpr (DT == kFP8) {
-            const int lr = pass * WTM + r;
-            float amax = 0.f;
+          for (int p = 0; p < TN / 2; ++p)
 #pragma unroll
-            for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + lr]);
-            const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
-#pragma unroll
-            for (int p = 0; p < TN / 2; ++p) {
-              uint32_t packed = 0;
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                packed |= f32_to_e4m3(__fdiv_rn(acc[i][2 * p][q], sc)) << (8 * q);
-              *reinterpret_cast<uint32_t*>(stage + st_off(r, wn * (WTN / 2) + 16 * p + 4 * lg)) =
-                  packed;
+            for (int r = 0; r < 4; ++r) {
+              acc[i][2 * p][r] = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
+              m = fmaxf(m, fabsf(acc[i][2 * p][r]));
             }
-            if (wn == 0 && lg == 0 && lr < rows)
-              g.sc[static_cast<int64_t>(row0 + lr) * (N / 128) + n0 / 256] = sc;
-          } else {
+          m = fmaxf(m, __shfl_xor(m, 16, 64));
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          if (lg == 0) red[wn * BM + wm * WTM + 16 * i + l16] = m;
+        }
+      }
+      __syncthreads();  // every wave is done with the ring (and the row maxima are in)
+
+      for (int pass = 0; pass < PASSES; ++pass) {
+        if ((wm * WTM) / PROWS == pass) {
 #pragma unroll
-            for (int p = 0; p < TN / 2; ++p) {
-              float h[4];
+          for (int i = 0; i < TM; ++i) {
+            const int lr = wm * WTM + 16 * i + l16;  // row within the tile
+            const int r = lr - pass * PROWS;          // row within this pass
+            if constexpr (PHASE == 2) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) h[q] = silu(acc[i][2 * p][q]) * acc[i][2 * p + 1][q];
-              const int cb = (wn * (WTN / 2) + 16 * p + 4 * lg) * ES;
-              if constexpr (DT == kBF16) {
-                u32x2 v;
-                v.x = f32_to_bf16_rne(h[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[1])) << 16);
-                v.y = f32_to_bf16_rne(h[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[3])) << 16);
-                *reinterpret_cast<u32x2*>(stage + st_off(r, cb)) = v;
-              } else {
-                *reinterpret_cast<f32x4*>(stage + st_off(r, cb)) = f32x4{h[0], h[1], h[2], h[3]};
+              for (int j = 0; j < TN; ++j)
+                *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
+                    acc[i][j];
+            } else if constexpr (DT == kFP8) {
+              float amax = 0.f;
+#pragma unroll
+              for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + lr]);
+              const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
+#pragma unroll
+              for (int p = 0; p < TN / 2; ++p) {
+                uint32_t packed = 0;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                  packed |= f32_to_e4m3(__fdiv_rn(acc[i][2 * p][q4], sc)) << (8 * q4);
+                *reinterpret_cast<uint32_t*>(stage + st_off(r, wn * (WTN / 2) + 16 * p + 4 * lg)) =
+                    packed;
+              }
+              if (wn == 0 && lg == 0 && lr < rows)
+                g.sc[static_cast<int64_t>(row0 + lr) * (N / 128) + n0 / 256] = sc;
+            } else {
+#pragma unroll
+              for (int p = 0; p < TN / 2; ++p) {
+                float h[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                  h[q4] = silu(acc[i][2 * p][q4]) * acc[i][2 * p + 1][q4];
+                const int cb = (wn * (WTN / 2) + 16 * p + 4 * lg) * ES;
+                if constexpr (DT == kBF16) {
+                  u32x2 v;
+                  v.x = f32_to_bf16_rne(h[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[1])) << 16);
+                  v.y = f32_to_bf16_rne(h[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[3])) << 16);
+                  *reinterpret_cast<u32x2*>(stage + st_off(r, cb)) = v;
+                } else {
+                  *reinterpret_cast<f32x4*>(stage + st_off(r, cb)) = f32x4{h[0], h[1], h[2], h[3]};
+                }
               }
             }
           }
         }
+        __syncthreads();
+        for (int idx = tid; idx < PROWS * CPR; idx += kThreads) {
+          const int r = idx / CPR, c = idx - r * CPR;
+          const int lr = pass * PROWS + r;
+          const int64_t col = col0 + c * (16 / OUT_ES);
+          if (lr < rows && col < N)
+            *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(row0 + lr) * N + col) * OUT_ES) =
+                *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
+        }
+        if (pass + 1 < PASSES) __syncthreads();
       }
-      __syncthreads();
-      for (int idx = tid; idx < WTM * CPR; idx += kThreads) {
-        const int r = idx / CPR, c = idx - r * CPR;
-        const int lr = pass * WTM + r;
-        const int64_t col = col0 + c * (16 / OUT_ES);
-        if (lr < rows && col < N)
-          *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(row0 + lr) * N + col) * OUT_ES) =
-              *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
-      }
-      __syncthreads();
     }
+
+    // hand over the next task; the barriers also separate this task's last
+    // LDS reads from the hand-over slot write and from the next task's
+    // first DMA writes
+    __syncthreads();
+    if (tid == 0) {
+      int t = -1;
+      if (next_v >= 0) {
+        if (next_v < own_limit) t = q.decode(next_v, q.xcd);
+        else own_open = false;
+      }
+      if (t < 0) t = q.pull(own_open ? 0 : 1);
+      s_task = t;
+    }
+    __syncthreads();
   }
 }
 
-template <int DT, int PHASE, int BM, int BN, int WM, int WN>
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB = (DT == kF32 ? 64 : 128)>
 struct Variant {
   static constexpr int kThreads = WM * WN * 64;
-  static constexpr int lds_bytes() { return Geo<DT, PHASE, BM, BN, WM, WN>::LDS; }
+  static constexpr int lds_bytes() { return Geo<DT, PHASE, BM, BN, WM, WN, KRB>::LDS; }
   static int launch(const GemmArgs& a, hipStream_t s) {
-    auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN>;
+    auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN, KRB>;
     static int grid = 0;
+    static hipError_t attr_err = hipSuccess;
     static std::once_flag once;
     std::call_once(once, [&] {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes());
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes());
       int dev = 0, cus = 0, per_cu = 0;
       (void)hipGetDevice(&dev);
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds_bytes());
       grid = max(1, cus) * max(1, per_cu);
     });
+    if (attr_err != hipSuccess) return static_cast<int>(attr_err);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes(), s, a);
     return static_cast<int>(hipGetLastError());
   }
@@ -515,13 +637,15 @@ int variant_choice() {
 // Kernel variant per (dtype, phase, tile height, tuning variant).
 template <typename F>
 int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
-#define MOE_V(DT, P, BM_, VAR, BN_, WM_, WN_)                     \
+#define MOE_V(DT, P, BM_, VAR, BN_, WM_, WN_, ...)                \
   if (dtype == DT && phase == P && bm == BM_ && var == VAR)        \
-    return f(Variant<DT, P, BM_, BN_, WM_, WN_>{});
+    return f(Variant<DT, P, BM_, BN_, WM_, WN_ __VA_OPT__(, ) __VA_ARGS__>{});
   MOE_V(kBF16, 1, 256, 0, 256, 2, 4)
   MOE_V(kBF16, 2, 256, 0, 256, 2, 4)
   MOE_V(kBF16, 1, 256, 1, 256, 2, 2)
   MOE_V(kBF16, 2, 256, 1, 256, 2, 2)
+  MOE_V(kBF16, 1, 256, 3, 256, 2, 4, 64)
+  MOE_V(kBF16, 2, 256, 3, 256, 2, 4, 64)
   MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 2, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 1, 128, 1, 256, 1, 4)
