@@ -323,6 +323,24 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       dma4(sa_src + (KS), st_ + (BM + BN) * KRB + wave * 256);                           \
   } while (0)
 
+    // FP8: the weight block scales of this tile are wave-uniform and
+    // read-only; they are loaded through the scalar cache (constant address
+    // space) one k-step ahead, off the vector-memory counter that orders the
+    // DMA ring.
+    typedef __attribute__((address_space(4))) const float cfloat;
+    const cfloat* sbp0 = nullptr;
+    const cfloat* sbp1 = nullptr;
+    float sb_cur0 = 0.f, sb_cur1 = 0.f, sb_nxt0 = 0.f, sb_nxt1 = 0.f;
+    if constexpr (DT == kFP8) {
+      const int nb = (PHASE == 1) ? static_cast<int>(n0 / 256)  // 128 f columns per tile
+                                  : static_cast<int>((n0 + wn * WTN) / 128);
+      const int64_t base = static_cast<int64_t>(e) * kblocks * nblocks + nb;
+      sbp0 = (const cfloat*)(g.sb0) + base;
+      sbp1 = (PHASE == 1) ? (const cfloat*)(g.sb1) + base : sbp0;
+      sb_nxt0 = sbp0[0];
+      sb_nxt1 = (PHASE == 1) ? sbp1[0] : 0.f;
+    }
+
     f32x4 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -391,6 +409,14 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
         ring_barrier();
         if (ks == k_pull && tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
         if (ks + NS - 1 < ksteps) MOE_ISSUE(ks + NS - 1);
+        if constexpr (DT == kFP8) {
+          sb_cur0 = sb_nxt0;
+          sb_cur1 = sb_nxt1;
+          if (ks + 1 < ksteps) {
+            sb_nxt0 = sbp0[static_cast<int64_t>(ks + 1) * nblocks];
+            if (PHASE == 1) sb_nxt1 = sbp1[static_cast<int64_t>(ks + 1) * nblocks];
+          }
+        }
         const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
         const uint8_t* Bb = Ab + BM * KRB;
         // A wave whose rows are all padding skips the step; a partly valid
@@ -439,7 +465,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
   #undef MOE_F32_ROWS
         } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
           i32x8 wf[TN];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < TN; ++j) {
             const int r = wn * WTN + 16 * j + l16;
             const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
@@ -447,35 +473,67 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
             wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
           const float* sa_st = reinterpret_cast<const float*>(Bb + BN * KRB);
-          float s_b0, s_b1 = 0.f;
-          if (PHASE == 1) {
-            const int fb = static_cast<int>(n0 / 256);  // 128 f columns per workgroup tile
-            s_b0 = g.sb0[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + fb];
-            s_b1 = g.sb1[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + fb];
-          } else {
-            const int nb = static_cast<int>((n0 + wn * WTN) / 128);
-            s_b0 = g.sb0[(static_cast<int64_t>(e) * kblocks + ks) * nblocks + nb];
+          const float s_b0 = sb_cur0, s_b1 = sb_cur1;
+          if constexpr (PHASE == 1) {
+            // Row by row: the TN block products of row i are issued before the
+            // scaled accumulation of row i-1, so the fp32 fmas overlap MFMAs.
+            f32x4 pp[TN];
+            float spg = 0.f, spu = 0.f;
+  #pragma unroll
+            for (int i = 0; i <= TM; ++i) {
+              f32x4 pc[TN];
+              float scg = 0.f, scu = 0.f;
+              if (i < TM) {
+                const int r = wm * WTM + 16 * i + l16;
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
+                const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const float s_a = sa_st[r];
+                scg = s_a * s_b0;
+                scu = s_a * s_b1;
+  #pragma unroll
+                for (int j = 0; j < TN; ++j)
+                  pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                      wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+              }
+              if (i > 0) {
+  #pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                  const float sc = (PHASE == 1 && (j & 1)) ? spu : spg;
+  #pragma unroll
+                  for (int q = 0; q < 4; ++q)
+                    acc[i - 1][j][q] = __builtin_fmaf(pp[j][q], sc, acc[i - 1][j][q]);
+                }
+              }
+  #pragma unroll
+              for (int j = 0; j < TN; ++j) pp[j] = pc[j];
+              spg = scg;
+              spu = scu;
+            }
+          } else {  // (measured: the lagged form loses here, to register pressure)
+            // per row of fragments: the TN block products first (independent
+            // MFMAs in flight), then their scaled accumulation
+  #pragma unroll
+            for (int i = 0; i < TM; ++i) {
+              const int r = wm * WTM + 16 * i + l16;
+              const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
+              const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
+              const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              const float s_a = sa_st[r];
+              const float sg = s_a * s_b0, su = s_a * s_b1;
+              f32x4 p[TN];
+  #pragma unroll
+              for (int j = 0; j < TN; ++j)
+                p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+  #pragma unroll
+              for (int j = 0; j < TN; ++j) {
+                const float sc = (PHASE == 1 && (j & 1)) ? su : sg;
+  #pragma unroll
+                for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(p[j][q], sc, acc[i][j][q]);
+              }
+            }
           }
-  #define MOE_FP8_ROWS(SKIP)                                                                \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
-      if (SKIP) break;                                                                      \
-      const int r = wm * WTM + 16 * i + l16;                                                \
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));           \
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));       \
-      const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};       \
-      const float s_a = sa_st[r];                                                           \
-      const float sg = s_a * s_b0, su = s_a * s_b1;                                         \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                      \
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};                                               \
-        const f32x4 p =                                                                     \
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 127, 0, 127); \
-        const float sc = (PHASE == 1 && (j & 1)) ? su : sg;                                 \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) acc[i][j][q] =                        \
-            __builtin_fmaf(p[q], sc, acc[i][j][q]);                                         \
-      }                                                                                     \
-    }
-          MOE_FP8_ROWS(false)
-  #undef MOE_FP8_ROWS
         }
       }
     }
