@@ -39,6 +39,65 @@ def _hip():
     return lib
 
 
+def _device_info():
+    """CU count and maximum shader clock as rocminfo reports them for the GPU
+    agent, and the dense peaks they imply (per CU and clock: 4096 bf16, 8192
+    fp8 and 256 fp32 MFMA FLOP)."""
+    import subprocess
+    cus = mhz = None
+    name = None
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        agent = {}
+        for line in txt.splitlines() + ["Agent end"]:
+            line = line.strip()
+            if line.startswith("Agent ") or line.startswith("*******"):
+                if agent.get("Device Type") == "GPU" and cus is None:
+                    name = agent.get("Name")
+                    cus = int(agent["Compute Unit"]) if "Compute Unit" in agent else None
+                    mhz = (int(agent["Max Clock Freq. (MHz)"])
+                           if "Max Clock Freq. (MHz)" in agent else None)
+                agent = {}
+            elif ":" in line:
+                k, v = line.split(":", 1)
+                agent.setdefault(k.strip(), v.strip())
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    info = {"agent": name, "cus": cus, "max_clock_mhz": mhz}
+    if cus and mhz:
+        f = cus * mhz * 1e6
+        info["derived_peak_tflops"] = {"bf16": f * 4096 / 1e12, "fp8": f * 8192 / 1e12,
+                                       "fp32_mfma": f * 256 / 1e12}
+    return info
+
+
+def _copy_gbps(torch):
+    """Device-to-device copy of 1 GiB (read + write bytes per second)."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(3):
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2.0 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, b
+    return best
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _events(hip, n):
     evs = []
     for _ in range(n):
@@ -146,7 +205,8 @@ def _cpu_baseline(cfg, inp, out_gpu, target_s):
         half_ulp = 0.5 * np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
         err["max_excess_over_half_bf16_ulp_over_rms"] = float(np.maximum(diff - half_ulp, 0).max()) / rms
     cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
-    return {"value": n / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": n / secs, "unit": "tokens/s", "cores": cores, "cpu": _cpu_model(),
+            "kind": "oracle",
             "sample": f"{n} of {cfg.T} tokens (seeded random rows), full layer forward per "
                       f"token, {secs:.1f} s", "seconds": secs}, err
 
@@ -197,8 +257,9 @@ def main():
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
+    clock = torch.zeros(4, dtype=torch.int64, device="cuda")
     for i in range(args.steps):
-        step({"stage_events": evs[i]})
+        step({"stage_events": evs[i], "gemm_clock": clock})
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -207,6 +268,12 @@ def main():
     for s, name in enumerate(STAGES, start=1):
         stage_ms[name] = float(np.mean([_elapsed(hip, e[s - 1], e[s]) for e in evs]))
     gpu_ms = _elapsed(hip, evs[0][0], evs[-1][-1]) / args.steps
+    per_step = np.array([_elapsed(hip, e[0], e[-1]) for e in evs])
+    step_stats = {"median": float(np.median(per_step)), "min": float(per_step.min()),
+                  "p90": float(np.percentile(per_step, 90))}
+    ck = clock.cpu().numpy().astype(np.float64)
+    sustained = {name: (1e2 * ck[2 * i] / ck[2 * i + 1] if ck[2 * i + 1] > 0 else None)
+                 for i, name in enumerate(("gemm_w13_swiglu", "gemm_w2"))}
     for e in evs:
         for v in e:
             hip.hipEventDestroy(v)
@@ -217,10 +284,11 @@ def main():
     dom = max(("gemm_w13_swiglu", "gemm_w2"), key=lambda k: stage_ms[k])
     dom_s = stage_ms[dom] * 1e-3
     decode = cfg.T * cfg.k / cfg.E < 16
+    copy_gbps = _copy_gbps(torch)
     if decode:
         achieved = work[dom]["bytes"] / dom_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBPS}
+                "frac": achieved / PEAK_HBM_GBPS, "frac_of_measured_copy": achieved / copy_gbps}
     else:
         achieved = work[dom]["flops"] / dom_s / 1e12
         peak = PEAK_TFLOPS[cfg.w_dtype]
@@ -236,7 +304,11 @@ def main():
         / (ms_per_step * 1e-3) / 1e9,
         "hit_experts": work["hit_experts"],
         "gpu_event_ms_per_step": gpu_ms,
+        "gpu_event_ms_per_step_stats": step_stats,
     }
+    device = _device_info()
+    device["sustained_clock_mhz"] = sustained
+    device["measured_copy_GBps"] = copy_gbps
 
     cpu = None
     parity = None
@@ -263,6 +335,7 @@ def main():
         "cpu_baseline": cpu,
         "stages_ms": stage_ms,
         "layer": layer,
+        "device": device,
         "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)

@@ -81,8 +81,9 @@ typedef enum {
  *              expected tokens per expert T*top_k/E (the serving-regime choice
  *              of the MegaMoE-vs-MoE-systems page, section 2.5, re-tuned for
  *              MFMA tiles).  Otherwise one of 16, 32, 64, 128, 256.
- * bf16/FP8 layers need d % 64 == 0 and f % 64 == 0; fp32 layers need
- * d % 16 == 0 and f % 16 == 0. */
+ * d and f must be multiples of 32 (fp32 weights), 64 (bf16) or 128 (FP8), and
+ * x, h and one expert's weight matrix must each span less than 2^31 bytes
+ * (MOE_ERR_UNSUPPORTED otherwise). */
 typedef struct {
     int64_t T, d, f;
     int32_t E, top_k;
@@ -99,7 +100,12 @@ typedef struct {
  * the call's stream at stage boundary i: 0 start, 1 after the gate, 2 after
  * the FP8 quantisation of x, 3 after histogram/scan/scatter, 4 after the
  * W1/W3 GEMM, 5 after the W2 GEMM, 6 after the combine.  Used to time each
- * kernel inside the whole-layer call. */
+ * kernel inside the whole-layer call.
+ * gemm_clock: [2][2] uint64 device buffer, or NULL: for the W1/W3 (row 0) and
+ * W2 (row 1) GEMM launches, the shader-clock ticks (s_memtime) and the
+ * 100 MHz reference ticks (s_memrealtime) that the first workgroup spent from
+ * its start to its exit -- the clock the chip sustained under that load is
+ * 1e8 * ticks[0] / ticks[1] Hz. */
 #define MOE_NUM_STAGE_EVENTS 7
 typedef struct {
     int32_t *topk_ids;    /* [T*k]  */
@@ -110,6 +116,7 @@ typedef struct {
     int32_t *slot_k;      /* [T*k]  */
     int32_t *token_slot;  /* [T*k]  */
     hipEvent_t stage_events[MOE_NUM_STAGE_EVENTS];
+    uint64_t *gemm_clock; /* [2][2]: shader ticks, reference ticks per GEMM */
 } moe_debug;
 
 /* Human-readable name of a status code (static storage). */

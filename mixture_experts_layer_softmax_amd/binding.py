@@ -38,7 +38,8 @@ DEBUG_BUFFERS = ("topk_ids", "topk_w", "counts", "offsets", "slot_token", "slot_
 
 class MoEDebug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in DEBUG_BUFFERS] + [
-        ("stage_events", ctypes.c_void_p * NUM_STAGE_EVENTS)]
+        ("stage_events", ctypes.c_void_p * NUM_STAGE_EVENTS),
+        ("gemm_clock", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -164,6 +165,8 @@ def moe_forward(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, dbg=N
                            for n in DEBUG_BUFFERS])
         for i, ev in enumerate(dbg.get("stage_events") or []):
             dbg_s.stage_events[i] = ev
+        if dbg.get("gemm_clock") is not None:  # int64 tensor [2][2]
+            dbg_s.gemm_clock = dbg["gemm_clock"].data_ptr()
     rc = load().moe_forward(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(W1t), _p(W3t),
                             _p(W2t), _p(W1s), _p(W3s), _p(W2s), _p(out), _p(ws), ws.numel(),
                             None if dbg_s is None else ctypes.byref(dbg_s), _stream(stream))

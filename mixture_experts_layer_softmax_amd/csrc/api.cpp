@@ -309,6 +309,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   g1.n_tiles_n = static_cast<int>(ceil_div(2 * p->f, moe::gemm_tile_n(1, gdt, L.bm)));
   g1.queue_idx = 0;
   g1.group_m = group_m(*p, L.bm);
+  g1.clock = dbg ? dbg->gemm_clock : nullptr;
   st = from_code(moe::launch_gemm(1, gdt, L.bm, g1, stream));
   if (st != MOE_OK) return st;
   mark(4);
@@ -331,6 +332,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   g2.n_tiles_n = static_cast<int>(ceil_div(p->d, moe::gemm_tile_n(2, gdt, L.bm)));
   g2.queue_idx = 1;
   g2.group_m = g1.group_m;
+  g2.clock = (dbg && dbg->gemm_clock) ? dbg->gemm_clock + 2 : nullptr;
   st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));
   if (st != MOE_OK) return st;
   mark(5);

@@ -211,6 +211,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint64_t clk0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
   const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, lg = lane >> 4;
   const int64_t K = g.K, N = g.N;
@@ -654,6 +655,14 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       s_task = t;
     }
     __syncthreads();
+  }
+  // sustained-clock record of the first workgroup (it lives as long as the
+  // launch): shader-clock and 100 MHz reference ticks
+  if (g.clock && blockIdx.x == 0 && tid == 0) {
+    const uint64_t clk = __builtin_amdgcn_s_memtime() - clk0;
+    const uint64_t ref = __builtin_amdgcn_s_memrealtime() - ref0;
+    g.clock[0] = clk;
+    g.clock[1] = ref;
   }
 }
 

@@ -54,6 +54,7 @@ struct GemmArgs {
   int n_tiles_n;          // column tiles per m-tile
   int queue_idx;
   int group_m;            // m-tiles per XCD work chunk (1..8)
+  uint64_t* clock;        // [2] or null: ticks of workgroup 0 (shader, 100 MHz reference)
 };
 
 void launch_logits(const void* x, const void* gate_w, const float* bias, float* logits,

@@ -177,6 +177,26 @@ def test_forward_is_deterministic():
         assert torch.equal(o, outs[0])
 
 
+def test_gemm_clock_record():
+    """moe_debug.gemm_clock receives, per GEMM launch, the shader-clock and
+    100 MHz reference ticks of the first workgroup; the implied clock lies in
+    the chip's range, and recording it leaves the output unchanged."""
+    cfg = REDUCED["prefill_bf16_r"]
+    say("gemm clock")
+    inp = gpu_inputs(cfg)
+    packed = B.pack_weights(inp)
+    ref = B.forward(cfg, inp, packed, out_dtype=F32)
+    clock = torch.zeros(4, dtype=torch.int64, device="cuda")
+    got = B.forward(cfg, inp, packed, out_dtype=F32, dbg={"gemm_clock": clock})
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    c = clock.cpu().tolist()
+    for i in range(2):
+        assert c[2 * i] > 0 and c[2 * i + 1] > 0, c
+        mhz = 100.0 * c[2 * i] / c[2 * i + 1]
+        assert 200.0 < mhz < 3000.0, (i, mhz, c)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads in the launch configuration the benchmark times;
 # outputs compared on a sample of tokens the oracle computes one by one
