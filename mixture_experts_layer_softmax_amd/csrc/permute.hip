@@ -44,14 +44,24 @@ __global__ __launch_bounds__(64) void hist_kernel(const int32_t* __restrict__ id
 
 // One workgroup of 1024 threads.  table [nchunk x E] in, becomes the base slot
 // of each (chunk, expert).  Also writes counts/offsets, the m-tile map for
-// tile height bm and zeroes the GEMM work-queue counters.
+// tile height bm and zeroes the GEMM work-queue counters.  When the table
+// fits (LDS_TABLE), it is scanned in LDS: loaded and stored back coalesced by
+// all threads, each expert's column summed by one thread from LDS.
+template <bool LDS_TABLE>
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table, int nchunk,
                                                     int E, int bm, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
                                                     TileMap tm) {
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t s_tiles[1024];
+  extern __shared__ int32_t s_tab[];  // [nchunk][E] when LDS_TABLE
+  int32_t* tab = LDS_TABLE ? s_tab : table;
   const int tid = threadIdx.x;
+  const int cells = nchunk * E;
+  if (LDS_TABLE) {
+    for (int i = tid; i < cells; i += 1024) s_tab[i] = table[i];
+    __syncthreads();
+  }
   int total = 0;
   if (tid < E) {
     // running sum down this expert's column; loads go out 8 at a time
@@ -59,10 +69,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
       int32_t v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        v[u] = (c0 + u < nchunk) ? table[static_cast<size_t>(c0 + u) * E + tid] : 0;
+        v[u] = (c0 + u < nchunk) ? tab[static_cast<size_t>(c0 + u) * E + tid] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (c0 + u < nchunk) table[static_cast<size_t>(c0 + u) * E + tid] = total;
+        if (c0 + u < nchunk) tab[static_cast<size_t>(c0 + u) * E + tid] = total;
         total += v[u];
       }
     }
@@ -91,13 +101,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
     const int off = s_cnt[tid];
     counts[tid] = total;
     offsets[tid] = off;
-    for (int c = 0; c < nchunk; ++c) table[static_cast<size_t>(c) * E + tid] += off;
+    if (!LDS_TABLE)
+      for (int c = 0; c < nchunk; ++c) table[static_cast<size_t>(c) * E + tid] += off;
     const int t0 = s_tiles[tid];
     for (int m = 0; m < tiles; ++m) {
       tm.e[t0 + m] = tid;
       tm.row0[t0 + m] = off + m * bm;
       tm.rows[t0 + m] = min(bm, total - m * bm);
     }
+  }
+  if (LDS_TABLE) {
+    __syncthreads();  // column sums and s_cnt (expert offsets) are final
+    for (int i = tid; i < cells; i += 1024) table[i] = s_tab[i] + s_cnt[i % E];
   }
 }
 
@@ -146,7 +161,16 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int bm, int32_t* ta
   while ((1 << nbits) < E) ++nbits;
   const size_t lds = sizeof(int32_t) * static_cast<size_t>(E);
   if (nchunk > 0) hist_kernel<<<nchunk, 64, lds, s>>>(ids, n, E, chunk, table);
-  scan_kernel<<<1, 1024, 0, s>>>(table, nchunk, E, bm, counts, offsets, tm);
+  // the table in LDS when it fits next to the kernel's 8 KB of static LDS
+  constexpr size_t kMaxTab = 144 * 1024;
+  static const bool big_lds = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel<true>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  static_cast<int>(kMaxTab)) == hipSuccess;
+  const size_t tab_bytes = sizeof(int32_t) * static_cast<size_t>(nchunk) * E;
+  if (tab_bytes <= (big_lds ? kMaxTab : 64 * 1024))
+    scan_kernel<true><<<1, 1024, tab_bytes, s>>>(table, nchunk, E, bm, counts, offsets, tm);
+  else
+    scan_kernel<false><<<1, 1024, 0, s>>>(table, nchunk, E, bm, counts, offsets, tm);
   if (nchunk > 0)
     scatter_kernel<<<nchunk, 64, lds, s>>>(ids, n, k, E, nbits, chunk, table, slot_token,
                                            slot_k, token_slot);
