@@ -240,8 +240,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 void launch_logits(const void* x, const void* gate_w, const float* bias, float* logits,
                    int T, int d, int E, bool bf16, hipStream_t s) {
-  // Largest register blocking that still gives the chip >= 256 workgroups
-  // and does not leave most expert lanes idle.
+  // Largest register blocking that still gives the chip >= 1024 workgroups
+  // (four per CU: the chains are latency-bound, measured) and does not leave
+  // most expert lanes idle.
   struct Cfg {
     int rt, re, tyl, txl;
   };
@@ -254,7 +255,7 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
   for (int c = 0; c < 5; ++c) {
     const int TT = cfgs[c].tyl * cfgs[c].rt, TE = cfgs[c].txl * cfgs[c].re;
     const long long wgs = static_cast<long long>((T + TT - 1) / TT) * ((E + TE - 1) / TE);
-    if (TE <= E && wgs >= 512) {  // two or more workgroups per CU
+    if (TE <= E && wgs >= 1024) {  // four or more workgroups per CU
       pick = c;
       break;
     }
