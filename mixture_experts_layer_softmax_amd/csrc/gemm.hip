@@ -304,22 +304,29 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       if (wave < G::SA_DMA) ++my_loads;
     }
 
-#define MOE_ISSUE(KS)                                                                    \
+// DMA of stage KS: the activation rows (and FP8 row scales) when DO_A, the
+// weight rows when DO_B
+#define MOE_ISSUE_PART(KS, DO_A, DO_B)                                                   \
   do {                                                                                   \
     uint8_t* st_ = lds + ((KS) % NS) * G::STAGE;                                         \
     const uint32_t ko_ = static_cast<uint32_t>(KS) * KRB;                                \
-    _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                  \
-      const int q = wave + NW * j;                                                       \
-      if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024);  \
+    if (DO_A) {                                                                          \
+      _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                \
+        const int q = wave + NW * j;                                                     \
+        if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024); \
+      }                                                                                  \
+      if (DT == kFP8 && wave < G::SA_DMA)                                                \
+        dma4(sa_src + (KS), st_ + (BM + BN) * KRB + wave * 256);                         \
     }                                                                                    \
-    _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                  \
-      const int q = wave + NW * j;                                                       \
-      if (G::BBLK % NW == 0 || q < G::BBLK)                                              \
-        dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + ko_), st_ + BM * KRB + q * 1024); \
+    if (DO_B) {                                                                          \
+      _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                \
+        const int q = wave + NW * j;                                                     \
+        if (G::BBLK % NW == 0 || q < G::BBLK)                                            \
+          dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + ko_), st_ + BM * KRB + q * 1024); \
+      }                                                                                  \
     }                                                                                    \
-    if (DT == kFP8 && wave < G::SA_DMA)                                                  \
-      dma4(sa_src + (KS), st_ + (BM + BN) * KRB + wave * 256);                           \
   } while (0)
+#define MOE_ISSUE(KS) MOE_ISSUE_PART(KS, true, true)
 
     // FP8: the weight block scales of this tile are wave-uniform and
     // read-only; they are loaded through the scalar cache (constant address
@@ -357,7 +364,12 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       wait_vmcnt(ahead * my_loads);
       ring_barrier();
       if (ks == k_pull && tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
-      if (ks + NS - 1 < ksteps) MOE_ISSUE(ks + NS - 1);
+      // bf16 stages hold two MFMA k-steps: the weight rows of the next stage
+      // are requested after the first one, which spreads the DMA's LDS writes
+      // over the stage instead of piling them onto its first fragment reads
+      constexpr bool kSplitDma = (DT == kBF16) && (KRB / 64 == 2);
+      const bool refill = ks + NS - 1 < ksteps;
+      if (refill) MOE_ISSUE_PART(ks + NS - 1, true, !kSplitDma);
       if constexpr (DT == kFP8) {
         sb_cur0 = sb_nxt0;
         sb_cur1 = sb_nxt1;
@@ -371,10 +383,12 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       // A wave whose rows are all padding skips the step; a partly valid
       // wave computes its padding rows too (their results are never stored),
       // which keeps the fragment loop free of branches.
-      if (wm * WTM >= rows) continue;
+      const bool compute = wm * WTM < rows;
       if constexpr (DT == kBF16) {
 #pragma unroll
         for (int kk = 0; kk < KRB / 64; ++kk) {
+          if (kSplitDma && kk == 1 && refill) MOE_ISSUE_PART(ks + NS - 1, false, true);
+          if (!compute) continue;
           bf16x8 wf[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j)
@@ -397,6 +411,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 #undef MOE_BF16_ROWS
         }
       } else if constexpr (DT == kF32) {
+        if (!compute) continue;
         f32x4 wf[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -413,6 +428,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
         MOE_F32_ROWS(false)
 #undef MOE_F32_ROWS
       } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
+        if (!compute) continue;
         i32x8 wf[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -486,6 +502,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       }
     }
 #undef MOE_ISSUE
+#undef MOE_ISSUE_PART
 
     // ---------------- epilogue ----------------
     // Output rows are staged in LDS (free after the main loop's last
