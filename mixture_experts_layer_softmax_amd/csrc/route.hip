@@ -11,6 +11,8 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <cstdlib>
+
 namespace moe {
 
 namespace {
@@ -30,6 +32,9 @@ __global__ __launch_bounds__(256) void logits_kernel(
     const float* __restrict__ bias, float* __restrict__ logits, int T, int d,
     int E) {
   static_assert(TYL * TXL == 256, "256 threads");
+  // fma-step unroll of whole chunks for lanes with one chain (its LDS
+  // latency is otherwise exposed); blocked shapes keep the plain loop
+  constexpr int UNR = (RT * RE == 1) ? 8 : 1;
   constexpr int TT = TYL * RT, TE = TXL * RE;
   constexpr int LD = KB + kRoutePad;
   constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte global load
@@ -133,19 +138,28 @@ __global__ __launch_bounds__(256) void logits_kernel(
     __syncthreads();
     if (i0 + KB < d) MOE_RLOAD(i0 + KB);  // in flight during this chunk's FMAs
     const int iend = min(KB, d - i0);     // d % 8 == 0, so iend % 4 == 0
-    for (int il = 0; il < iend; il += 4) {
-      f32x4 xv4[RT], wv4[RE];
-#pragma unroll
-      for (int a = 0; a < RT; ++a) xv4[a] = *reinterpret_cast<const f32x4*>(&xs[ty * RT + a][il]);
-#pragma unroll
-      for (int b = 0; b < RE; ++b) wv4[b] = *reinterpret_cast<const f32x4*>(&ws[tx * RE + b][il]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int a = 0; a < RT; ++a)
-#pragma unroll
-          for (int b = 0; b < RE; ++b) acc[a][b] = __builtin_fmaf(xv4[a][u], wv4[b][u], acc[a][b]);
+#define MOE_GATE_STEP(IL)                                                                 \
+  do {                                                                                    \
+    f32x4 xv4[RT], wv4[RE];                                                               \
+    _Pragma("unroll") for (int a = 0; a < RT; ++a) xv4[a] =                               \
+        *reinterpret_cast<const f32x4*>(&xs[ty * RT + a][(IL)]);                          \
+    _Pragma("unroll") for (int b = 0; b < RE; ++b) wv4[b] =                               \
+        *reinterpret_cast<const f32x4*>(&ws[tx * RE + b][(IL)]);                          \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                         \
+    _Pragma("unroll") for (int a = 0; a < RT; ++a)                                        \
+    _Pragma("unroll") for (int b = 0; b < RE; ++b) acc[a][b] =                            \
+        __builtin_fmaf(xv4[a][u], wv4[b][u], acc[a][b]);                                  \
+  } while (0)
+    if (UNR > 1 && iend == KB) {
+      // whole chunk: a compile-time trip count, unrolled so that the LDS
+      // reads of the next steps are issued ahead of this step's fma chain
+      // (the fma order of every chain stays i ascending)
+#pragma unroll UNR
+      for (int il = 0; il < KB; il += 4) MOE_GATE_STEP(il);
+    } else {
+      for (int il = 0; il < iend; il += 4) MOE_GATE_STEP(il);
     }
+#undef MOE_GATE_STEP
     __syncthreads();
   }
 #undef MOE_RLOAD
@@ -260,9 +274,19 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
       break;
     }
   }
+  {
+    static const int forced = [] {
+      const char* v = getenv("MOE_GATE_CFG");
+      return v ? atoi(v) : -1;
+    }();
+    if (forced >= 0) pick = forced;
+  }
   auto go = [&](auto kern, int TT, int TE, int KB) {
     dim3 grid((T + TT - 1) / TT, (E + TE - 1) / TE);
     const size_t lds = sizeof(float) * static_cast<size_t>(TT + TE) * (KB + kRoutePad);
+    if (lds > 64 * 1024)
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     kern<<<grid, 256, lds, s>>>(x, gate_w, bias, logits, T, d, E);
   };
 #define MOE_L(C, RT, RE, TYL, TXL, KB)                                                    \
@@ -279,6 +303,8 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
   MOE_L(3, 2, 2, 16, 16, 128)
   MOE_L(4, 1, 2, 32, 8, 128)
   MOE_L(5, 1, 1, 16, 16, 128)
+  MOE_L(6, 1, 1, 16, 16, 256)
+  MOE_L(7, 1, 1, 16, 16, 512)
 #undef MOE_L
 }
 
