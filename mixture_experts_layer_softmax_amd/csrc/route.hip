@@ -11,8 +11,6 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
-#include <cstdlib>
-
 namespace moe {
 
 namespace {
@@ -274,19 +272,9 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
       break;
     }
   }
-  {
-    static const int forced = [] {
-      const char* v = getenv("MOE_GATE_CFG");
-      return v ? atoi(v) : -1;
-    }();
-    if (forced >= 0) pick = forced;
-  }
   auto go = [&](auto kern, int TT, int TE, int KB) {
     dim3 grid((T + TT - 1) / TT, (E + TE - 1) / TE);
     const size_t lds = sizeof(float) * static_cast<size_t>(TT + TE) * (KB + kRoutePad);
-    if (lds > 64 * 1024)
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     kern<<<grid, 256, lds, s>>>(x, gate_w, bias, logits, T, d, E);
   };
 #define MOE_L(C, RT, RE, TYL, TXL, KB)                                                    \
@@ -303,8 +291,6 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
   MOE_L(3, 2, 2, 16, 16, 128)
   MOE_L(4, 1, 2, 32, 8, 128)
   MOE_L(5, 1, 1, 16, 16, 128)
-  MOE_L(6, 1, 1, 16, 16, 256)
-  MOE_L(7, 1, 1, 16, 16, 512)
 #undef MOE_L
 }
 
