@@ -42,6 +42,11 @@
  *     0) and the code is e4m3(v / s) with an fp32 quotient.
  *   - All sums of products are exact-order fp64 loops with the contraction
  *     index ascending.
+ *   - Shared experts (MegaMoE-vs-MoE-systems page, section 2.7: shared-expert
+ *     GEMMs are phases of the same task queue as the routed ones) see every
+ *     token and are added with weight 1 after the gate-weighted routed sum:
+ *     out = sum_j w_j y_j (j ascending) + sum_s ys_s (s ascending).  Their
+ *     weights follow the E routed experts' in the weight lists.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
@@ -57,6 +62,7 @@ typedef struct {
     int32_t E, k;
     int32_t act_dtype; /* x and gate_w: ORC_F32 or ORC_BF16                 */
     int32_t w_dtype;   /* W1, W3, W2: ORC_F32, ORC_BF16 or ORC_FP8          */
+    int32_t n_shared;  /* shared experts, weights at list index E + s       */
 } orc_problem;
 
 /* ------------------------------------------------------------------ */
@@ -413,7 +419,8 @@ static void expert_ffn(const orc_problem *p, int nr, const double *rows,
 /* Layer forward for a list of tokens.
  *
  * W1[e], W3[e]: [d x f]; W2[e]: [f x d], one pointer per expert (an expert no
- * listed token routes to may be NULL).  For FP8 weights W1s/W3s/W2s[e] point
+ * listed token routes to may be NULL); entries E .. E + n_shared - 1 are the
+ * shared experts (never NULL when n_shared > 0).  For FP8 weights W1s/W3s/W2s[e] point
  * to the [K/128 x N/128] fp32 block scales of that expert's [K x N] matrix;
  * otherwise they are NULL.  x is the full [T x d] activation matrix, gate_w is
  * [d x E], bias is [E] or NULL.
@@ -438,8 +445,14 @@ int orc_forward(const orc_problem *p, const void *x, const void *gate_w,
     int64_t nitems = 0, *item_e, *item_beg, *item_len;
     int bad = 0;
     init_e4m3_values();
-    if (k < 1 || k > p->E || k > 512)
+    if (k < 1 || k > p->E || k > 512 || p->n_shared < 0)
         bad = 1;
+    for (int s = 0; s < p->n_shared && !bad; ++s) {
+        int e = p->E + s;
+        if (!W1[e] || !W3[e] || !W2[e] ||
+            (p->w_dtype == ORC_FP8 && (!W1s[e] || !W3s[e] || !W2s[e])))
+            bad = 1;
+    }
 
     /* gate, token by token */
     for (it = 0; it < ntok && !bad; ++it) {
@@ -502,15 +515,41 @@ int orc_forward(const orc_problem *p, const void *x, const void *gate_w,
         free(yb);
     }
 
-    /* combine: gate-weighted sum over the k slots of each token, j ascending */
+    /* shared experts: every listed token, blocks of ORC_BLOCK tokens */
+    double *ys = NULL;
+    if (p->n_shared > 0) {
+        int64_t nsb = (ntok + ORC_BLOCK - 1) / ORC_BLOCK;
+        ys = (double *)malloc(sizeof(double) * (size_t)(p->n_shared * ntok * d));
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t wi = 0; wi < p->n_shared * nsb; ++wi) {
+            int e = p->E + (int)(wi / nsb);
+            int64_t t0 = (wi % nsb) * ORC_BLOCK;
+            int nr = (int)((ntok - t0) < ORC_BLOCK ? (ntok - t0) : ORC_BLOCK), r;
+            double *rows = (double *)malloc(sizeof(double) * (size_t)(nr * d));
+            for (r = 0; r < nr; ++r)
+                expert_input_row(p, x, tokens[t0 + r], rows + r * d);
+            expert_ffn(p, nr, rows, W1[e], W3[e], W2[e],
+                       p->w_dtype == ORC_FP8 ? W1s[e] : NULL,
+                       p->w_dtype == ORC_FP8 ? W3s[e] : NULL,
+                       p->w_dtype == ORC_FP8 ? W2s[e] : NULL,
+                       ys + ((int64_t)(e - p->E) * ntok + t0) * d);
+            free(rows);
+        }
+    }
+
+    /* combine: gate-weighted sum over the k slots of each token, j ascending,
+     * then the shared experts, s ascending */
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < ntok; ++t)
         for (int64_t m = 0; m < d; ++m) {
             double acc = 0.0;
             for (int64_t j = 0; j < k; ++j)
                 acc += (double)w[t * k + j] * y[(t * k + j) * d + m];
+            for (int s = 0; s < p->n_shared; ++s)
+                acc += ys[((int64_t)s * ntok + t) * d + m];
             out[t * d + m] = acc;
         }
+    free(ys);
     if (ids_out)
         memcpy(ids_out, ids, sizeof(int32_t) * (size_t)npair);
     if (w_out)

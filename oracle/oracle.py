@@ -29,6 +29,7 @@ class _Problem(ctypes.Structure):
         ("k", ctypes.c_int32),
         ("act_dtype", ctypes.c_int32),
         ("w_dtype", ctypes.c_int32),
+        ("n_shared", ctypes.c_int32),
     ]
 
 
@@ -81,8 +82,8 @@ def _act(a, act_dtype):
     return _c(a, np.float32 if act_dtype == ORC_F32 else np.uint16)
 
 
-def _problem(T, d, f, E, k, act_dtype, w_dtype):
-    return _Problem(T, d, f, E, k, act_dtype, w_dtype)
+def _problem(T, d, f, E, k, act_dtype, w_dtype, n_shared=0):
+    return _Problem(T, d, f, E, k, act_dtype, w_dtype, n_shared)
 
 
 def route(x, gate_w, bias, k, act_dtype):
@@ -129,11 +130,13 @@ def permute(ids, E):
 
 
 def forward(x, gate_w, bias, W1, W3, W2, k, act_dtype, w_dtype, tokens=None,
-            W1s=None, W3s=None, W2s=None):
+            W1s=None, W3s=None, W2s=None, n_shared=0):
     """Layer forward for the listed tokens (all tokens if None).
 
-    W1, W3, W2: sequences of E per-expert arrays ([d x f], [d x f], [f x d]);
-    an entry may be None for an expert none of the listed tokens routes to.
+    W1, W3, W2: sequences of E + n_shared per-expert arrays ([d x f],
+    [d x f], [f x d]), the n_shared shared experts last; a routed entry may
+    be None for an expert none of the listed tokens routes to.  Shared
+    experts see every token and are added with weight 1.
     For FP8 weights (uint8 codes) W1s/W3s/W2s hold each expert's fp32
     [K/128 x N/128] block scales.
     Returns (out fp64 [ntok x d] unrounded, ids [ntok x k], w [ntok x k]).
@@ -147,9 +150,11 @@ def forward(x, gate_w, bias, W1, W3, W2, k, act_dtype, w_dtype, tokens=None,
     wdt = {ORC_F32: np.float32, ORC_BF16: np.uint16, ORC_FP8: np.uint8}[w_dtype]
     keep = []
 
+    ne = E + n_shared
+
     def plist(arrs, dt):
-        ptrs = (ctypes.c_void_p * E)()
-        for e in range(E):
+        ptrs = (ctypes.c_void_p * ne)()
+        for e in range(ne):
             a = None if arrs is None else arrs[e]
             if a is not None:
                 a = _c(a, dt)
@@ -175,7 +180,7 @@ def forward(x, gate_w, bias, W1, W3, W2, k, act_dtype, w_dtype, tokens=None,
     out = np.empty((ntok, d), np.float64)
     ids = np.empty((ntok, k), np.int32)
     w = np.empty((ntok, k), np.float32)
-    p = _problem(T, d, f, E, k, act_dtype, w_dtype)
+    p = _problem(T, d, f, E, k, act_dtype, w_dtype, n_shared)
     cp = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
     rc = lib.orc_forward(ctypes.byref(p), _ptr(x), _ptr(gate_w), _ptr(bias),
                          cp(p1), cp(p3), cp(p2), cp(s1), cp(s3), cp(s2),
