@@ -142,13 +142,14 @@ def _traffic(workload, kernel):
 
 def _stage_work(cfg, counts):
     """Algorithmic work per launch of each GEMM stage: FLOPs, and HBM bytes
-    (weights of the experts that receive a token, activations in, outputs)."""
+    (weights of the experts that receive a token, activations in, outputs).
+    Shared experts count as experts hit by every token: T more rows each."""
     import numpy as np
     es = {0: 4, 1: 2, 2: 1}[cfg.w_dtype]
     ae = {0: 4, 1: 2}[cfg.act_dtype] if cfg.w_dtype != 2 else 1
     he = {0: 4, 1: 2, 2: 1}[cfg.w_dtype]
-    hit = int(np.count_nonzero(counts))
-    n = cfg.T * cfg.k
+    hit = int(np.count_nonzero(counts)) + cfg.n_shared
+    n = cfg.T * (cfg.k + cfg.n_shared)
     w13 = dict(flops=4.0 * n * cfg.d * cfg.f,
                bytes=hit * 2.0 * cfg.d * cfg.f * es + cfg.T * cfg.d * ae + n * cfg.f * he)
     w2 = dict(flops=2.0 * n * cfg.d * cfg.f,
@@ -172,13 +173,14 @@ def _cpu_baseline(cfg, inp, out_gpu, target_s):
     def run(rows):
         x = host_arrays(inp["x"][torch.as_tensor(rows, device=inp["x"].device)])
         _, ids, _ = oracle.route(x, gw, bias, cfg.k, orc[cfg.act_dtype])
-        for e in sorted(set(int(v) for v in ids.reshape(-1))):
+        need = set(int(v) for v in ids.reshape(-1)) | set(range(cfg.E, cfg.E + cfg.n_shared))
+        for e in sorted(need):
             if e not in host_w:
                 host_w[e] = {n: host_arrays(inp[n][e]) for n in ("W1", "W3", "W2")}
                 if cfg.w_dtype == 2:
                     host_w[e].update({n + "s": inp[n + "s"][e].cpu().numpy()
                                       for n in ("W1", "W3", "W2")})
-        W = {n: [host_w.get(e, {}).get(n) for e in range(cfg.E)]
+        W = {n: [host_w.get(e, {}).get(n) for e in range(cfg.E + cfg.n_shared)]
              for n in ("W1", "W3", "W2", "W1s", "W3s", "W2s")}
         fp8 = cfg.w_dtype == 2
         t0 = time.perf_counter()
@@ -186,7 +188,7 @@ def _cpu_baseline(cfg, inp, out_gpu, target_s):
                                    orc[cfg.act_dtype], orc[cfg.w_dtype],
                                    W1s=W["W1s"] if fp8 else None,
                                    W3s=W["W3s"] if fp8 else None,
-                                   W2s=W["W2s"] if fp8 else None)
+                                   W2s=W["W2s"] if fp8 else None, n_shared=cfg.n_shared)
         return out, time.perf_counter() - t0
 
     rng = np.random.default_rng(0)
@@ -283,7 +285,7 @@ def main():
     work = _stage_work(cfg, counts.cpu().numpy())
     dom = max(("gemm_w13_swiglu", "gemm_w2"), key=lambda k: stage_ms[k])
     dom_s = stage_ms[dom] * 1e-3
-    decode = cfg.T * cfg.k / cfg.E < 16
+    decode = cfg.T * cfg.k / cfg.E < 16  # expected rows per routed expert
     copy_gbps = _copy_gbps(torch)
     if decode:
         achieved = work[dom]["bytes"] / dom_s / 1e9
@@ -330,7 +332,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
-                   "top_k": cfg.k, "parallelism": "single GPU"},
+                   "top_k": cfg.k, "n_shared": cfg.n_shared, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages_ms": stage_ms,

@@ -81,6 +81,12 @@ typedef enum {
  *              expected tokens per expert T*top_k/E (the serving-regime choice
  *              of the MegaMoE-vs-MoE-systems page, section 2.5, re-tuned for
  *              MFMA tiles).  Otherwise one of 16, 32, 64, 128, 256.
+ * n_shared: shared experts, 0..8 (MegaMoE-vs-MoE-systems page, section 2.7:
+ *            the shared expert's GEMMs are phases of the same task queue as
+ *            the routed ones).  A shared expert sees every token and its
+ *            output is added with weight 1 after the gate-weighted routed
+ *            sum; its weights follow the E routed experts' in W1/W3/W2 (and
+ *            their FP8 scales), which then hold E + n_shared experts.
  * d and f must be multiples of 32 (fp32 weights), 64 (bf16) or 128 (FP8), and
  * x, h and one expert's weight matrix must each span less than 2^31 bytes
  * (MOE_ERR_UNSUPPORTED otherwise). */
@@ -91,6 +97,7 @@ typedef struct {
     int32_t w_dtype;
     int32_t out_dtype;
     int32_t block_m;
+    int32_t n_shared;
 } moe_problem;
 
 /* Optional device outputs filled from inside moe_forward, so that the routing
@@ -129,7 +136,7 @@ int moe_last_hip_error(void);
  * moe_permute and moe_forward need for this problem.  A pure function of the
  * problem, never of the routing: the dropless worst case of T*k slot rows
  * (the worst-case pool of the MegaMoE-vs-MoE-systems page, section 2.6, with
- * one rank), plus tables, tile maps and FP8 scales. */
+ * one rank) plus T rows per shared expert, tables, tile maps and FP8 scales. */
 moe_status moe_workspace_size(const moe_problem *p, size_t *bytes);
 
 /* Gate (FlashMoE Kernel page, opening paragraph: the first stage).
@@ -156,7 +163,8 @@ moe_status moe_route(const moe_problem *p, const void *x, const void *gate_w,
  *   slot_token [T*k] source token of each slot
  *   slot_k     [T*k] source top-k index of each slot
  *   token_slot [T*k] inverse: slot of (t, j) at index t*k + j
- *   ws/ws_bytes workspace of at least moe_workspace_size(). */
+ *   ws/ws_bytes workspace of at least moe_workspace_size().
+ * Only the routed experts are permuted here (n_shared is ignored). */
 moe_status moe_permute(const moe_problem *p, const int32_t *topk_ids,
                        int32_t *counts, int32_t *offsets, int32_t *slot_token,
                        int32_t *slot_k, int32_t *token_slot, void *ws,
@@ -169,7 +177,7 @@ moe_status moe_quantize_fp8(int64_t rows, int64_t cols, const void *x_bf16,
                             uint8_t *q, float *s, hipStream_t stream);
 
 /* Bytes of each expert-weight tensor in the layout moe_forward reads
- * (element size of w_dtype times E*d*f). */
+ * (element size of w_dtype times (E + n_shared)*d*f). */
 moe_status moe_weight_bytes(const moe_problem *p, size_t *bytes);
 
 /* One-time weight re-layout (untimed, done when weights are loaded): each
@@ -184,10 +192,11 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
  *   x       [T][d]       act_dtype
  *   gate_w  [d][E]       act_dtype
  *   bias    [E]          fp32 or NULL
- *   W1t,W3t [E][f][d]    w_dtype, packed by moe_pack_weight (gate, up)
- *   W2t     [E][d][f]    w_dtype, packed by moe_pack_weight (down)
- *   W1s,W3s [E][d/128][f/128] fp32 block scales (FP8 only, else NULL)
- *   W2s     [E][f/128][d/128] fp32 block scales (FP8 only, else NULL)
+ *   W1t,W3t [E+S][f][d]  w_dtype, packed by moe_pack_weight (gate, up)
+ *   W2t     [E+S][d][f]  w_dtype, packed by moe_pack_weight (down)
+ *   W1s,W3s [E+S][d/128][f/128] fp32 block scales (FP8 only, else NULL)
+ *   W2s     [E+S][f/128][d/128] fp32 block scales (FP8 only, else NULL)
+ *           (S = n_shared: the shared experts follow the routed ones)
  *   out     [T][d]       out_dtype
  *   ws/ws_bytes          workspace of at least moe_workspace_size()
  *   dbg                  NULL, or device buffers receiving the routing used.

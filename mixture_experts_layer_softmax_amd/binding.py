@@ -28,7 +28,8 @@ class MoEProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64),
                 ("E", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("block_m", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32)]
 
 
 NUM_STAGE_EVENTS = 7
@@ -103,13 +104,15 @@ def _check(fn, rc):
         raise MoEError(fn, rc, load().moe_last_hip_error())
 
 
-def problem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m=0) -> MoEProblem:
-    return MoEProblem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m)
+def problem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m=0,
+            n_shared=0) -> MoEProblem:
+    return MoEProblem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m, n_shared)
 
 
 def problem_of(cfg, T=None, block_m=0, out_dtype=None) -> MoEProblem:
     return problem(cfg.T if T is None else T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act_dtype,
-                   cfg.w_dtype, cfg.out_dtype if out_dtype is None else out_dtype, block_m)
+                   cfg.w_dtype, cfg.out_dtype if out_dtype is None else out_dtype, block_m,
+                   cfg.n_shared)
 
 
 def workspace_size(p: MoEProblem) -> int:

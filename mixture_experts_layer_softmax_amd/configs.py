@@ -23,6 +23,7 @@ class MoEConfig:
     out_dtype: int
     skew_bias: bool = False  # router bias_e = -1.2 ln(pi(e)+1)
     seed: int = 0
+    n_shared: int = 0        # shared experts: every token, weight 1
 
     @property
     def slots(self) -> int:
@@ -30,8 +31,8 @@ class MoEConfig:
 
     @property
     def expert_flops(self) -> float:
-        """Algorithmic expert-GEMM FLOPs: 2 * T*k * 3 * d * f."""
-        return 2.0 * self.T * self.k * 3 * self.d * self.f
+        """Algorithmic expert-GEMM FLOPs: 2 * T*(k + n_shared) * 3 * d * f."""
+        return 2.0 * self.T * (self.k + self.n_shared) * 3 * self.d * self.f
 
     @property
     def router_flops(self) -> float:
@@ -44,12 +45,17 @@ class MoEConfig:
 
 
 CONFIGS = {
+    # the five stated workloads
     "tiny_fp32": MoEConfig("tiny_fp32", 64, 128, 256, 8, 2, F32, F32, F32),
     "prefill_bf16": MoEConfig("prefill_bf16", 16384, 2048, 2048, 32, 2, BF16, BF16, BF16),
     "decode_bf16": MoEConfig("decode_bf16", 64, 7168, 2048, 256, 8, BF16, BF16, BF16),
     "skewed_bf16": MoEConfig("skewed_bf16", 8192, 4096, 1536, 64, 6, BF16, BF16, BF16,
                              skew_bias=True),
     "prefill_fp8": MoEConfig("prefill_fp8", 32768, 7168, 2048, 256, 8, BF16, FP8, BF16),
+    # the prefill workload with one shared expert of the routed experts' shape
+    # (the shared-expert phases of the MegaMoE-vs-MoE-systems page, section 2.7)
+    "prefill_bf16_shared": MoEConfig("prefill_bf16_shared", 16384, 2048, 2048, 32, 2, BF16,
+                                     BF16, BF16, n_shared=1),
 }
 
 ORDER = ["tiny_fp32", "prefill_bf16", "decode_bf16", "skewed_bf16", "prefill_fp8"]

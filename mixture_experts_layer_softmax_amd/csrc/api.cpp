@@ -55,7 +55,8 @@ bool valid_problem(const moe_problem* p) {
   if (!p) return false;
   if (p->T < 0 || p->d <= 0 || p->f <= 0) return false;
   if (p->E < 1 || p->E > 1024 || p->top_k < 1 || p->top_k > p->E) return false;
-  if (p->T > (1ll << 31) / 1024 || p->T * p->top_k > (1ll << 30)) return false;
+  if (p->n_shared < 0 || p->n_shared > 8) return false;
+  if (p->T > (1ll << 31) / 1024 || p->T * (p->top_k + p->n_shared) > (1ll << 30)) return false;
   const bool ok_types = (p->act_dtype == MOE_F32 && p->w_dtype == MOE_F32) ||
                         (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_BF16) ||
                         (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_FP8_E4M3);
@@ -67,6 +68,10 @@ bool valid_problem(const moe_problem* p) {
   return true;
 }
 
+// Expert rows of the grouped GEMMs: the T*k routed slots, then T per shared
+// expert.
+int64_t gemm_rows(const moe_problem& p) { return p.T * (p.top_k + p.n_shared); }
+
 // Shapes the kernels support (valid but unsupported -> MOE_ERR_UNSUPPORTED):
 // contraction rows of 128 bytes, and every GEMM operand addressable with
 // 32-bit byte offsets (x or its FP8 codes, h, one expert's weight matrix).
@@ -75,7 +80,7 @@ bool supported_shape(const moe_problem* p) {
   if (p->d % m != 0 || p->f % m != 0) return false;
   const int64_t es = p->w_dtype == MOE_F32 ? 4 : (p->w_dtype == MOE_BF16 ? 2 : 1);
   const int64_t lim = 1ll << 31;
-  return p->T * p->d * es < lim && p->T * p->top_k * p->f * es < lim && p->d * p->f * es < lim;
+  return p->T * p->d * es < lim && gemm_rows(*p) * p->f * es < lim && p->d * p->f * es < lim;
 }
 
 struct Layout {
@@ -91,8 +96,10 @@ Layout make_layout(const moe_problem& p) {
   Layout L{};
   const int64_t n = p.T * p.top_k;
   const int64_t nchunk = ceil_div(n, moe::permute_chunk(n));
+  const int64_t rows = gemm_rows(p);
   L.bm = pick_bm(p);
-  L.max_mtiles = (n + static_cast<int64_t>(p.E) * (L.bm - 1)) / L.bm + 1;
+  L.max_mtiles = (n + static_cast<int64_t>(p.E) * (L.bm - 1)) / L.bm + 1 +
+                 static_cast<int64_t>(p.n_shared) * ceil_div(p.T, L.bm);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -105,8 +112,8 @@ Layout make_layout(const moe_problem& p) {
   L.table = take(sizeof(int32_t) * nchunk * p.E);
   L.counts = take(sizeof(int32_t) * p.E);
   L.offsets = take(sizeof(int32_t) * (p.E + 1));
-  L.slot_token = take(sizeof(int32_t) * n);
-  L.slot_k = take(sizeof(int32_t) * n);
+  L.slot_token = take(sizeof(int32_t) * rows);
+  L.slot_k = take(sizeof(int32_t) * rows);
   L.token_slot = take(sizeof(int32_t) * n);
   L.tm_e = take(sizeof(int32_t) * L.max_mtiles);
   L.tm_row0 = take(sizeof(int32_t) * L.max_mtiles);
@@ -115,9 +122,9 @@ Layout make_layout(const moe_problem& p) {
   const bool fp8 = p.w_dtype == MOE_FP8_E4M3;
   L.xq = take(fp8 ? static_cast<size_t>(p.T) * p.d : 0);
   L.sx = take(fp8 ? sizeof(float) * p.T * (p.d / 128) : 0);
-  L.hs = take(fp8 ? sizeof(float) * n * (p.f / 128) : 0);
-  L.h = take(static_cast<size_t>(n) * p.f * esize(p.w_dtype == MOE_FP8_E4M3 ? MOE_FP8_E4M3 : p.act_dtype));
-  L.y = take(sizeof(float) * n * p.d);
+  L.hs = take(fp8 ? sizeof(float) * rows * (p.f / 128) : 0);
+  L.h = take(static_cast<size_t>(rows) * p.f * esize(p.w_dtype == MOE_FP8_E4M3 ? MOE_FP8_E4M3 : p.act_dtype));
+  L.y = take(sizeof(float) * rows * p.d);
   L.total = off;
   return L;
 }
@@ -179,7 +186,7 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
 
 moe_status moe_weight_bytes(const moe_problem* p, size_t* bytes) {
   if (!valid_problem(p) || !bytes) return MOE_ERR_INVALID_ARG;
-  *bytes = static_cast<size_t>(p->E) * p->d * p->f * esize(p->w_dtype);
+  *bytes = static_cast<size_t>(p->E + p->n_shared) * p->d * p->f * esize(p->w_dtype);
   return MOE_OK;
 }
 
@@ -213,7 +220,7 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* c
   const Layout L = make_layout(*p);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   (void)hipGetLastError();
-  moe::launch_permute(topk_ids, static_cast<int>(p->T), p->top_k, p->E, L.bm,
+  moe::launch_permute(topk_ids, static_cast<int>(p->T), p->top_k, p->E, 0, L.bm,
                       at<int32_t>(ws, L.table), counts, offsets, slot_token, slot_k, token_slot,
                       tile_map(ws, L), stream);
   return hip_status();
@@ -285,8 +292,8 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
                           at<float>(ws, L.sx), stream);
   mark(2);
   // 3. histogram, scan + tile map, scatter
-  moe::launch_permute(ids, T, k, E, L.bm, at<int32_t>(ws, L.table), counts, offsets, slot_token,
-                      slot_k, token_slot, tm, stream);
+  moe::launch_permute(ids, T, k, E, p->n_shared, L.bm, at<int32_t>(ws, L.table), counts,
+                      offsets, slot_token, slot_k, token_slot, tm, stream);
   mark(3);
   moe_status st = hip_status();
   if (st != MOE_OK) return st;
@@ -338,7 +345,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   mark(5);
 
   // 6. combine
-  moe::launch_combine(at<float>(ws, L.y), w, token_slot, out, T, d, k,
+  moe::launch_combine(at<float>(ws, L.y), w, token_slot, out, T, d, k, p->n_shared,
                       p->out_dtype == MOE_BF16, stream);
   mark(6);
 

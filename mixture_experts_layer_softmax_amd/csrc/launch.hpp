@@ -61,7 +61,10 @@ void launch_logits(const void* x, const void* gate_w, const float* bias, float* 
                    int T, int d, int E, bool bf16, hipStream_t s);
 void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
                  hipStream_t s);
-void launch_permute(const int32_t* ids, int T, int k, int E, int bm, int32_t* table,
+// S shared experts add T slots each after the T*k routed ones (slot
+// T*k + s*T + t holds token t, k-slot k + s) and their m-tiles after the
+// routed ones.
+void launch_permute(const int32_t* ids, int T, int k, int E, int S, int bm, int32_t* table,
                     int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_k,
                     int32_t* token_slot, TileMap tm, hipStream_t s);
 void launch_quant_fp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
@@ -71,7 +74,7 @@ int launch_gemm(int phase, int dtype, int bm, const GemmArgs& a, hipStream_t s);
 // Column tiles per m-tile for a phase (depends on the kernel variant).
 int gemm_tile_n(int phase, int dtype, int bm);
 void launch_combine(const float* Y, const float* w, const int32_t* token_slot, void* out,
-                    int T, int d, int k, bool out_bf16, hipStream_t s);
+                    int T, int d, int k, int S, bool out_bf16, hipStream_t s);
 void launch_pack(int E, int64_t K, int64_t N, int elem_bytes, const void* src, void* dst,
                  hipStream_t s);
 

@@ -44,16 +44,21 @@ __global__ __launch_bounds__(64) void hist_kernel(const int32_t* __restrict__ id
 
 // One workgroup of 1024 threads.  table [nchunk x E] in, becomes the base slot
 // of each (chunk, expert).  Also writes counts/offsets, the m-tile map for
-// tile height bm and zeroes the GEMM work-queue counters.  When the table
+// tile height bm and zeroes the GEMM work-queue counters.  The S shared
+// experts (every token, after the routed slots) get their slot records and
+// m-tiles here too.  When the table
 // fits (LDS_TABLE), it is scanned in LDS: loaded and stored back coalesced by
 // all threads, each expert's column summed by one thread from LDS.
 template <bool LDS_TABLE>
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table, int nchunk,
                                                     int E, int bm, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
-                                                    TileMap tm) {
+                                                    TileMap tm, int T, int k, int S,
+                                                    int32_t* __restrict__ slot_token,
+                                                    int32_t* __restrict__ slot_k) {
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t s_tiles[1024];
+  __shared__ int32_t s_shared_tile0;  // first m-tile of the shared experts
   extern __shared__ int32_t s_tab[];  // [nchunk][E] when LDS_TABLE
   int32_t* tab = LDS_TABLE ? s_tab : table;
   const int tid = threadIdx.x;
@@ -93,7 +98,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
       acc_t += t;
     }
     offsets[E] = acc_c;
-    *tm.n_mtiles = acc_t;
+    s_shared_tile0 = acc_t;
+    *tm.n_mtiles = acc_t + S * ((T + bm - 1) / bm);
     for (int q = 0; q < kQueueWords; ++q) tm.queue[q] = 0;
   }
   __syncthreads();
@@ -113,6 +119,23 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
   if (LDS_TABLE) {
     __syncthreads();  // column sums and s_cnt (expert offsets) are final
     for (int i = tid; i < cells; i += 1024) table[i] = s_tab[i] + s_cnt[i % E];
+  }
+  if (S > 0) {
+    // shared experts: slot T*k + s*T + t holds (token t, k-slot k + s); their
+    // m-tiles follow the routed ones, expert index E + s
+    __syncthreads();
+    const int mt_per = (T + bm - 1) / bm, t_sh0 = s_shared_tile0;
+    const int64_t base = static_cast<int64_t>(T) * k;
+    for (int64_t i = tid; i < static_cast<int64_t>(S) * T; i += 1024) {
+      slot_token[base + i] = static_cast<int32_t>(i % T);
+      slot_k[base + i] = k + static_cast<int32_t>(i / T);
+    }
+    for (int i = tid; i < S * mt_per; i += 1024) {
+      const int sh = i / mt_per, m = i - sh * mt_per;
+      tm.e[t_sh0 + i] = E + sh;
+      tm.row0[t_sh0 + i] = static_cast<int32_t>(base + static_cast<int64_t>(sh) * T + m * bm);
+      tm.rows[t_sh0 + i] = min(bm, T - m * bm);
+    }
   }
 }
 
@@ -151,7 +174,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 
 }  // namespace
 
-void launch_permute(const int32_t* ids, int T, int k, int E, int bm, int32_t* table,
+void launch_permute(const int32_t* ids, int T, int k, int E, int S, int bm, int32_t* table,
                     int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_k,
                     int32_t* token_slot, TileMap tm, hipStream_t s) {
   const int n = T * k;
@@ -168,9 +191,11 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int bm, int32_t* ta
                                                   static_cast<int>(kMaxTab)) == hipSuccess;
   const size_t tab_bytes = sizeof(int32_t) * static_cast<size_t>(nchunk) * E;
   if (tab_bytes <= (big_lds ? kMaxTab : 64 * 1024))
-    scan_kernel<true><<<1, 1024, tab_bytes, s>>>(table, nchunk, E, bm, counts, offsets, tm);
+    scan_kernel<true><<<1, 1024, tab_bytes, s>>>(table, nchunk, E, bm, counts, offsets, tm, T,
+                                                 k, S, slot_token, slot_k);
   else
-    scan_kernel<false><<<1, 1024, 0, s>>>(table, nchunk, E, bm, counts, offsets, tm);
+    scan_kernel<false><<<1, 1024, 0, s>>>(table, nchunk, E, bm, counts, offsets, tm, T, k, S,
+                                          slot_token, slot_k);
   if (nchunk > 0)
     scatter_kernel<<<nchunk, 64, lds, s>>>(ids, n, k, E, nbits, chunk, table, slot_token,
                                            slot_k, token_slot);

@@ -7,7 +7,8 @@ exact bits produced here.
 Recipe (per workload, seed s):
   x       ~ N(0, 1)     [T x d], rounded once to the activation type
   gate_w  ~ N(0, 0.02)  [d x E] (0.02 is the standard deviation)
-  W1, W3  ~ N(0, 0.02)  [E][d][f];  W2 ~ N(0, 0.02) [E][f][d]
+  W1, W3  ~ N(0, 0.02)  [E+S][d][f];  W2 ~ N(0, 0.02) [E+S][f][d] (S shared
+          experts drawn after the E routed ones)
   bias (skewed workload): bias_e = -1.2 ln(pi(e) + 1), pi a seeded random
           permutation of the experts, fp32
   FP8 weights: drawn fp32, then stored as E4M3FN codes with one fp32 scale per
@@ -72,30 +73,32 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: int | None = None,
     """Draw the layer inputs of `cfg` on `device`.
 
     Returns a dict with x, gate_w, bias (or None), W1, W3, W2 and, for FP8
-    weights, W1s, W3s, W2s.  Weight tensors are [E][K][N] in the stated
-    layouts (W1/W3 [E][d][f], W2 [E][f][d]).  `experts` (optional) limits the
-    weight draw to those expert indices (others stay zero) -- a test
+    weights, W1s, W3s, W2s.  Weight tensors are [E+S][K][N] in the stated
+    layouts (W1/W3 [.][d][f], W2 [.][f][d]), the S shared experts last.
+    `experts` (optional) limits the weight draw to those expert indices
+    (others stay zero) -- a test
     convenience only; the draws of the listed experts do not change.
     """
     seed = cfg.seed if seed is None else seed
     T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
+    NE = E + cfg.n_shared  # weight sets: routed, then shared
     act = _tdtype(cfg.act_dtype)
     out = {}
     out["x"] = _normal((T, d), 1.0, _gen(seed, "x", device), device).to(act)
     out["gate_w"] = _normal((d, E), 0.02, _gen(seed, "gate_w", device), device).to(act)
     out["bias"] = skew_bias(E, seed).to(device) if cfg.skew_bias else None
 
-    wanted = set(range(E)) if experts is None else set(int(e) for e in experts)
+    wanted = set(range(NE)) if experts is None else set(int(e) for e in experts)
     for name, (K, N) in (("W1", (d, f)), ("W3", (d, f)), ("W2", (f, d))):
         g = _gen(seed, name, device)
         if cfg.w_dtype == FP8:
-            codes = torch.zeros((E, K, N), dtype=torch.uint8, device=device)
-            scales = torch.zeros((E, (K + 127) // 128, (N + 127) // 128),
+            codes = torch.zeros((NE, K, N), dtype=torch.uint8, device=device)
+            scales = torch.zeros((NE, (K + 127) // 128, (N + 127) // 128),
                                  dtype=torch.float32, device=device)
         else:
-            codes = torch.zeros((E, K, N), dtype=_tdtype(cfg.w_dtype), device=device)
+            codes = torch.zeros((NE, K, N), dtype=_tdtype(cfg.w_dtype), device=device)
             scales = None
-        for e in range(E):
+        for e in range(NE):
             # every expert is drawn in order so that a subset draw reproduces
             # the full draw bit for bit
             w = _normal((K, N), 0.02, g, device)

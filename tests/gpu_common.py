@@ -33,12 +33,13 @@ def oracle_route_rows(cfg, inp, rows):
 
 def oracle_forward_rows(cfg, inp, rows):
     """Oracle forward of the listed token rows; copies only the experts those
-    tokens route to (routing taken from the oracle's own gate)."""
+    tokens route to (routing taken from the oracle's own gate) and the shared
+    experts, which every token uses."""
     rows = np.asarray(rows, np.int64)
     _, ids, _ = oracle_route_rows(cfg, inp, rows)
-    need = sorted(set(int(e) for e in ids.reshape(-1)))
     E = cfg.E
-    W = {n: [None] * E for n in ("W1", "W3", "W2", "W1s", "W3s", "W2s")}
+    need = sorted(set(int(e) for e in ids.reshape(-1))) + list(range(E, E + cfg.n_shared))
+    W = {n: [None] * (E + cfg.n_shared) for n in ("W1", "W3", "W2", "W1s", "W3s", "W2s")}
     for e in need:
         for n in ("W1", "W3", "W2"):
             W[n][e] = host_arrays(inp[n][e])
@@ -51,7 +52,7 @@ def oracle_forward_rows(cfg, inp, rows):
     out, ids, w = oracle.forward(x, gw, bias, W["W1"], W["W3"], W["W2"], cfg.k,
                                  ORC[cfg.act_dtype], ORC[cfg.w_dtype],
                                  W1s=W["W1s"] if fp8 else None, W3s=W["W3s"] if fp8 else None,
-                                 W2s=W["W2s"] if fp8 else None)
+                                 W2s=W["W2s"] if fp8 else None, n_shared=cfg.n_shared)
     return out, ids, w
 
 

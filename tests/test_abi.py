@@ -48,10 +48,23 @@ def test_workspace_size_is_pure_and_checks_args():
                 B.problem(16, 64, 64, 0, 1, 1, 1, 1),       # no experts
                 B.problem(16, 64, 64, 4, 2, 0, 1, 1),       # fp32 x with bf16 weights
                 B.problem(16, 64, 64, 4, 2, 1, 1, 2),       # FP8 output
-                B.problem(16, 64, 64, 4, 2, 1, 1, 1, 48)):  # unknown tile height
+                B.problem(16, 64, 64, 4, 2, 1, 1, 1, 48),   # unknown tile height
+                B.problem(16, 64, 64, 4, 2, 1, 1, 1, 0, 9),  # too many shared experts
+                B.problem(16, 64, 64, 4, 2, 1, 1, 1, 0, -1)):
         with pytest.raises(B.MoEError) as e:
             B.workspace_size(bad)
         assert e.value.code == 1
+
+
+def test_shared_experts_size_workspace_and_weights():
+    # each shared expert adds T slot rows (h and Y) and one weight set
+    _lib()
+    base = B.problem(4096, 1024, 512, 16, 2, 1, 1, 1)
+    sh = B.problem(4096, 1024, 512, 16, 2, 1, 1, 1, 0, 2)
+    assert B.weight_bytes(base) == 16 * 1024 * 512 * 2
+    assert B.weight_bytes(sh) == 18 * 1024 * 512 * 2
+    grow = B.workspace_size(sh) - B.workspace_size(base)
+    assert grow >= 2 * 4096 * (512 * 2 + 1024 * 4)
 
 
 def test_null_pointers_rejected_before_launch():

@@ -198,15 +198,70 @@ def test_gemm_clock_record():
 
 
 # ---------------------------------------------------------------------------
+# shared experts: every token, weight 1, after the routed sum
+# ---------------------------------------------------------------------------
+
+SHARED = {
+    "sh_fp32": CONFIGS["tiny_fp32"].replace(name="sh_fp32", n_shared=1),
+    "sh_bf16": REDUCED["prefill_bf16_r"].replace(name="sh_bf16", n_shared=2),
+    "sh_decode": REDUCED["decode_bf16_r"].replace(name="sh_decode", n_shared=1),
+    "sh_fp8": REDUCED["prefill_fp8_r"].replace(name="sh_fp8", n_shared=1),
+    "sh_T1": EDGE["T1"].replace(name="sh_T1", n_shared=3),
+    "sh_ragged": EDGE["ragged"].replace(name="sh_ragged", n_shared=1),
+}
+
+
+@pytest.mark.parametrize("name", list(SHARED))
+def test_shared_expert_parity(name):
+    cfg = SHARED[name]
+    say("shared", name)
+    inp = gpu_inputs(cfg)
+    ref, _, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
+    if cfg.w_dtype == BF16:
+        _outputs_ok(cfg, _forward(cfg, inp, out_dtype=F32), ref, "fp32 out")
+    _outputs_ok(cfg, _forward(cfg, inp), ref, "native out")
+
+
+@pytest.mark.parametrize("block_m", [16, 64, 256])
+def test_shared_expert_tile_heights(block_m):
+    cfg = SHARED["sh_bf16"]
+    say("shared bm", block_m)
+    inp = gpu_inputs(cfg)
+    ref, _, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
+    _outputs_ok(cfg, _forward(cfg, inp, out_dtype=F32, block_m=block_m), ref, f"bm={block_m}")
+
+
+def test_shared_expert_leaves_routing_alone():
+    # the shared experts change neither the routing nor its permutation, and
+    # the routed part of the output is the n_shared = 0 layer's
+    cfg = SHARED["sh_bf16"]
+    plain = cfg.replace(n_shared=0)
+    say("shared routing")
+    inp = gpu_inputs(cfg)
+    n = cfg.T * cfg.k
+    keys = ("topk_ids", "counts", "offsets", "slot_token", "slot_k", "token_slot")
+    sizes = {"counts": cfg.E, "offsets": cfg.E + 1}
+    dbgs = []
+    for c in (cfg, plain):
+        dbg = {key: torch.empty(sizes.get(key, n), dtype=torch.int32, device="cuda")
+               for key in keys}
+        _forward(c, inp, dbg=dbg)
+        dbgs.append(dbg)
+    for key in keys:
+        assert torch.equal(dbgs[0][key], dbgs[1][key]), key
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads in the launch configuration the benchmark times;
 # outputs compared on a sample of tokens the oracle computes one by one
 # ---------------------------------------------------------------------------
 
-FULL_SAMPLE = {"prefill_bf16": 48, "decode_bf16": 12, "skewed_bf16": 24, "prefill_fp8": 6}
+FULL_SAMPLE = {"prefill_bf16": 48, "decode_bf16": 12, "skewed_bf16": 24, "prefill_fp8": 6,
+               "prefill_bf16_shared": 24}
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16", "decode_bf16", "skewed_bf16",
-                                  "prefill_fp8"])
+                                  "prefill_fp8", "prefill_bf16_shared"])
 def test_full_size_parity(name):
     cfg = CONFIGS[name]
     say("full", name)
@@ -267,6 +322,9 @@ def test_abi_errors_launch_nothing():
     assert e.value.code in (1, 2)
     with pytest.raises(B.MoEError) as e:
         call(B.problem(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, F32, BF16, BF16))
+    assert e.value.code == 1
+    with pytest.raises(B.MoEError) as e:
+        call(B.problem(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, BF16, BF16, BF16, 0, 9))
     assert e.value.code == 1
     torch.cuda.synchronize()
     assert (out.float() == 7.0).all()  # nothing was written
