@@ -8,11 +8,18 @@ from .oracle import (  # noqa: F401
     ORC_BF16,
     ORC_F32,
     ORC_FP8,
+    ORC_MXFP4,
+    MX_E2M1,
+    MX_E4M3,
     build,
+    e2m1_decode,
+    e2m1_encode,
     e4m3_decode,
     e4m3_encode,
     fp8_quant_rows,
     forward,
+    mx_exponent,
+    mx_quant_rows,
     permute,
     round_bf16,
     route,

@@ -42,6 +42,16 @@
  *     0) and the code is e4m3(v / s) with an fp32 quotient.
  *   - All sums of products are exact-order fp64 loops with the contraction
  *     index ascending.
+ *   - MXFP4 layers (the FP8 x FP4 expert variant of the MegaMoE-vs-MoE-systems
+ *     page, sections 1 and 4): weights are OCP MX FP4, i.e. E2M1 codes
+ *     (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) sharing one E8M0 power-of-two
+ *     scale per 32 consecutive elements along the contraction axis; x and h
+ *     are OCP MX FP8 (E4M3 codes, one E8M0 scale per 32 consecutive
+ *     elements).  A block's scale exponent is floor(log2(amax)) minus the
+ *     element format's largest exponent (2 for E2M1, 8 for E4M3), clamped to
+ *     [-127, 127], and 0 for an all-zero block; each element is v * 2^-X
+ *     (exact) rounded to nearest, ties to even, saturating at the format's
+ *     largest magnitude.  h is requantised from fp32(h).
  *   - Shared experts (MegaMoE-vs-MoE-systems page, section 2.7: shared-expert
  *     GEMMs are phases of the same task queue as the routed ones) see every
  *     token and are added with weight 1 after the gate-weighted routed sum:
@@ -55,13 +65,14 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_MXFP4 = 3 };
+enum { ORC_MX_E4M3 = 0, ORC_MX_E2M1 = 1 }; /* element formats of the MX blocks */
 
 typedef struct {
     int64_t T, d, f;
     int32_t E, k;
     int32_t act_dtype; /* x and gate_w: ORC_F32 or ORC_BF16                 */
-    int32_t w_dtype;   /* W1, W3, W2: ORC_F32, ORC_BF16 or ORC_FP8          */
+    int32_t w_dtype;   /* W1, W3, W2: ORC_F32, ORC_BF16, ORC_FP8, ORC_MXFP4 */
     int32_t n_shared;  /* shared experts, weights at list index E + s       */
 } orc_problem;
 
@@ -98,10 +109,10 @@ double orc_e4m3_decode(uint8_t q)
 }
 
 /* OCP E4M3FN encode, round to nearest (ties to even), saturating at 448. */
-uint8_t orc_e4m3_encode(float v)
+static uint8_t e4m3_encode_d(double v)
 {
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
-    double a = fabs((double)v), quantum, r;
+    double a = fabs(v), quantum, r;
     int e, ex, m;
     if (isnan(v))
         return 0x7f;
@@ -124,6 +135,87 @@ uint8_t orc_e4m3_encode(float v)
         return sign | (uint8_t)(r / ldexp(1.0, -9));
     m = (int)(r / ldexp(1.0, ex - 3)) - 8;
     return sign | (uint8_t)(((ex + 7) << 3) | m);
+}
+
+uint8_t orc_e4m3_encode(float v) { return e4m3_encode_d((double)v); }
+
+/* OCP E2M1 (FP4) decode: 1 sign bit (bit 3), 2 exponent bits (bias 1), 1
+ * mantissa bit; exponent field 0 is subnormal (m * 0.5).  No inf or NaN. */
+double orc_e2m1_decode(uint8_t q)
+{
+    int s = (q >> 3) & 1, e = (q >> 1) & 3, m = q & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* E2M1 encode, round to nearest (ties to even), saturating at 6. */
+static uint8_t e2m1_encode_d(double v)
+{
+    uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    double a = fabs(v), r;
+    int e, ex;
+    if (isnan(v) || a >= 6.0)
+        return sign | 0x7;
+    /* binade of a: a in [2^ex, 2^(ex+1)); below 1 the spacing is 0.5 */
+    frexp(a, &e);
+    ex = e - 1;
+    if (ex < 0)
+        ex = 0;
+    r = nearbyint(a / ldexp(1.0, ex - 1)) * ldexp(1.0, ex - 1); /* exact scaling; RNE */
+    if (r == 0.0)
+        return sign;
+    if (r < 1.0) /* 0.5: the subnormal code */
+        return sign | 0x1;
+    frexp(r, &e);
+    ex = e - 1; /* 0, 1 or 2 */
+    return sign | (uint8_t)(((ex + 1) << 1) | (r > ldexp(1.0, ex) ? 1 : 0));
+}
+
+uint8_t orc_e2m1_encode(float v) { return e2m1_encode_d((double)v); }
+
+/* Shared exponent X of one MX block (scale 2^X, stored as the E8M0 byte
+ * X + 127): floor(log2(amax)) - emax, emax = 2 for E2M1 and 8 for E4M3,
+ * clamped to [-127, 127]; 0 for an all-zero block. */
+int orc_mx_exponent(float amax, int elem)
+{
+    int e, x;
+    if (amax == 0.0f)
+        return 0;
+    frexp((double)amax, &e); /* amax in [2^(e-1), 2^e) */
+    x = (e - 1) - (elem == ORC_MX_E2M1 ? 2 : 8);
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+/* MX quantisation of a [rows x cols] fp32 matrix along its rows (cols a
+ * multiple of 32): codes [rows x cols], one per byte; scales
+ * [rows x cols/32] E8M0 bytes. */
+void orc_mx_quant_rows(int64_t rows, int64_t cols, int elem, const float *v,
+                       uint8_t *q, uint8_t *s)
+{
+    int64_t nb = cols / 32;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *vb = v + r * cols + b * 32;
+            float amax = 0.0f;
+            int i, x;
+            for (i = 0; i < 32; ++i)
+                if (fabsf(vb[i]) > amax)
+                    amax = fabsf(vb[i]);
+            x = orc_mx_exponent(amax, elem);
+            s[r * nb + b] = (uint8_t)(x + 127);
+            for (i = 0; i < 32; ++i) {
+                double u = ldexp((double)vb[i], -x);
+                q[r * cols + b * 32 + i] =
+                    elem == ORC_MX_E2M1 ? e2m1_encode_d(u) : e4m3_encode_d(u);
+            }
+        }
+}
+
+/* Decoded value of one MX element: code value times 2^(scale byte - 127). */
+double orc_mx_value(int elem, uint8_t code, uint8_t scale)
+{
+    double c = elem == ORC_MX_E2M1 ? orc_e2m1_decode(code) : orc_e4m3_decode(code);
+    return ldexp(c, (int)scale - 127);
 }
 
 /* Round an fp64 value to the nearest bfloat16 value (ties to even), returned
@@ -188,6 +280,18 @@ void orc_e4m3_decode_array(int64_t n, const uint8_t *q, double *v)
 {
     for (int64_t i = 0; i < n; ++i)
         v[i] = orc_e4m3_decode(q[i]);
+}
+
+void orc_e2m1_encode_array(int64_t n, const float *v, uint8_t *q)
+{
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = orc_e2m1_encode(v[i]);
+}
+
+void orc_e2m1_decode_array(int64_t n, const uint8_t *q, double *v)
+{
+    for (int64_t i = 0; i < n; ++i)
+        v[i] = orc_e2m1_decode(q[i]);
 }
 
 void orc_round_bf16_array(int64_t n, const double *in, double *out)
@@ -314,16 +418,34 @@ static void init_e4m3_values(void)
     }
 }
 
-/* Value of weight element (r, c) of one expert's [R x C] matrix. */
-static double load_w(const orc_problem *p, const void *W, const float *Ws,
+/* Value of weight element (r, c) of one expert's [R x C] matrix.  FP8:
+ * Ws = fp32 [R/128 x C/128] block scales; MXFP4: W holds one E2M1 code per
+ * byte and Ws = E8M0 bytes [R/32 x C] (blocks of 32 along the contraction
+ * axis r). */
+static double load_w(const orc_problem *p, const void *W, const void *Ws,
                      int64_t C, int64_t r, int64_t c)
 {
     if (p->w_dtype == ORC_FP8) {
         int64_t ncb = (C + 127) / 128;
         return e4m3_value[((const uint8_t *)W)[r * C + c]] *
-               (double)Ws[(r / 128) * ncb + c / 128];
+               (double)((const float *)Ws)[(r / 128) * ncb + c / 128];
     }
+    if (p->w_dtype == ORC_MXFP4)
+        return orc_mx_value(ORC_MX_E2M1, ((const uint8_t *)W)[r * C + c],
+                            ((const uint8_t *)Ws)[(r / 32) * C + c]);
     return (double)load_f(W, p->w_dtype, r * C + c);
+}
+
+/* MX FP8 round trip of n fp32 values (n a multiple of 32), into fp64. */
+static void mx_fp8_roundtrip(int64_t n, const float *v, double *out)
+{
+    uint8_t *q = (uint8_t *)malloc((size_t)n);
+    uint8_t *s = (uint8_t *)malloc((size_t)(n / 32));
+    orc_mx_quant_rows(1, n, ORC_MX_E4M3, v, q, s);
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_mx_value(ORC_MX_E4M3, q[i], s[i / 32]);
+    free(q);
+    free(s);
 }
 
 /* Activation row of token t as the experts consume it (fp64).  For FP8 layers
@@ -344,6 +466,12 @@ static void expert_input_row(const orc_problem *p, const void *x, int64_t t,
         free(v);
         free(q);
         free(s);
+    } else if (p->w_dtype == ORC_MXFP4) {
+        float *v = (float *)malloc(sizeof(float) * (size_t)p->d);
+        for (i = 0; i < p->d; ++i)
+            v[i] = load_f(x, p->act_dtype, t * p->d + i);
+        mx_fp8_roundtrip(p->d, v, row);
+        free(v);
     } else {
         for (i = 0; i < p->d; ++i)
             row[i] = (double)load_f(x, p->act_dtype, t * p->d + i);
@@ -367,6 +495,12 @@ static void mirror_h(const orc_problem *p, double *h)
         free(v);
         free(q);
         free(s);
+    } else if (p->w_dtype == ORC_MXFP4) {
+        float *v = (float *)malloc(sizeof(float) * (size_t)p->f);
+        for (n = 0; n < p->f; ++n)
+            v[n] = (float)h[n];
+        mx_fp8_roundtrip(p->f, v, h);
+        free(v);
     } else if (p->act_dtype == ORC_BF16) {
         for (n = 0; n < p->f; ++n)
             h[n] = orc_round_bf16(h[n]);
@@ -377,13 +511,14 @@ static void mirror_h(const orc_problem *p, double *h)
 }
 
 #define ORC_BLOCK 8 /* slots of one expert evaluated together */
+#define SCALED(p) ((p)->w_dtype == ORC_FP8 || (p)->w_dtype == ORC_MXFP4)
 
 /* Expert FFN for up to ORC_BLOCK activation rows of one expert.
  * rows: [nr x d]; y: [nr x d].  Each output element is an fp64 sum over the
  * contraction index ascending. */
 static void expert_ffn(const orc_problem *p, int nr, const double *rows,
                        const void *W1, const void *W3, const void *W2,
-                       const float *W1s, const float *W3s, const float *W2s,
+                       const void *W1s, const void *W3s, const void *W2s,
                        double *y)
 {
     int64_t d = p->d, f = p->f, i, n, m;
@@ -420,9 +555,11 @@ static void expert_ffn(const orc_problem *p, int nr, const double *rows,
  *
  * W1[e], W3[e]: [d x f]; W2[e]: [f x d], one pointer per expert (an expert no
  * listed token routes to may be NULL); entries E .. E + n_shared - 1 are the
- * shared experts (never NULL when n_shared > 0).  For FP8 weights W1s/W3s/W2s[e] point
- * to the [K/128 x N/128] fp32 block scales of that expert's [K x N] matrix;
- * otherwise they are NULL.  x is the full [T x d] activation matrix, gate_w is
+ * shared experts (never NULL when n_shared > 0).  For FP8 weights
+ * W1s/W3s/W2s[e] point to the [K/128 x N/128] fp32 block scales of that
+ * expert's [K x N] matrix; for MXFP4 weights W holds one E2M1 code per byte
+ * and W1s/W3s/W2s[e] the [K/32 x N] E8M0 scale bytes; otherwise they are
+ * NULL.  x is the full [T x d] activation matrix, gate_w is
  * [d x E], bias is [E] or NULL.
  *
  * out:   [ntok x d] fp64, the unrounded combine of each listed token.
@@ -432,8 +569,8 @@ static void expert_ffn(const orc_problem *p, int nr, const double *rows,
 int orc_forward(const orc_problem *p, const void *x, const void *gate_w,
                 const float *bias, const void *const *W1,
                 const void *const *W3, const void *const *W2,
-                const float *const *W1s, const float *const *W3s,
-                const float *const *W2s, const int64_t *tokens, int64_t ntok,
+                const void *const *W1s, const void *const *W3s,
+                const void *const *W2s, const int64_t *tokens, int64_t ntok,
                 double *out, int32_t *ids_out, float *w_out)
 {
     int64_t d = p->d, k = p->k, npair = ntok * k, it;
@@ -450,7 +587,7 @@ int orc_forward(const orc_problem *p, const void *x, const void *gate_w,
     for (int s = 0; s < p->n_shared && !bad; ++s) {
         int e = p->E + s;
         if (!W1[e] || !W3[e] || !W2[e] ||
-            (p->w_dtype == ORC_FP8 && (!W1s[e] || !W3s[e] || !W2s[e])))
+            (SCALED(p) && (!W1s[e] || !W3s[e] || !W2s[e])))
             bad = 1;
     }
 
@@ -479,7 +616,7 @@ int orc_forward(const orc_problem *p, const void *x, const void *gate_w,
         free(fill);
         for (int e = 0; e < p->E; ++e)
             if (start[e + 1] > start[e] && (!W1[e] || !W3[e] || !W2[e] ||
-                (p->w_dtype == ORC_FP8 && (!W1s[e] || !W3s[e] || !W2s[e]))))
+                (SCALED(p) && (!W1s[e] || !W3s[e] || !W2s[e]))))
                 bad = 1;
     }
     if (bad) {
@@ -506,9 +643,8 @@ int orc_forward(const orc_problem *p, const void *x, const void *gate_w,
         for (r = 0; r < nr; ++r)
             expert_input_row(p, x, tokens[order[item_beg[wi] + r] / k], rows + r * d);
         expert_ffn(p, nr, rows, W1[e], W3[e], W2[e],
-                   p->w_dtype == ORC_FP8 ? W1s[e] : NULL,
-                   p->w_dtype == ORC_FP8 ? W3s[e] : NULL,
-                   p->w_dtype == ORC_FP8 ? W2s[e] : NULL, yb);
+                   SCALED(p) ? W1s[e] : NULL, SCALED(p) ? W3s[e] : NULL,
+                   SCALED(p) ? W2s[e] : NULL, yb);
         for (r = 0; r < nr; ++r)
             memcpy(y + order[item_beg[wi] + r] * d, yb + r * d, sizeof(double) * (size_t)d);
         free(rows);
@@ -529,9 +665,8 @@ int orc_forward(const orc_problem *p, const void *x, const void *gate_w,
             for (r = 0; r < nr; ++r)
                 expert_input_row(p, x, tokens[t0 + r], rows + r * d);
             expert_ffn(p, nr, rows, W1[e], W3[e], W2[e],
-                       p->w_dtype == ORC_FP8 ? W1s[e] : NULL,
-                       p->w_dtype == ORC_FP8 ? W3s[e] : NULL,
-                       p->w_dtype == ORC_FP8 ? W2s[e] : NULL,
+                       SCALED(p) ? W1s[e] : NULL, SCALED(p) ? W3s[e] : NULL,
+                       SCALED(p) ? W2s[e] : NULL,
                        ys + ((int64_t)(e - p->E) * ntok + t0) * d);
             free(rows);
         }

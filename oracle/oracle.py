@@ -1,8 +1,9 @@
 """ctypes binding of liboracle.so (oracle.c) -- TEST INFRASTRUCTURE ONLY.
 
 Arrays are numpy arrays in host memory.  bf16 data is passed as its raw
-``uint16`` bit patterns, FP8 E4M3FN data as ``uint8`` codes, so the oracle
-reads exactly the bits the GPU reads.
+``uint16`` bit patterns, FP8 E4M3FN data as ``uint8`` codes, MX FP4 (E2M1)
+data as one ``uint8`` code per element and MX scales as ``uint8`` E8M0 bytes,
+so the oracle reads exactly the bits the GPU reads.
 """
 from __future__ import annotations
 
@@ -12,7 +13,8 @@ import subprocess
 
 import numpy as np
 
-ORC_F32, ORC_BF16, ORC_FP8 = 0, 1, 2
+ORC_F32, ORC_BF16, ORC_FP8, ORC_MXFP4 = 0, 1, 2, 3
+MX_E4M3, MX_E2M1 = 0, 1  # element formats of MX blocks
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -63,6 +65,11 @@ def _load():
     lib.orc_e4m3_encode_array.argtypes = [i64, P, P]
     lib.orc_e4m3_decode_array.argtypes = [i64, P, P]
     lib.orc_round_bf16_array.argtypes = [i64, P, P]
+    lib.orc_e2m1_encode_array.argtypes = [i64, P, P]
+    lib.orc_e2m1_decode_array.argtypes = [i64, P, P]
+    lib.orc_mx_exponent.argtypes = [ctypes.c_float, ctypes.c_int]
+    lib.orc_mx_exponent.restype = ctypes.c_int
+    lib.orc_mx_quant_rows.argtypes = [i64, i64, ctypes.c_int, P, P, P]
     _lib = lib
     return lib
 
@@ -138,7 +145,8 @@ def forward(x, gate_w, bias, W1, W3, W2, k, act_dtype, w_dtype, tokens=None,
     be None for an expert none of the listed tokens routes to.  Shared
     experts see every token and are added with weight 1.
     For FP8 weights (uint8 codes) W1s/W3s/W2s hold each expert's fp32
-    [K/128 x N/128] block scales.
+    [K/128 x N/128] block scales; for MXFP4 weights (one uint8 E2M1 code per
+    element) they hold each expert's [K/32 x N] uint8 E8M0 scales.
     Returns (out fp64 [ntok x d] unrounded, ids [ntok x k], w [ntok x k]).
     """
     lib = _load()
@@ -147,7 +155,8 @@ def forward(x, gate_w, bias, W1, W3, W2, k, act_dtype, w_dtype, tokens=None,
     T, d = x.shape
     E = gate_w.shape[1]
     f = None
-    wdt = {ORC_F32: np.float32, ORC_BF16: np.uint16, ORC_FP8: np.uint8}[w_dtype]
+    wdt = {ORC_F32: np.float32, ORC_BF16: np.uint16, ORC_FP8: np.uint8,
+           ORC_MXFP4: np.uint8}[w_dtype]
     keep = []
 
     ne = E + n_shared
@@ -169,9 +178,10 @@ def forward(x, gate_w, bias, W1, W3, W2, k, act_dtype, w_dtype, tokens=None,
     if f is None:
         raise ValueError("no expert weights given")
     p1, p3, p2 = plist(W1, wdt), plist(W3, wdt), plist(W2, wdt)
-    s1 = plist(W1s, np.float32) if w_dtype == ORC_FP8 else None
-    s3 = plist(W3s, np.float32) if w_dtype == ORC_FP8 else None
-    s2 = plist(W2s, np.float32) if w_dtype == ORC_FP8 else None
+    sdt = {ORC_FP8: np.float32, ORC_MXFP4: np.uint8}.get(w_dtype)
+    s1 = plist(W1s, sdt) if sdt else None
+    s3 = plist(W3s, sdt) if sdt else None
+    s2 = plist(W2s, sdt) if sdt else None
     if tokens is None:
         tokens = np.arange(T, dtype=np.int64)
     tokens = _c(np.asarray(tokens, dtype=np.int64), np.int64)
@@ -224,3 +234,38 @@ def round_bf16(v):
     out = np.empty(v.shape, np.float64)
     lib.orc_round_bf16_array(v.size, _ptr(v), _ptr(out))
     return out
+
+
+def e2m1_encode(v):
+    lib = _load()
+    v = _c(np.asarray(v, np.float32).ravel(), np.float32)
+    q = np.empty(v.shape, np.uint8)
+    lib.orc_e2m1_encode_array(v.size, _ptr(v), _ptr(q))
+    return q
+
+
+def e2m1_decode(q):
+    lib = _load()
+    q = _c(np.asarray(q, np.uint8).ravel(), np.uint8)
+    v = np.empty(q.shape, np.float64)
+    lib.orc_e2m1_decode_array(q.size, _ptr(q), _ptr(v))
+    return v
+
+
+def mx_exponent(amax, elem):
+    return _load().orc_mx_exponent(float(amax), elem)
+
+
+def mx_quant_rows(v, elem):
+    """MX quantisation of an fp32 [rows x cols] matrix along its rows, blocks
+    of 32.  Returns (codes uint8 [rows x cols], E8M0 scales uint8
+    [rows x cols/32])."""
+    lib = _load()
+    v = _c(v, np.float32)
+    rows, cols = v.shape
+    if cols % 32:
+        raise ValueError("MX rows need a multiple of 32 columns")
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 32), np.uint8)
+    lib.orc_mx_quant_rows(rows, cols, elem, _ptr(v), _ptr(q), _ptr(s))
+    return q, s
