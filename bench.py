@@ -24,7 +24,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {0: 157.3, 1: 2516.6, 2: 5033.2}  # dense MFMA: fp32, bf16, fp8
+# dense MFMA peaks: fp32, bf16, fp8; FP4 weights x FP8 activations run at the
+# fp8 rate (the scaled MFMA with one FP8 operand), so MXFP4 layers use it too
+PEAK_TFLOPS = {0: 157.3, 1: 2516.6, 2: 5033.2, 3: 5033.2}
 PEAK_HBM_GBPS = 8000.0
 STAGES = ["gate", "quant_x", "permute", "gemm_w13_swiglu", "gemm_w2", "combine"]
 
@@ -145,9 +147,11 @@ def _stage_work(cfg, counts):
     (weights of the experts that receive a token, activations in, outputs).
     Shared experts count as experts hit by every token: T more rows each."""
     import numpy as np
-    es = {0: 4, 1: 2, 2: 1}[cfg.w_dtype]
-    ae = {0: 4, 1: 2}[cfg.act_dtype] if cfg.w_dtype != 2 else 1
-    he = {0: 4, 1: 2, 2: 1}[cfg.w_dtype]
+    # bytes per weight / activation / h element; MXFP4: half-byte codes and
+    # MX FP8 activations, each with one E8M0 byte per 32 elements
+    es = {0: 4, 1: 2, 2: 1, 3: 0.5 + 1 / 32}[cfg.w_dtype]
+    ae = {0: 4, 1: 2}[cfg.act_dtype] if cfg.w_dtype < 2 else (1 if cfg.w_dtype == 2 else 1 + 1 / 32)
+    he = {0: 4, 1: 2, 2: 1, 3: 1 + 1 / 32}[cfg.w_dtype]
     hit = int(np.count_nonzero(counts)) + cfg.n_shared
     n = cfg.T * (cfg.k + cfg.n_shared)
     w13 = dict(flops=4.0 * n * cfg.d * cfg.f,
@@ -163,9 +167,9 @@ def _cpu_baseline(cfg, inp, out_gpu, target_s):
     import torch
 
     import oracle
-    from mixture_experts_layer_softmax_amd.inputs import host_arrays
+    from mixture_experts_layer_softmax_amd.inputs import host_arrays, host_weight
 
-    orc = {0: oracle.ORC_F32, 1: oracle.ORC_BF16, 2: oracle.ORC_FP8}
+    orc = {0: oracle.ORC_F32, 1: oracle.ORC_BF16, 2: oracle.ORC_FP8, 3: oracle.ORC_MXFP4}
     gw = host_arrays(inp["gate_w"])
     bias = None if inp.get("bias") is None else inp["bias"].cpu().numpy()
     host_w = {}
@@ -176,19 +180,18 @@ def _cpu_baseline(cfg, inp, out_gpu, target_s):
         need = set(int(v) for v in ids.reshape(-1)) | set(range(cfg.E, cfg.E + cfg.n_shared))
         for e in sorted(need):
             if e not in host_w:
-                host_w[e] = {n: host_arrays(inp[n][e]) for n in ("W1", "W3", "W2")}
-                if cfg.w_dtype == 2:
-                    host_w[e].update({n + "s": inp[n + "s"][e].cpu().numpy()
-                                      for n in ("W1", "W3", "W2")})
+                host_w[e] = {}
+                for n in ("W1", "W3", "W2"):
+                    host_w[e][n], host_w[e][n + "s"] = host_weight(cfg, inp, n, e)
         W = {n: [host_w.get(e, {}).get(n) for e in range(cfg.E + cfg.n_shared)]
              for n in ("W1", "W3", "W2", "W1s", "W3s", "W2s")}
-        fp8 = cfg.w_dtype == 2
+        sc = cfg.w_dtype in (2, 3)
         t0 = time.perf_counter()
         out, _, _ = oracle.forward(x, gw, bias, W["W1"], W["W3"], W["W2"], cfg.k,
                                    orc[cfg.act_dtype], orc[cfg.w_dtype],
-                                   W1s=W["W1s"] if fp8 else None,
-                                   W3s=W["W3s"] if fp8 else None,
-                                   W2s=W["W2s"] if fp8 else None, n_shared=cfg.n_shared)
+                                   W1s=W["W1s"] if sc else None,
+                                   W3s=W["W3s"] if sc else None,
+                                   W2s=W["W2s"] if sc else None, n_shared=cfg.n_shared)
         return out, time.perf_counter() - t0
 
     rng = np.random.default_rng(0)
@@ -317,7 +320,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu, parity = _cpu_baseline(cfg, inp, out, args.cpu_seconds)
 
-    dtype = {0: "f32", 1: "bf16", 2: "fp8e4m3"}[cfg.w_dtype]
+    dtype = {0: "f32", 1: "bf16", 2: "fp8e4m3", 3: "mxfp4xmxfp8"}[cfg.w_dtype]
     line = {
         "metric": "MoE-layer tokens/s on 1 MI355X; MFMA % peak (prefill), HBM GB/s (decode)",
         "value": value,

@@ -67,15 +67,22 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,
     MOE_BF16 = 1,
-    MOE_FP8_E4M3 = 2
+    MOE_FP8_E4M3 = 2,
+    MOE_MXFP4 = 3   /* OCP MX FP4: E2M1 codes, E8M0 scale per 32 along K */
 } moe_dtype;
 
 /* Problem description.  Sizes: T tokens, hidden d, expert intermediate f,
  * E experts, top_k experts per token (1 <= top_k <= E <= 1024).
  *   act_dtype: x and gate_w -- MOE_F32 or MOE_BF16.
  *   w_dtype:   W1, W3, W2   -- MOE_F32 (needs act_dtype F32), MOE_BF16 (needs
- *              act_dtype BF16) or MOE_FP8_E4M3 (needs act_dtype BF16, d and f
- *              multiples of 128).
+ *              act_dtype BF16), MOE_FP8_E4M3 (needs act_dtype BF16, d and f
+ *              multiples of 128) or MOE_MXFP4 (needs act_dtype BF16, d and f
+ *              multiples of 128): the FP8 x FP4 expert variant of the
+ *              MegaMoE-vs-MoE-systems page (sections 1 and 4) in OCP MX form
+ *              -- FP4 E2M1 weights with one E8M0 power-of-two scale per 32
+ *              consecutive contraction elements, x and h quantised to MX FP8
+ *              (E4M3, one E8M0 scale per 32) inside the layer, and the block
+ *              scales applied by the scaled MFMA itself.
  *   out_dtype: MOE_F32 or MOE_BF16.
  *   block_m:   rows per expert tile of the grouped GEMMs; 0 picks it from the
  *              expected tokens per expert T*top_k/E (the serving-regime choice
@@ -87,7 +94,7 @@ typedef enum {
  *            output is added with weight 1 after the gate-weighted routed
  *            sum; its weights follow the E routed experts' in W1/W3/W2 (and
  *            their FP8 scales), which then hold E + n_shared experts.
- * d and f must be multiples of 32 (fp32 weights), 64 (bf16) or 128 (FP8), and
+ * d and f must be multiples of 32 (fp32 weights), 64 (bf16) or 128 (FP8, MXFP4), and
  * x, h and one expert's weight matrix must each span less than 2^31 bytes
  * (MOE_ERR_UNSUPPORTED otherwise). */
 typedef struct {
@@ -176,15 +183,25 @@ moe_status moe_permute(const moe_problem *p, const int32_t *topk_ids,
 moe_status moe_quantize_fp8(int64_t rows, int64_t cols, const void *x_bf16,
                             uint8_t *q, float *s, hipStream_t stream);
 
+/* OCP MX FP8 quantisation of a bf16 [rows][cols] matrix (cols % 32 == 0), as
+ * the MXFP4 layer applies it to x: per block of 32 consecutive elements of a
+ * row, X = floor(log2(amax)) - 8 (clamped to >= -127; 0 for an all-zero
+ * block), s = X + 127 (E8M0 byte) and q = E4M3FN(v * 2^-X), round to nearest
+ * even, saturating at 448.  q [rows][cols] codes, s [rows][cols/32] bytes. */
+moe_status moe_quantize_mx(int64_t rows, int64_t cols, const void *x_bf16,
+                           uint8_t *q, uint8_t *s, hipStream_t stream);
+
 /* Bytes of each expert-weight tensor in the layout moe_forward reads
- * (element size of w_dtype times (E + n_shared)*d*f). */
+ * (element size of w_dtype times (E + n_shared)*d*f; MXFP4: half a byte per
+ * element, the E8M0 scales, (E + n_shared)*d*f/32 bytes, not included). */
 moe_status moe_weight_bytes(const moe_problem *p, size_t *bytes);
 
 /* One-time weight re-layout (untimed, done when weights are loaded): each
  * expert matrix given as [K][N] (W1, W3: [d][f]; W2: [f][d], the stated
  * layouts) is written as its transpose [N][K], so that the contraction axis
  * is contiguous for the MFMA operand loads.  src and dst must not overlap.
- * elem_bytes is 4 (fp32), 2 (bf16) or 1 (FP8 codes); E matrices of K x N. */
+ * elem_bytes is 4 (fp32), 2 (bf16) or 1 (FP8 codes); E matrices of K x N.
+ * MXFP4 weights are given already K-major and need no packing. */
 moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
                            const void *src, void *dst, hipStream_t stream);
 
@@ -194,19 +211,24 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
  *   bias    [E]          fp32 or NULL
  *   W1t,W3t [E+S][f][d]  w_dtype, packed by moe_pack_weight (gate, up)
  *   W2t     [E+S][d][f]  w_dtype, packed by moe_pack_weight (down)
- *   W1s,W3s [E+S][d/128][f/128] fp32 block scales (FP8 only, else NULL)
- *   W2s     [E+S][f/128][d/128] fp32 block scales (FP8 only, else NULL)
+ *           (MXFP4: the same [N][K] shapes with two E2M1 codes per byte,
+ *           element 2i in the low nibble of byte i -- K-major as given)
+ *   W1s,W3s FP8: [E+S][d/128][f/128] fp32 block scales;
+ *           MXFP4: [E+S][f][d/32] E8M0 bytes (one per 32 elements along K);
+ *           NULL otherwise
+ *   W2s     FP8: [E+S][f/128][d/128] fp32; MXFP4: [E+S][d][f/32] E8M0 bytes
  *           (S = n_shared: the shared experts follow the routed ones)
  *   out     [T][d]       out_dtype
  *   ws/ws_bytes          workspace of at least moe_workspace_size()
  *   dbg                  NULL, or device buffers receiving the routing used.
- * Kernels enqueued: route (logits, top-k), FP8 quantisation of x (FP8 only),
+ * Kernels enqueued: route (logits, top-k), FP8 / MX FP8 quantisation of x
+ * (FP8 and MXFP4 layers),
  * histogram, scan + tile map, scatter, grouped W1/W3 GEMM + SwiGLU, grouped
  * W2 GEMM, combine. */
 moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
                        const float *bias, const void *W1t, const void *W3t,
-                       const void *W2t, const float *W1s, const float *W3s,
-                       const float *W2s, void *out, void *ws, size_t ws_bytes,
+                       const void *W2t, const void *W1s, const void *W3s,
+                       const void *W2s, void *out, void *ws, size_t ws_bytes,
                        const moe_debug *dbg, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -15,13 +15,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 
 EXPORTS = ["moe_status_string", "moe_last_hip_error", "moe_workspace_size", "moe_route",
-           "moe_permute", "moe_quantize_fp8", "moe_weight_bytes", "moe_pack_weight",
-           "moe_forward"]
+           "moe_permute", "moe_quantize_fp8", "moe_quantize_mx", "moe_weight_bytes",
+           "moe_pack_weight", "moe_forward"]
 
 
 class MoEProblem(ctypes.Structure):
@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH):
     lib.moe_route.argtypes = [PP, P, P, P, P, P, P, P, S, P]
     lib.moe_permute.argtypes = [PP, P, P, P, P, P, P, P, S, P]
     lib.moe_quantize_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, P, P, P, P]
+    lib.moe_quantize_mx.argtypes = [ctypes.c_int64, ctypes.c_int64, P, P, P, P]
     lib.moe_pack_weight.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int32, P, P, P]
     lib.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, S,
@@ -152,6 +153,12 @@ def moe_quantize_fp8(x_bf16, q, s, stream=None):
     _check("moe_quantize_fp8", rc)
 
 
+def moe_quantize_mx(x_bf16, q, s, stream=None):
+    rows, cols = x_bf16.shape
+    rc = load().moe_quantize_mx(rows, cols, _p(x_bf16), _p(q), _p(s), _stream(stream))
+    _check("moe_quantize_mx", rc)
+
+
 def moe_pack_weight(src, dst, stream=None):
     """src [E][K][N] -> dst [E][N][K] (any 1/2/4-byte element type)."""
     E, K, N = src.shape
@@ -181,8 +188,12 @@ def moe_forward(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, dbg=N
 # ---------------------------------------------------------------------------
 
 def pack_weights(inp: dict, stream=None) -> dict:
-    """One-time re-layout of W1/W3/W2 ([E][K][N] -> [E][N][K]) on the GPU."""
+    """One-time re-layout of W1/W3/W2 ([E][K][N] -> [E][N][K]) on the GPU.
+    MXFP4 weights (uint8 E8M0 scales) come K-major already and pass through."""
     out = {}
+    if inp.get("W1s") is not None and inp["W1s"].dtype == torch.uint8:
+        return {"W1t": inp["W1"], "W3t": inp["W3"], "W2t": inp["W2"],
+                "W1s": inp["W1s"], "W3s": inp["W3s"], "W2s": inp["W2s"]}
     for name in ("W1", "W3", "W2"):
         w = inp[name]
         E, K, N = w.shape

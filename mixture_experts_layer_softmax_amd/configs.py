@@ -1,4 +1,4 @@
-"""The five MoE-layer workloads this library is measured and checked on.
+"""The MoE-layer workloads this library is measured and checked on.
 
 Each is a single-GPU layer forward.  Names say what the workload is; sizes are
 tokens T, hidden d, expert intermediate f, experts E and top-k.
@@ -7,7 +7,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-F32, BF16, FP8 = 0, 1, 2  # same codes as moe_dtype in include/moe.h
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3  # same codes as moe_dtype in include/moe.h
 
 
 @dataclass(frozen=True)
@@ -56,6 +56,10 @@ CONFIGS = {
     # (the shared-expert phases of the MegaMoE-vs-MoE-systems page, section 2.7)
     "prefill_bf16_shared": MoEConfig("prefill_bf16_shared", 16384, 2048, 2048, 32, 2, BF16,
                                      BF16, BF16, n_shared=1),
+    # the FP8 x FP4 expert variant (MX FP4 weights, MX FP8 activations) at
+    # the FP8 prefill and the decode shapes
+    "prefill_mxfp4": MoEConfig("prefill_mxfp4", 32768, 7168, 2048, 256, 8, BF16, MXFP4, BF16),
+    "decode_mxfp4": MoEConfig("decode_mxfp4", 64, 7168, 2048, 256, 8, BF16, MXFP4, BF16),
 }
 
 ORDER = ["tiny_fp32", "prefill_bf16", "decode_bf16", "skewed_bf16", "prefill_fp8"]

@@ -24,6 +24,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int esize(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
 
+// Bytes of a [rows x cols] expert-weight matrix in w_dtype (FP4: two per byte).
+int64_t weight_matrix_bytes(int dt, int64_t rows, int64_t cols) {
+  return dt == MOE_MXFP4 ? rows * cols / 2 : rows * cols * esize(dt);
+}
+
+bool quantised_weights(int dt) { return dt == MOE_FP8_E4M3 || dt == MOE_MXFP4; }
+
 // Tile height from the expected rows per expert, T*k/E: the serving-regime
 // choice of the MegaMoE-vs-MoE-systems page (section 2.5), re-tuned for
 // 16-row MFMA fragments and four 64-wide waves per workgroup.
@@ -59,7 +66,8 @@ bool valid_problem(const moe_problem* p) {
   if (p->T > (1ll << 31) / 1024 || p->T * (p->top_k + p->n_shared) > (1ll << 30)) return false;
   const bool ok_types = (p->act_dtype == MOE_F32 && p->w_dtype == MOE_F32) ||
                         (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_BF16) ||
-                        (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_FP8_E4M3);
+                        (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_FP8_E4M3) ||
+                        (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_MXFP4);
   if (!ok_types) return false;
   if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return false;
   if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
@@ -78,9 +86,11 @@ int64_t gemm_rows(const moe_problem& p) { return p.T * (p.top_k + p.n_shared); }
 bool supported_shape(const moe_problem* p) {
   const int64_t m = p->w_dtype == MOE_F32 ? 32 : (p->w_dtype == MOE_BF16 ? 64 : 128);
   if (p->d % m != 0 || p->f % m != 0) return false;
+  // activation element bytes of the GEMM operands (FP8 and MX FP8: 1)
   const int64_t es = p->w_dtype == MOE_F32 ? 4 : (p->w_dtype == MOE_BF16 ? 2 : 1);
   const int64_t lim = 1ll << 31;
-  return p->T * p->d * es < lim && gemm_rows(*p) * p->f * es < lim && p->d * p->f * es < lim;
+  return p->T * p->d * es < lim && gemm_rows(*p) * p->f * es < lim &&
+         weight_matrix_bytes(p->w_dtype, p->d, p->f) < lim;
 }
 
 struct Layout {
@@ -119,11 +129,12 @@ Layout make_layout(const moe_problem& p) {
   L.tm_row0 = take(sizeof(int32_t) * L.max_mtiles);
   L.tm_rows = take(sizeof(int32_t) * L.max_mtiles);
   L.tm_misc = take(sizeof(int32_t) * (1 + moe::kQueueWords));
-  const bool fp8 = p.w_dtype == MOE_FP8_E4M3;
-  L.xq = take(fp8 ? static_cast<size_t>(p.T) * p.d : 0);
-  L.sx = take(fp8 ? sizeof(float) * p.T * (p.d / 128) : 0);
-  L.hs = take(fp8 ? sizeof(float) * rows * (p.f / 128) : 0);
-  L.h = take(static_cast<size_t>(rows) * p.f * esize(p.w_dtype == MOE_FP8_E4M3 ? MOE_FP8_E4M3 : p.act_dtype));
+  const bool fp8 = p.w_dtype == MOE_FP8_E4M3, mx = p.w_dtype == MOE_MXFP4;
+  // FP8: fp32 scales per 128 elements; MX: one E8M0 byte per 32 elements
+  L.xq = take(fp8 || mx ? static_cast<size_t>(p.T) * p.d : 0);
+  L.sx = take(fp8 ? sizeof(float) * p.T * (p.d / 128) : (mx ? p.T * (p.d / 32) : 0));
+  L.hs = take(fp8 ? sizeof(float) * rows * (p.f / 128) : (mx ? rows * (p.f / 32) : 0));
+  L.h = take(static_cast<size_t>(rows) * p.f * (fp8 || mx ? 1 : esize(p.act_dtype)));
   L.y = take(sizeof(float) * rows * p.d);
   L.total = off;
   return L;
@@ -186,7 +197,7 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
 
 moe_status moe_weight_bytes(const moe_problem* p, size_t* bytes) {
   if (!valid_problem(p) || !bytes) return MOE_ERR_INVALID_ARG;
-  *bytes = static_cast<size_t>(p->E + p->n_shared) * p->d * p->f * esize(p->w_dtype);
+  *bytes = static_cast<size_t>((p->E + p->n_shared) * weight_matrix_bytes(p->w_dtype, p->d, p->f));
   return MOE_OK;
 }
 
@@ -236,6 +247,16 @@ moe_status moe_quantize_fp8(int64_t rows, int64_t cols, const void* x_bf16, uint
   return hip_status();
 }
 
+moe_status moe_quantize_mx(int64_t rows, int64_t cols, const void* x_bf16, uint8_t* q,
+                           uint8_t* s, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x_bf16 || !q || !s) return MOE_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  moe::launch_quant_mx(static_cast<const uint16_t*>(x_bf16), rows, cols, q, s, stream);
+  return hip_status();
+}
+
 moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes, const void* src,
                            void* dst, hipStream_t stream) {
   if (E < 1 || K < 1 || N < 1 || !src || !dst) return MOE_ERR_INVALID_ARG;
@@ -250,15 +271,16 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes, 
 }
 
 moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, const float* bias,
-                       const void* W1t, const void* W3t, const void* W2t, const float* W1s,
-                       const float* W3s, const float* W2s, void* out, void* ws, size_t ws_bytes,
+                       const void* W1t, const void* W3t, const void* W2t, const void* W1s,
+                       const void* W3s, const void* W2s, void* out, void* ws, size_t ws_bytes,
                        const moe_debug* dbg, hipStream_t stream) {
   if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
   if (!supported_shape(p)) return MOE_ERR_UNSUPPORTED;
   if (p->T == 0) return MOE_OK;
   if (!x || !gate_w || !W1t || !W3t || !W2t || !out || !ws) return MOE_ERR_INVALID_ARG;
-  const bool fp8 = p->w_dtype == MOE_FP8_E4M3;
-  if (fp8 && (!W1s || !W3s || !W2s)) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = p->w_dtype == MOE_FP8_E4M3, mx = p->w_dtype == MOE_MXFP4;
+  const bool q8 = fp8 || mx;  // the GEMMs read 1-byte activation codes + scales
+  if (q8 && (!W1s || !W3s || !W2s)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(*p);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
@@ -274,7 +296,8 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   int32_t* slot_k = at<int32_t>(ws, L.slot_k);
   int32_t* token_slot = at<int32_t>(ws, L.token_slot);
   const moe::TileMap tm = tile_map(ws, L);
-  const int hdt = fp8 ? moe::kFP8 : (p->act_dtype == MOE_BF16 ? moe::kBF16 : moe::kF32);
+  const int hdt = fp8 ? moe::kFP8
+                      : (mx ? moe::kMX4 : (p->act_dtype == MOE_BF16 ? moe::kBF16 : moe::kF32));
   const int gdt = hdt;
 
   auto mark = [&](int i) {
@@ -286,10 +309,13 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   moe::launch_logits(x, gate_w, bias, logits, T, d, E, p->act_dtype == MOE_BF16, stream);
   moe::launch_topk(logits, ids, w, T, E, k, stream);
   mark(1);
-  // 2. FP8 activations
+  // 2. FP8 (or MX FP8) activations
   if (fp8)
     moe::launch_quant_fp8(static_cast<const uint16_t*>(x), p->T, p->d, at<uint8_t>(ws, L.xq),
                           at<float>(ws, L.sx), stream);
+  if (mx)
+    moe::launch_quant_mx(static_cast<const uint16_t*>(x), p->T, p->d, at<uint8_t>(ws, L.xq),
+                         at<uint8_t>(ws, L.sx), stream);
   mark(2);
   // 3. histogram, scan + tile map, scatter
   moe::launch_permute(ids, T, k, E, p->n_shared, L.bm, at<int32_t>(ws, L.table), counts,
@@ -300,18 +326,18 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
 
   // 4. W1/W3 + SwiGLU
   moe::GemmArgs g1{};
-  g1.A = fp8 ? at<uint8_t>(ws, L.xq) : static_cast<const uint8_t*>(x);
-  g1.a_row_bytes = p->d * esize(fp8 ? MOE_FP8_E4M3 : p->act_dtype);
+  g1.A = q8 ? at<uint8_t>(ws, L.xq) : static_cast<const uint8_t*>(x);
+  g1.a_row_bytes = p->d * (q8 ? 1 : esize(p->act_dtype));
   g1.gather = slot_token;
-  g1.sa = fp8 ? at<float>(ws, L.sx) : nullptr;
+  g1.sa = q8 ? at<float>(ws, L.sx) : nullptr;  // (MX: E8M0 bytes)
   g1.B0 = static_cast<const uint8_t*>(W1t);
   g1.B1 = static_cast<const uint8_t*>(W3t);
-  g1.sb0 = W1s;
-  g1.sb1 = W3s;
+  g1.sb0 = static_cast<const float*>(W1s);
+  g1.sb1 = static_cast<const float*>(W3s);
   g1.K = p->d;
   g1.N = p->f;
   g1.C = at<uint8_t>(ws, L.h);
-  g1.sc = fp8 ? at<float>(ws, L.hs) : nullptr;
+  g1.sc = q8 ? at<float>(ws, L.hs) : nullptr;
   g1.tm = tm;
   g1.n_tiles_n = static_cast<int>(ceil_div(2 * p->f, moe::gemm_tile_n(1, gdt, L.bm)));
   g1.queue_idx = 0;
@@ -324,12 +350,12 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   // 5. W2
   moe::GemmArgs g2{};
   g2.A = at<uint8_t>(ws, L.h);
-  g2.a_row_bytes = p->f * esize(fp8 ? MOE_FP8_E4M3 : p->act_dtype);
+  g2.a_row_bytes = p->f * (q8 ? 1 : esize(p->act_dtype));
   g2.gather = nullptr;
-  g2.sa = fp8 ? at<float>(ws, L.hs) : nullptr;
+  g2.sa = q8 ? at<float>(ws, L.hs) : nullptr;
   g2.B0 = static_cast<const uint8_t*>(W2t);
   g2.B1 = nullptr;
-  g2.sb0 = W2s;
+  g2.sb0 = static_cast<const float*>(W2s);
   g2.sb1 = nullptr;
   g2.K = p->f;
   g2.N = p->d;

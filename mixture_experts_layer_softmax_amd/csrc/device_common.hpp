@@ -49,6 +49,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | code;
 }
 
+// Shared exponent X of an OCP MX block of E4M3 elements (scale 2^X, stored
+// as the E8M0 byte X + 127): floor(log2(amax)) - 8, clamped below at -127
+// (which also covers fp32 subnormal amax); 0 for an all-zero block.
+__device__ __forceinline__ int mx_exponent_e4m3(float amax) {
+  if (amax == 0.f) return 0;
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+  return max(-127, e - 127 - 8);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

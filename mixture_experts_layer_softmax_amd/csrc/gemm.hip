@@ -52,6 +52,8 @@ template <>
 struct ESize<kBF16> { static constexpr int v = 2; };
 template <>
 struct ESize<kFP8> { static constexpr int v = 1; };
+template <>
+struct ESize<kMX4> { static constexpr int v = 1; };  // activations: MX FP8 codes
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 
@@ -64,13 +66,22 @@ struct Geo {
   // contraction bytes per LDS row and stage: two 16x16x32 bf16 MFMA steps,
   // four 16x16x4 fp32 steps, or one 16x16x128 FP8 step.  128-byte rows keep
   // every DMA request a whole cache line and halve the barriers per MFMA.
+  // MX layers (FP4 weights): a stage spans KRB activation bytes = KRB
+  // contraction elements, which the FP4 weight rows hold in KRB/2 bytes.
+  static constexpr bool MX = DT == kMX4;
   static constexpr int KRB = KRB_;
-  static constexpr int ROWS_PER_DMA = 1024 / KRB;  // rows one wave-wide DMA load fills
-  static constexpr int ABLK = BM / ROWS_PER_DMA, BBLK = BN / ROWS_PER_DMA;
+  static constexpr int KRBW = MX ? KRB_ / 2 : KRB_;  // weight row bytes per stage
+  static constexpr int ROWS_PER_DMA = 1024 / KRB;    // activation rows one wave-wide DMA fills
+  static constexpr int ROWS_PER_DMAW = 1024 / KRBW;  // weight rows one wave-wide DMA fills
+  static constexpr int ABLK = BM / ROWS_PER_DMA, BBLK = BN / ROWS_PER_DMAW;
   static constexpr int AW = (ABLK + NW - 1) / NW, BW = (BBLK + NW - 1) / NW;
-  static constexpr int SA_DMA = (DT == kFP8) ? (BM + 63) / 64 : 0;  // A-scale dword DMAs
-  static constexpr int SCALE_BYTES = SA_DMA * 256;                    // per stage
-  static constexpr int STAGE = (BM + BN) * KRB + SCALE_BYTES;
+  // per-stage scale DMAs (one dword per row): FP8 A-row scales; MX A-row and
+  // weight-row E8M0 scale dwords (4 blocks of 32 elements each)
+  static constexpr int SA_DMA = (DT == kFP8 || MX) ? (BM + 63) / 64 : 0;
+  static constexpr int SB_DMA = MX ? (BN + 63) / 64 : 0;
+  static constexpr int SCW = (SA_DMA + SB_DMA + NW - 1) / NW;  // scale DMAs per wave (MX)
+  static constexpr int SCALE_BYTES = (SA_DMA + SB_DMA) * 256;  // per stage
+  static constexpr int STAGE = BM * KRB + BN * KRBW + SCALE_BYTES;
   static constexpr int RED = (DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0;
   static constexpr int NS0 = (kLdsBytes - RED) / STAGE;
   static constexpr int NS = NS0 > 6 ? 6 : NS0;
@@ -80,7 +91,7 @@ struct Geo {
   static constexpr int LDS = (RING > EPI ? RING : EPI) + RED;
   static_assert(NS >= 2, "at least two LDS stages");
   static_assert(LDS <= kLdsBytes, "LDS budget");
-  static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMA == 0, "whole DMA blocks");
+  static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMAW == 0, "whole DMA blocks");
 };
 
 // LDS byte offset of 16-byte chunk c of row r in a tile of KRB-byte rows.
@@ -190,12 +201,14 @@ template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   using G = Geo<DT, PHASE, BM, BN, WM, WN, KRB_>;
   constexpr int kThreads = G::kThreads, ES = G::ES, KRB = G::KRB, NS = G::NS;
-  constexpr int NW = G::NW, RPD = G::ROWS_PER_DMA;
+  constexpr int NW = G::NW, RPD = G::ROWS_PER_DMA, RPDW = G::ROWS_PER_DMAW, KRBW = G::KRBW;
+  constexpr bool MX = G::MX;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(PHASE == 2 || TN % 2 == 0, "gate/up pairs");
   static_assert(!(DT == kFP8 && PHASE == 1) || BN == 256, "FP8 h groups of 128 f");
+  static_assert(!(MX && PHASE == 1) || WTN % 64 == 0, "MX h blocks of 32 f inside one wave");
 
   // LDS: NS stages of [BM rows A | BN rows B | BM A-scales (FP8)], reused by
   // the epilogue staging; then (FP8 phase 1) the per-wave row maxima.
@@ -258,11 +271,14 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     // span less than 2^31 bytes).  A wave-wide DMA fills RPD rows of KRB
     // bytes; lane L fills row L / (KRB/16), physical chunk L % (KRB/16), so it
     // loads the logical chunk that the swizzle maps there. ----
-    const int64_t w_bytes = N * K * ES;
+    const int64_t w_row = MX ? K / 2 : K * ES;  // weight row bytes (FP4: two per byte)
+    const int64_t w_bytes = N * w_row;
     const uint8_t* b0 = g.B0 + static_cast<int64_t>(e) * w_bytes;
     const uint8_t* b1 = (PHASE == 1) ? g.B1 + static_cast<int64_t>(e) * w_bytes : b0;
-    constexpr int CPRK = KRB / 16;  // 16-byte chunks per LDS row
+    constexpr int CPRK = KRB / 16;    // 16-byte chunks per activation LDS row
+    constexpr int CPRKW = KRBW / 16;  // and per weight LDS row
     const int lrow = lane / CPRK, lphys = lane % CPRK;
+    const int lroww = lane / CPRKW, lphysw = lane % CPRKW;
     uint32_t oa[G::AW], ob[G::BW];
     uint32_t up_mask = 0;  // bit j: B block j of this wave comes from W3 (up)
     int my_loads = 0;      // DMA instructions this wave issues per stage
@@ -279,21 +295,21 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
     for (int j = 0; j < G::BW; ++j) {
       const int q = wave + NW * j;
-      const int r = q * RPD + lrow;
-      const int logical = lphys ^ swz_key<KRB>(r);
+      const int r = q * RPDW + lroww;
+      const int logical = lphysw ^ swz_key<KRBW>(r);
       const int64_t n = n0 + r;
       int64_t col;
       if (PHASE == 1) {  // combined rows: 16 gate rows, then 16 up rows, per f block
         // the RPD rows of one DMA lie in one 16-row block (RPD divides 16 and
         // n0 is a multiple of 32), so the gate/up choice is wave-uniform
-        static_assert(16 % RPD == 0, "DMA rows inside one gate/up block");
+        static_assert(16 % RPDW == 0, "DMA rows inside one gate/up block");
         col = (n >> 5) * 16 + (n & 15);
-        if ((q * RPD) & 16) up_mask |= 1u << j;
+        if ((q * RPDW) & 16) up_mask |= 1u << j;
       } else {
         col = n;
       }
       col = min(col, N - 1);
-      ob[j] = static_cast<uint32_t>(col * K * ES + logical * 16);
+      ob[j] = static_cast<uint32_t>(col * w_row + logical * 16);
       if (q < G::BBLK) ++my_loads;
     }
     const float* sa_src = g.sa;  // FP8: this lane's A-row scale row
@@ -302,6 +318,31 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
       sa_src = g.sa + src * kblocks;
       if (wave < G::SA_DMA) ++my_loads;
+    }
+    // MX: E8M0 scale rows of this lane, one dword (4 blocks of 32) per stage.
+    // Scale DMA number c < SA_DMA covers activation rows 64c.., the others
+    // weight rows 64(c - SA_DMA).. of the tile; wave w issues c = w, w + NW, ...
+    const uint8_t* msc[G::SCW > 0 ? G::SCW : 1];
+    if constexpr (MX) {
+      const int64_t kb32 = K / 32;
+#pragma unroll
+      for (int u = 0; u < G::SCW; ++u) {
+        const int c = wave + NW * u;
+        msc[u] = nullptr;
+        if (c < G::SA_DMA) {
+          const int rr = min(c * 64 + lane, rows - 1);
+          const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
+          msc[u] = reinterpret_cast<const uint8_t*>(g.sa) + src * kb32;
+          ++my_loads;
+        } else if (c < G::SA_DMA + G::SB_DMA) {
+          const int64_t n = n0 + (c - G::SA_DMA) * 64 + lane;
+          int64_t col = (PHASE == 1) ? (n >> 5) * 16 + (n & 15) : n;
+          col = min(col, N - 1);
+          const float* sb = (PHASE == 1 && (n & 16)) ? g.sb1 : g.sb0;
+          msc[u] = reinterpret_cast<const uint8_t*>(sb) + (static_cast<int64_t>(e) * N + col) * kb32;
+          ++my_loads;
+        }
+      }
     }
 
 // DMA of stage KS: the activation rows (and FP8 row scales) when DO_A, the
@@ -316,13 +357,21 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
         if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024); \
       }                                                                                  \
       if (DT == kFP8 && wave < G::SA_DMA)                                                \
-        dma4(sa_src + (KS), st_ + (BM + BN) * KRB + wave * 256);                         \
+        dma4(sa_src + (KS), st_ + BM * KRB + BN * KRBW + wave * 256);                    \
     }                                                                                    \
     if (DO_B) {                                                                          \
+      const uint32_t kw_ = static_cast<uint32_t>(KS) * KRBW;                             \
       _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                \
         const int q = wave + NW * j;                                                     \
         if (G::BBLK % NW == 0 || q < G::BBLK)                                            \
-          dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + ko_), st_ + BM * KRB + q * 1024); \
+          dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + kw_), st_ + BM * KRB + q * 1024); \
+      }                                                                                  \
+      if (MX) {                                                                          \
+        _Pragma("unroll") for (int u = 0; u < G::SCW; ++u) {                             \
+          const int c = wave + NW * u;                                                   \
+          if (c < G::SA_DMA + G::SB_DMA)                                                 \
+            dma4(msc[u] + (KS) * 4, st_ + BM * KRB + BN * KRBW + c * 256);               \
+        }                                                                                \
       }                                                                                  \
     }                                                                                    \
   } while (0)
@@ -380,6 +429,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       }
       const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
       const uint8_t* Bb = Ab + BM * KRB;
+      const uint8_t* Sb = Bb + BN * KRBW;  // per-stage scale dwords
       // A wave whose rows are all padding skips the step; a partly valid
       // wave computes its padding rows too (their results are never stored),
       // which keeps the fragment loop free of branches.
@@ -427,6 +477,39 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
   }
         MOE_F32_ROWS(false)
 #undef MOE_F32_ROWS
+      } else if constexpr (MX) {
+        // FP4 weights x MX FP8 activations: one scaled 16x16x128 MFMA per
+        // fragment pair; the E8M0 block scales are MFMA operands.  Lane group
+        // lg of a fragment covers contraction block lg (32 elements) of the
+        // step: the FP4 operand holds it in its 16 bytes in order, the FP8
+        // operand takes it as 16-byte chunks lg and lg + 4 (the hardware pairs
+        // a lane's FP8 bytes 0-15 with its FP4 block's first half and bytes
+        // 16-31 with the second half of block lg's partner), and each lane
+        // passes its own row's scale byte of block lg.
+        if (!compute) continue;
+        const uint32_t* sa_st = reinterpret_cast<const uint32_t*>(Sb);
+        const uint32_t* sw_st = sa_st + G::SA_DMA * 64;
+        i32x8 wf[TN];
+        int wsc[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int r = wn * WTN + 16 * j + l16;
+          const i32x4 c = *reinterpret_cast<const i32x4*>(Bb + swz<KRBW>(r, lg));
+          wf[j] = i32x8{c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+          wsc[j] = static_cast<int>((sw_st[r] >> (8 * lg)) & 0xffu);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int r = wm * WTM + 16 * i + l16;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, lg));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, lg + 4));
+          const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const int xsc = static_cast<int>((sa_st[r] >> (8 * lg)) & 0xffu);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 4, 0,
+                                                                         0, wsc[j], 0, xsc);
+        }
       } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
         if (!compute) continue;
         i32x8 wf[TN];
@@ -437,7 +520,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
           const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
           wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
-        const float* sa_st = reinterpret_cast<const float*>(Bb + BN * KRB);
+        const float* sa_st = reinterpret_cast<const float*>(Sb);
         const float s_b0 = sb_cur0, s_b1 = sb_cur1;
         if constexpr (PHASE == 1) {
           // Row by row: the TN block products of row i are issued before the
@@ -556,6 +639,40 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
               for (int j = 0; j < TN; ++j)
                 *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
                     acc[i][j];
+            } else if constexpr (MX) {
+              // h = SiLU(gate) * up; each block of 32 h columns (two 16-column
+              // fragments, held by the four lanes of this row) gets its MX FP8
+              // exponent from the block amax, then E4M3 codes of h * 2^-X
+#pragma unroll
+              for (int qb = 0; qb < TN / 4; ++qb) {
+                float h[2][4];
+                float m = 0.f;
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                  const int p = 2 * qb + pp;
+#pragma unroll
+                  for (int q4 = 0; q4 < 4; ++q4) {
+                    h[pp][q4] = silu(acc[i][2 * p][q4]) * acc[i][2 * p + 1][q4];
+                    m = fmaxf(m, fabsf(h[pp][q4]));
+                  }
+                }
+                m = fmaxf(m, __shfl_xor(m, 16, 64));
+                m = fmaxf(m, __shfl_xor(m, 32, 64));
+                const int x = mx_exponent_e4m3(m);
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                  uint32_t packed = 0;
+#pragma unroll
+                  for (int q4 = 0; q4 < 4; ++q4)
+                    packed |= f32_to_e4m3(__builtin_ldexpf(h[pp][q4], -x)) << (8 * q4);
+                  *reinterpret_cast<uint32_t*>(
+                      stage + st_off(r, wn * (WTN / 2) + 16 * (2 * qb + pp) + 4 * lg)) = packed;
+                }
+                if (lg == 0 && lr < rows)
+                  reinterpret_cast<uint8_t*>(g.sc)[static_cast<int64_t>(row0 + lr) * (N / 32) +
+                                                   (col0 + wn * (WTN / 2) + 32 * qb) / 32] =
+                      static_cast<uint8_t>(x + 127);
+              }
             } else if constexpr (DT == kFP8) {
               float amax = 0.f;
 #pragma unroll
@@ -697,6 +814,16 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kFP8, 2, 32, 0, 128, 1, 4)
   MOE_V(kFP8, 1, 16, 0, 256, 1, 4)
   MOE_V(kFP8, 2, 16, 0, 128, 1, 4)
+  MOE_V(kMX4, 1, 256, 0, 256, 2, 4)
+  MOE_V(kMX4, 2, 256, 0, 256, 2, 4)
+  MOE_V(kMX4, 1, 128, 0, 256, 2, 4)
+  MOE_V(kMX4, 2, 128, 0, 256, 2, 4)
+  MOE_V(kMX4, 1, 64, 0, 256, 1, 4)
+  MOE_V(kMX4, 2, 64, 0, 256, 1, 4)
+  MOE_V(kMX4, 1, 32, 0, 256, 1, 4)
+  MOE_V(kMX4, 2, 32, 0, 256, 1, 4)
+  MOE_V(kMX4, 1, 16, 0, 256, 1, 4)
+  MOE_V(kMX4, 2, 16, 0, 256, 1, 4)
   MOE_V(kF32, 1, 256, 0, 128, 2, 2)
   MOE_V(kF32, 2, 256, 0, 128, 2, 2)
   MOE_V(kF32, 1, 128, 0, 128, 2, 2)

@@ -31,25 +31,26 @@ struct TileMap {
   int32_t* queue;
 };
 
-// dtype codes (same values as moe_dtype)
-constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2;
+// dtype codes (same values as moe_dtype); kMX4 = FP4 (E2M1) weights with
+// E8M0 block scales, the activations MX FP8
+constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2, kMX4 = 3;
 
 struct GemmArgs {
   // activation operand: rows of K elements
   const uint8_t* A;
   int64_t a_row_bytes;
   const int32_t* gather;  // row index table (slot -> token), or null (row = slot)
-  const float* sa;        // FP8: [rows][K/128] scales of A rows
+  const float* sa;        // FP8: [rows][K/128] scales of A rows; MX: E8M0 bytes [rows][K/32]
   // weight operand(s): [E][N][K] (contraction axis contiguous)
   const uint8_t* B0;      // W1t (phase 1) or W2t (phase 2)
   const uint8_t* B1;      // W3t (phase 1)
-  const float* sb0;       // FP8: [E][K/128][N/128]
+  const float* sb0;       // FP8: [E][K/128][N/128]; MX: E8M0 bytes [E][N][K/32]
   const float* sb1;
   int64_t K;              // contraction length (elements)
   int64_t N;              // output columns: f (phase 1) or d (phase 2)
   // outputs
   uint8_t* C;             // h [slots][f] (phase 1) or Y fp32 [slots][d] (phase 2)
-  float* sc;              // FP8 phase 1: [slots][f/128] scales of h
+  float* sc;              // phase 1 h scales: FP8 [slots][f/128]; MX E8M0 bytes [slots][f/32]
   TileMap tm;
   int n_tiles_n;          // column tiles per m-tile
   int queue_idx;
@@ -69,6 +70,9 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int S, int bm, int3
                     int32_t* token_slot, TileMap tm, hipStream_t s);
 void launch_quant_fp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
                       hipStream_t st);
+// MX FP8: blocks of 32 along the row, E4M3 codes + E8M0 scale bytes [rows][cols/32].
+void launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                     hipStream_t st);
 // Grouped GEMMs.  bm = tile height; returns a hipError_t.
 int launch_gemm(int phase, int dtype, int bm, const GemmArgs& a, hipStream_t s);
 // Column tiles per m-tile for a phase (depends on the kernel variant).

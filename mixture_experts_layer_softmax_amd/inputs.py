@@ -15,6 +15,13 @@ Recipe (per workload, seed s):
           128x128 (K, N) block (scale = block amax / 448, codes = the value /
           scale cast by torch's float8_e4m3fn conversion after a clamp to
           +-448).  These codes and scales *are* the weights.
+  MXFP4 weights: drawn fp32, then stored in OCP MX FP4: per column n and
+          block of 32 consecutive K elements, X = floor(log2(amax)) - 2 (0 for
+          an all-zero block, clamped to [-127, 127]), the E8M0 byte X + 127
+          and E2M1 codes of v * 2^-X rounded to nearest even (saturating at
+          6), packed K-major [E][N][K/2] (element 2i in the low nibble of byte
+          i) with scales [E][N][K/32].  These codes and scales are the
+          weights.
 Every tensor has its own torch.Generator seeded from (seed, tensor id), so
 the draw order does not matter.  Draws on a CUDA device use that device's
 generator, draws on the CPU the CPU one: the bits differ between the two, so
@@ -24,7 +31,7 @@ from __future__ import annotations
 
 import torch
 
-from .configs import BF16, F32, FP8, MoEConfig
+from .configs import BF16, F32, FP8, MXFP4, MoEConfig
 
 _IDS = {"x": 1, "gate_w": 2, "W1": 3, "W3": 4, "W2": 5, "perm": 6}
 
@@ -68,13 +75,46 @@ def fp8_block_quantize(w: torch.Tensor):
     return codes.contiguous(), scale.contiguous()
 
 
+# code of each E2M1 magnitude m, indexed by 2*m (0, .5, 1, 1.5, 2, 3, 4, 6)
+_E2M1_CODE = {0: 0, 1: 1, 2: 2, 3: 3, 4: 4, 6: 5, 8: 6, 12: 7}
+
+
+def mxfp4_quantize(w: torch.Tensor):
+    """Store an fp32 [K x N] matrix (K a multiple of 32) as OCP MX FP4:
+    packed codes [N x K/2] uint8 and E8M0 scales [N x K/32] uint8."""
+    K, N = w.shape
+    wt = w.t().contiguous().view(N, K // 32, 32).to(torch.float64)
+    amax = wt.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)  # amax = m * 2^e, 0.5 <= m < 1
+    x = torch.where(amax > 0, (e.to(torch.int64) - 1 - 2).clamp(-127, 127),
+                    torch.zeros_like(e, dtype=torch.int64))
+    a = wt.abs() * torch.pow(2.0, -x.to(torch.float64))[..., None]  # exact
+    quantum = torch.where(a < 2, 0.5, torch.where(a < 4, 1.0, 2.0))
+    r = (torch.round(a / quantum) * quantum).clamp(max=6.0)  # round half to even
+    lut = torch.zeros(13, dtype=torch.uint8, device=w.device)
+    for m2, c in _E2M1_CODE.items():
+        lut[m2] = c
+    code = lut[(r * 2).to(torch.int64)] | (torch.signbit(wt).to(torch.uint8) << 3)
+    code = code.view(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed, (x + 127).to(torch.uint8).contiguous()
+
+
+def unpack_mxfp4(packed: torch.Tensor) -> torch.Tensor:
+    """[.., N, K/2] packed codes -> [.., N, K] one code per byte."""
+    lo, hi = packed & 15, packed >> 4
+    return torch.stack([lo, hi], dim=-1).flatten(-2)
+
+
 def make_inputs(cfg: MoEConfig, device="cpu", seed: int | None = None,
                 experts=None) -> dict:
     """Draw the layer inputs of `cfg` on `device`.
 
     Returns a dict with x, gate_w, bias (or None), W1, W3, W2 and, for FP8
     weights, W1s, W3s, W2s.  Weight tensors are [E+S][K][N] in the stated
-    layouts (W1/W3 [.][d][f], W2 [.][f][d]), the S shared experts last.
+    layouts (W1/W3 [.][d][f], W2 [.][f][d]), the S shared experts last; MXFP4
+    weights are the packed K-major codes [.][N][K/2] and W1s/W3s/W2s their
+    E8M0 scales [.][N][K/32].
     `experts` (optional) limits the weight draw to those expert indices
     (others stay zero) -- a test
     convenience only; the draws of the listed experts do not change.
@@ -91,7 +131,10 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: int | None = None,
     wanted = set(range(NE)) if experts is None else set(int(e) for e in experts)
     for name, (K, N) in (("W1", (d, f)), ("W3", (d, f)), ("W2", (f, d))):
         g = _gen(seed, name, device)
-        if cfg.w_dtype == FP8:
+        if cfg.w_dtype == MXFP4:
+            codes = torch.zeros((NE, N, K // 2), dtype=torch.uint8, device=device)
+            scales = torch.zeros((NE, N, K // 32), dtype=torch.uint8, device=device)
+        elif cfg.w_dtype == FP8:
             codes = torch.zeros((NE, K, N), dtype=torch.uint8, device=device)
             scales = torch.zeros((NE, (K + 127) // 128, (N + 127) // 128),
                                  dtype=torch.float32, device=device)
@@ -104,7 +147,11 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: int | None = None,
             w = _normal((K, N), 0.02, g, device)
             if e not in wanted:
                 continue
-            if cfg.w_dtype == FP8:
+            if cfg.w_dtype == MXFP4:
+                c, s = mxfp4_quantize(w)
+                codes[e] = c
+                scales[e] = s
+            elif cfg.w_dtype == FP8:
                 c, s = fp8_block_quantize(w)
                 codes[e] = c
                 scales[e] = s
@@ -132,6 +179,20 @@ def host_arrays(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+def host_weight(cfg: MoEConfig, inp: dict, name: str, e: int):
+    """Expert e's weight `name` (W1, W3, W2) in host memory as a [K x N] array
+    in the storage convention of host_arrays, with its scales (FP8: fp32
+    [K/128 x N/128]; MXFP4: E8M0 bytes [K/32 x N]; otherwise None).  MXFP4
+    codes are unpacked from the K-major nibble layout to one code per byte:
+    a change of layout only, the bits are the ones the GPU reads."""
+    if cfg.w_dtype == MXFP4:
+        codes = unpack_mxfp4(inp[name][e]).t().contiguous().cpu().numpy()
+        return codes, inp[name + "s"][e].t().contiguous().cpu().numpy()
+    if cfg.w_dtype == FP8:
+        return host_arrays(inp[name][e]), inp[name + "s"][e].cpu().numpy()
+    return host_arrays(inp[name][e]), None
 
 
 def round_up(x: int, m: int) -> int:

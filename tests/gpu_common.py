@@ -7,10 +7,10 @@ import torch
 
 import oracle
 from mixture_experts_layer_softmax_amd import binding as B
-from mixture_experts_layer_softmax_amd.configs import BF16, F32, FP8
-from mixture_experts_layer_softmax_amd.inputs import host_arrays, make_inputs
+from mixture_experts_layer_softmax_amd.configs import BF16, F32, FP8, MXFP4
+from mixture_experts_layer_softmax_amd.inputs import host_arrays, host_weight, make_inputs
 
-ORC = {F32: oracle.ORC_F32, BF16: oracle.ORC_BF16, FP8: oracle.ORC_FP8}
+ORC = {F32: oracle.ORC_F32, BF16: oracle.ORC_BF16, FP8: oracle.ORC_FP8, MXFP4: oracle.ORC_MXFP4}
 
 
 def say(*a):
@@ -42,17 +42,15 @@ def oracle_forward_rows(cfg, inp, rows):
     W = {n: [None] * (E + cfg.n_shared) for n in ("W1", "W3", "W2", "W1s", "W3s", "W2s")}
     for e in need:
         for n in ("W1", "W3", "W2"):
-            W[n][e] = host_arrays(inp[n][e])
-            if cfg.w_dtype == FP8:
-                W[n + "s"][e] = inp[n + "s"][e].cpu().numpy()
+            W[n][e], W[n + "s"][e] = host_weight(cfg, inp, n, e)
     x = host_arrays(inp["x"][torch.as_tensor(rows, device=inp["x"].device)])
     gw = host_arrays(inp["gate_w"])
     bias = None if inp.get("bias") is None else inp["bias"].cpu().numpy()
-    fp8 = cfg.w_dtype == FP8
+    sc = cfg.w_dtype in (FP8, MXFP4)
     out, ids, w = oracle.forward(x, gw, bias, W["W1"], W["W3"], W["W2"], cfg.k,
                                  ORC[cfg.act_dtype], ORC[cfg.w_dtype],
-                                 W1s=W["W1s"] if fp8 else None, W3s=W["W3s"] if fp8 else None,
-                                 W2s=W["W2s"] if fp8 else None, n_shared=cfg.n_shared)
+                                 W1s=W["W1s"] if sc else None, W3s=W["W3s"] if sc else None,
+                                 W2s=W["W2s"] if sc else None, n_shared=cfg.n_shared)
     return out, ids, w
 
 

@@ -7,8 +7,9 @@ import numpy as np
 import torch
 
 # Output tolerance, relative to the RMS of the exact (unrounded) oracle output:
-# bf16 layers 1e-2 (on the fp32-output run), FP8 layers 5e-2, fp32 layers 1e-4.
-TOL = {0: 1e-4, 1: 1e-2, 2: 5e-2}
+# bf16 layers 1e-2 (on the fp32-output run), FP8 and MXFP4 layers 5e-2, fp32
+# layers 1e-4.
+TOL = {0: 1e-4, 1: 1e-2, 2: 5e-2, 3: 5e-2}
 
 
 def ulp_bf16(v: np.ndarray) -> np.ndarray:

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from mixture_experts_layer_softmax_amd import binding as B
-from mixture_experts_layer_softmax_amd.configs import BF16, CONFIGS, F32, FP8, MoEConfig
+from mixture_experts_layer_softmax_amd.configs import BF16, CONFIGS, F32, FP8, MXFP4, MoEConfig
 from tests.gpu_common import (free, gpu_inputs, gpu_permute, gpu_route, oracle_forward_rows,
                               oracle_route_rows, say)
 from tests.helpers import TOL, check_output, f32_ulps
@@ -27,6 +27,8 @@ REDUCED = {
     "skewed_bf16_r": MoEConfig("skewed_bf16_r", 600, 512, 384, 64, 6, BF16, BF16, BF16,
                                skew_bias=True),
     "prefill_fp8_r": MoEConfig("prefill_fp8_r", 300, 512, 256, 16, 8, BF16, FP8, BF16),
+    "prefill_mxfp4_r": MoEConfig("prefill_mxfp4_r", 300, 512, 256, 16, 8, BF16, MXFP4, BF16),
+    "decode_mxfp4_r": MoEConfig("decode_mxfp4_r", 16, 1024, 512, 64, 8, BF16, MXFP4, BF16),
 }
 
 
@@ -81,7 +83,8 @@ def test_forward_parity_reduced(name):
 
 
 @pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
-@pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16_r", "prefill_fp8_r"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16_r", "prefill_fp8_r",
+                                  "prefill_mxfp4_r"])
 def test_forward_every_tile_height(name, block_m):
     cfg = REDUCED[name]
     say("forward bm", name, block_m)
@@ -107,6 +110,23 @@ def test_quantize_fp8_bit_exact():
     assert np.array_equal(s.cpu().numpy(), rs)
 
 
+def test_quantize_mx_bit_exact():
+    say("quant mx")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    x = (torch.randn((333, 1024), generator=g, device="cuda") *
+         torch.logspace(-3, 3, 1024, device="cuda")).to(torch.bfloat16)
+    x[7, 128:160] = 0  # an all-zero block
+    x[9, 0:32] = 3.0   # a constant block
+    q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    s = torch.empty((333, 32), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mx(x, q, s)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quant_rows(x.float().cpu().numpy(), oracle.MX_E4M3)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy(), rs)
+
+
 EDGE = {
     "T1": MoEConfig("T1", 1, 256, 128, 8, 2, BF16, BF16, BF16),
     "ragged": MoEConfig("ragged", 37, 128, 192, 4, 3, BF16, BF16, BF16),
@@ -115,6 +135,8 @@ EDGE = {
     "k_eq_E": MoEConfig("k_eq_E", 40, 128, 128, 8, 8, BF16, BF16, BF16),
     "fp32_small": MoEConfig("fp32_small", 50, 32, 64, 3, 2, F32, F32, F32),
     "fp8_small": MoEConfig("fp8_small", 20, 128, 128, 4, 2, BF16, FP8, BF16),
+    "mx_small": MoEConfig("mx_small", 20, 128, 128, 4, 2, BF16, MXFP4, BF16),
+    "mx_T1": MoEConfig("mx_T1", 1, 256, 384, 8, 2, BF16, MXFP4, BF16),
 }
 
 
@@ -208,6 +230,7 @@ SHARED = {
     "sh_fp8": REDUCED["prefill_fp8_r"].replace(name="sh_fp8", n_shared=1),
     "sh_T1": EDGE["T1"].replace(name="sh_T1", n_shared=3),
     "sh_ragged": EDGE["ragged"].replace(name="sh_ragged", n_shared=1),
+    "sh_mx": REDUCED["prefill_mxfp4_r"].replace(name="sh_mx", n_shared=1),
 }
 
 
@@ -257,11 +280,12 @@ def test_shared_expert_leaves_routing_alone():
 # ---------------------------------------------------------------------------
 
 FULL_SAMPLE = {"prefill_bf16": 48, "decode_bf16": 12, "skewed_bf16": 24, "prefill_fp8": 6,
-               "prefill_bf16_shared": 24}
+               "prefill_bf16_shared": 24, "prefill_mxfp4": 6, "decode_mxfp4": 12}
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16", "decode_bf16", "skewed_bf16",
-                                  "prefill_fp8", "prefill_bf16_shared"])
+                                  "prefill_fp8", "prefill_bf16_shared", "prefill_mxfp4",
+                                  "decode_mxfp4"])
 def test_full_size_parity(name):
     cfg = CONFIGS[name]
     say("full", name)
