@@ -201,7 +201,8 @@ moe_status moe_weight_bytes(const moe_problem *p, size_t *bytes);
  * layouts) is written as its transpose [N][K], so that the contraction axis
  * is contiguous for the MFMA operand loads.  src and dst must not overlap.
  * elem_bytes is 4 (fp32), 2 (bf16) or 1 (FP8 codes); E matrices of K x N.
- * MXFP4 weights are given already K-major and need no packing. */
+ * MXFP4 weight codes are given already K-major and need no packing; their
+ * E8M0 scales [E][N][K/32] are packed as E matrices of N x K/128 dwords. */
 moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
                            const void *src, void *dst, hipStream_t stream);
 
@@ -214,9 +215,12 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
  *           (MXFP4: the same [N][K] shapes with two E2M1 codes per byte,
  *           element 2i in the low nibble of byte i -- K-major as given)
  *   W1s,W3s FP8: [E+S][d/128][f/128] fp32 block scales;
- *           MXFP4: [E+S][f][d/32] E8M0 bytes (one per 32 elements along K);
+ *           MXFP4: E8M0 bytes, one per 32 elements along K, given as
+ *           [E+S][f][d/32] and packed by moe_pack_weight (elem_bytes 4, the
+ *           rows' dwords of 4 blocks transposed) to [E+S][d/128][f] dwords;
  *           NULL otherwise
  *   W2s     FP8: [E+S][f/128][d/128] fp32; MXFP4: [E+S][d][f/32] E8M0 bytes
+ *           packed likewise to [E+S][f/128][d] dwords
  *           (S = n_shared: the shared experts follow the routed ones)
  *   out     [T][d]       out_dtype
  *   ws/ws_bytes          workspace of at least moe_workspace_size()

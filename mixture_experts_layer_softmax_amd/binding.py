@@ -189,11 +189,19 @@ def moe_forward(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, dbg=N
 
 def pack_weights(inp: dict, stream=None) -> dict:
     """One-time re-layout of W1/W3/W2 ([E][K][N] -> [E][N][K]) on the GPU.
-    MXFP4 weights (uint8 E8M0 scales) come K-major already and pass through."""
+    MXFP4 weights (uint8 E8M0 scales) come K-major already; their scales
+    [E][N][K/32] are re-laid as [E][K/128][N] dwords (4 blocks of 32 each)."""
     out = {}
     if inp.get("W1s") is not None and inp["W1s"].dtype == torch.uint8:
-        return {"W1t": inp["W1"], "W3t": inp["W3"], "W2t": inp["W2"],
-                "W1s": inp["W1s"], "W3s": inp["W3s"], "W2s": inp["W2s"]}
+        out = {"W1t": inp["W1"], "W3t": inp["W3"], "W2t": inp["W2"]}
+        for name in ("W1s", "W3s", "W2s"):
+            sc = inp[name]
+            E, N, KB = sc.shape
+            src = sc.view(torch.int32)  # [E][N][K/128] dwords
+            dst = torch.empty((E, KB // 4, N), dtype=torch.int32, device=sc.device)
+            moe_pack_weight(src, dst, stream)
+            out[name] = dst.view(torch.uint8)
+        return out
     for name in ("W1", "W3", "W2"):
         w = inp[name]
         E, K, N = w.shape

@@ -84,7 +84,9 @@ struct Geo {
   static constexpr int STAGE = BM * KRB + BN * KRBW + SCALE_BYTES;
   static constexpr int RED = (DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0;
   static constexpr int NS0 = (kLdsBytes - RED) / STAGE;
-  static constexpr int NS = NS0 > 6 ? 6 : NS0;
+  // small tiles (decode: HBM bound) keep more stages in flight
+  static constexpr int NS_CAP = BM <= 32 ? 8 : 6;
+  static constexpr int NS = NS0 > NS_CAP ? NS_CAP : NS0;
   static constexpr int EPI =  // output staging, one pass per wave row
       (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : 4);
   static constexpr int RING = NS * STAGE;
@@ -319,16 +321,21 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       sa_src = g.sa + src * kblocks;
       if (wave < G::SA_DMA) ++my_loads;
     }
-    // MX: E8M0 scale rows of this lane, one dword (4 blocks of 32) per stage.
-    // Scale DMA number c < SA_DMA covers activation rows 64c.., the others
-    // weight rows 64(c - SA_DMA).. of the tile; wave w issues c = w, w + NW, ...
+    // MX: E8M0 scale dwords of this lane (4 blocks of 32 = one stage).
+    // Scale DMA number c < SA_DMA covers activation rows 64c.. ([rows][K/32]
+    // bytes: the next stage's dword follows), the others weight rows
+    // 64(c - SA_DMA).. of the tile (packed [E][K/128][N] dwords: a stage's
+    // dwords of consecutive rows are contiguous, the next stage is N dwords
+    // on); wave w issues c = w, w + NW, ...
     const uint8_t* msc[G::SCW > 0 ? G::SCW : 1];
+    uint32_t mstep[G::SCW > 0 ? G::SCW : 1];
     if constexpr (MX) {
       const int64_t kb32 = K / 32;
 #pragma unroll
       for (int u = 0; u < G::SCW; ++u) {
         const int c = wave + NW * u;
         msc[u] = nullptr;
+        mstep[u] = 4;
         if (c < G::SA_DMA) {
           const int rr = min(c * 64 + lane, rows - 1);
           const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
@@ -339,7 +346,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
           int64_t col = (PHASE == 1) ? (n >> 5) * 16 + (n & 15) : n;
           col = min(col, N - 1);
           const float* sb = (PHASE == 1 && (n & 16)) ? g.sb1 : g.sb0;
-          msc[u] = reinterpret_cast<const uint8_t*>(sb) + (static_cast<int64_t>(e) * N + col) * kb32;
+          msc[u] = reinterpret_cast<const uint8_t*>(sb) + (static_cast<int64_t>(e) * N * kb32 + col * 4);
+          mstep[u] = static_cast<uint32_t>(N * 4);
           ++my_loads;
         }
       }
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
         _Pragma("unroll") for (int u = 0; u < G::SCW; ++u) {                             \
           const int c = wave + NW * u;                                                   \
           if (c < G::SA_DMA + G::SB_DMA)                                                 \
-            dma4(msc[u] + (KS) * 4, st_ + BM * KRB + BN * KRBW + c * 256);               \
+            dma4(msc[u] + (KS) * mstep[u], st_ + BM * KRB + BN * KRBW + c * 256);        \
         }                                                                                \
       }                                                                                  \
     }                                                                                    \
