@@ -487,13 +487,15 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 #undef MOE_F32_ROWS
       } else if constexpr (MX) {
         // FP4 weights x MX FP8 activations: one scaled 16x16x128 MFMA per
-        // fragment pair; the E8M0 block scales are MFMA operands.  Lane group
-        // lg of a fragment covers contraction block lg (32 elements) of the
-        // step: the FP4 operand holds it in its 16 bytes in order, the FP8
-        // operand takes it as 16-byte chunks lg and lg + 4 (the hardware pairs
-        // a lane's FP8 bytes 0-15 with its FP4 block's first half and bytes
-        // 16-31 with the second half of block lg's partner), and each lane
-        // passes its own row's scale byte of block lg.
+        // fragment pair; the E8M0 block scales are MFMA operands.  Measured
+        // operand layout: FP4 lane group lg holds 32 elements in its 16 bytes
+        // (low nibble first) and, in both operands, lane group lg's scale
+        // byte governs exactly those 32 elements; FP8 lane group lg pairs its
+        // bytes 0-15 and 16-31 with half (lg & 1) of FP4 groups lg >> 1 and
+        // (lg >> 1) + 2.  So contraction block lg (32 elements) of the step
+        // goes to FP4 lane group lg in order, the FP8 lanes take 16-byte
+        // chunks lg and lg + 4 of the activation row, and each lane passes
+        // its own row's scale byte of block lg.
         if (!compute) continue;
         const uint32_t* sa_st = reinterpret_cast<const uint32_t*>(Sb);
         const uint32_t* sw_st = sa_st + G::SA_DMA * 64;
