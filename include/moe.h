@@ -153,7 +153,8 @@ moe_status moe_workspace_size(const moe_problem *p, size_t *bytes);
  *   logits   [T][E]   fp32 output, or NULL (then kept in the workspace)
  *   topk_ids [T][k]   int32 output, descending logit, ties to lower index
  *   topk_w   [T][k]   fp32 output, renormalised softmax weights
- *   ws/ws_bytes       workspace; may be NULL/0 when logits != NULL. */
+ *   ws/ws_bytes       workspace; may be NULL/0 when logits != NULL.
+ * d must be a multiple of 32 (MOE_ERR_UNSUPPORTED otherwise). */
 moe_status moe_route(const moe_problem *p, const void *x, const void *gate_w,
                      const float *bias, float *logits, int32_t *topk_ids,
                      float *topk_w, void *ws, size_t ws_bytes,

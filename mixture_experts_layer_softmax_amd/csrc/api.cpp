@@ -205,6 +205,7 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* gate_w, co
                      float* logits, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
   if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
+  if (p->d % 32 != 0) return MOE_ERR_UNSUPPORTED;  // hidden chunks of 32 in the gate
   if (p->T == 0) return MOE_OK;
   if (!x || !gate_w || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   float* lg = logits;
@@ -215,9 +216,8 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* gate_w, co
     lg = at<float>(ws, L.logits);
   }
   (void)hipGetLastError();
-  moe::launch_logits(x, gate_w, bias, lg, static_cast<int>(p->T), static_cast<int>(p->d), p->E,
-                     p->act_dtype == MOE_BF16, stream);
-  moe::launch_topk(lg, topk_ids, topk_w, static_cast<int>(p->T), p->E, p->top_k, stream);
+  moe::launch_gate(x, gate_w, bias, lg, topk_ids, topk_w, static_cast<int>(p->T),
+                   static_cast<int>(p->d), p->E, p->top_k, p->act_dtype == MOE_BF16, stream);
   return hip_status();
 }
 
@@ -306,8 +306,8 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   (void)hipGetLastError();
   mark(0);
   // 1. gate
-  moe::launch_logits(x, gate_w, bias, logits, T, d, E, p->act_dtype == MOE_BF16, stream);
-  moe::launch_topk(logits, ids, w, T, E, k, stream);
+  moe::launch_gate(x, gate_w, bias, logits, ids, w, T, d, E, k, p->act_dtype == MOE_BF16,
+                   stream);
   mark(1);
   // 2. FP8 (or MX FP8) activations
   if (fp8)

@@ -58,10 +58,9 @@ struct GemmArgs {
   uint64_t* clock;        // [2] or null: ticks of workgroup 0 (shader, 100 MHz reference)
 };
 
-void launch_logits(const void* x, const void* gate_w, const float* bias, float* logits,
-                   int T, int d, int E, bool bf16, hipStream_t s);
-void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
-                 hipStream_t s);
+// Gate: logits [T][E] (+ bias), top-k ids and renormalised weights [T][k].
+void launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
+                 int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s);
 // S shared experts add T slots each after the T*k routed ones (slot
 // T*k + s*T + t holds token t, k-slot k + s) and their m-tiles after the
 // routed ones.

@@ -5,210 +5,42 @@
 //
 // Logits follow one fixed fp32 order so the selection is reproducible bit for
 // bit on any device: acc = +0, acc = fma(x[t][i], w[i][e], acc) for i
-// ascending, then acc + bias[e].  Each logit is one lane's sequential chain;
-// parallelism comes from the T x E outputs, register-blocked RT x RE per lane
-// over LDS tiles that hold x and gate_w already widened to fp32.
+// ascending, then acc + bias[e].  The chains run on the fp32 MFMA, whose
+// four-product step is exactly four such fmas in order (see gate_kernel).
 #include "device_common.hpp"
 #include "launch.hpp"
+
+#include <algorithm>
 
 namespace moe {
 
 namespace {
 
-constexpr int kRoutePad = 4;  // floats of padding per LDS row (keeps float4 alignment)
-
-// Block of 256 threads = TYL x TXL lanes; lane (ty, tx) owns tokens
-// t0 + ty * RT + a (a < RT) and experts e0 + tx * RE + b (b < RE).  LDS holds
-// x[t][i] and gate_w[i][e] of one hidden chunk already widened to fp32, both
-// with the hidden index contiguous, so a lane reads four consecutive i of one
-// row with one float4 load and then runs its RT x RE chains four FMA steps, i
-// ascending -- the fixed summation order is untouched by the blocking.  The
-// next chunk is loaded into registers while the current one is computed.
-template <int RT, int RE, int TYL, int TXL, int KB, bool BF16>
-__global__ __launch_bounds__(256) void logits_kernel(
-    const void* __restrict__ xv, const void* __restrict__ wv,
-    const float* __restrict__ bias, float* __restrict__ logits, int T, int d,
-    int E) {
-  static_assert(TYL * TXL == 256, "256 threads");
-  // fma-step unroll of whole chunks for lanes with one chain (its LDS
-  // latency is otherwise exposed); blocked shapes keep the plain loop
-  constexpr int UNR = (RT * RE == 1) ? 8 : 1;
-  constexpr int TT = TYL * RT, TE = TXL * RE;
-  constexpr int LD = KB + kRoutePad;
-  constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte global load
-  constexpr int XCH = TT * (KB / EPC), WCH = KB * (TE / EPC);  // 16-byte chunks
-  constexpr int XR = (XCH + 255) / 256, WR = (WCH + 255) / 256;
-  extern __shared__ __attribute__((aligned(16))) float route_lds[];
-  float (*xs)[LD] = reinterpret_cast<float (*)[LD]>(route_lds);            // [TT][LD]
-  float (*ws)[LD] = reinterpret_cast<float (*)[LD]>(route_lds + TT * LD);  // [TE][LD]
-  const int tid = threadIdx.x, tx = tid % TXL, ty = tid / TXL;
-  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
-  float acc[RT][RE];
+// Top-k of one token's E logits l[0..E) (global or LDS) by one wavefront: k
+// rounds of a wave-wide argmax ordered by (logit descending, expert index
+// ascending), then the softmax over the k selected logits in fp64 (lane j
+// evaluates exp(l_j - l_0) of selection j; the sum is a wave reduction).
+// E <= 64 * SLOTS.
+template <int SLOTS>
+__device__ __forceinline__ void topk_row(const float* l, int E, int k, int32_t* out_ids,
+                                         float* out_w, int lane) {
+  float v[SLOTS];
 #pragma unroll
-  for (int a = 0; a < RT; ++a)
-#pragma unroll
-    for (int b = 0; b < RE; ++b) acc[a][b] = 0.0f;
-
-  // prefetch registers: raw 16-byte pieces of the next chunk (widened when
-  // stored to LDS); out-of-range pieces are zero
-  u32x4 xr[XR], wr[WR];
-  bool wvec[WR];  // piece loaded as one aligned 16-byte vector
-#define MOE_RLOAD(I0)                                                                    \
-  do {                                                                                   \
-    _Pragma("unroll") for (int r = 0; r < XR; ++r) {                                     \
-      const int idx = tid + 256 * r;                                                     \
-      const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;                    \
-      const int t = t0 + tl, i = (I0) + il;                                              \
-      xr[r] = u32x4{0u, 0u, 0u, 0u};                                                     \
-      if (idx < XCH && t < T && i < d) {                                                 \
-        const size_t o = static_cast<size_t>(t) * d + i;                                 \
-        xr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xv) + o) \
-                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(xv) + o); \
-      }                                                                                  \
-    }                                                                                    \
-    _Pragma("unroll") for (int r = 0; r < WR; ++r) {                                     \
-      const int idx = tid + 256 * r;                                                     \
-      const int il = idx / (TE / EPC), el = (idx % (TE / EPC)) * EPC;                    \
-      const int e = e0 + el, i = (I0) + il;                                              \
-      wr[r] = u32x4{0u, 0u, 0u, 0u};                                                     \
-      wvec[r] = idx < WCH && i < d && E % EPC == 0 && e + EPC <= E;                      \
-      if (wvec[r]) {                                                                     \
-        const size_t o = static_cast<size_t>(i) * E + e;                                 \
-        wr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wv) + o) \
-                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(wv) + o); \
-      }                                                                                  \
-    }                                                                                    \
-  } while (0)
-#define MOE_RSTORE(I0)                                                                   \
-  do {                                                                                   \
-    _Pragma("unroll") for (int r = 0; r < XR; ++r) {                                     \
-      const int idx = tid + 256 * r;                                                     \
-      if (idx < XCH) {                                                                   \
-        const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;                  \
-        float v[EPC];                                                                    \
-        if (BF16) {                                                                      \
-          _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
-            v[2 * q] = __uint_as_float(xr[r][q] << 16);                                  \
-            v[2 * q + 1] = __uint_as_float(xr[r][q] & 0xffff0000u);                      \
-          }                                                                              \
-        } else {                                                                         \
-          _Pragma("unroll") for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(xr[r][q]); \
-        }                                                                                \
-        _Pragma("unroll") for (int q = 0; q < EPC; q += 4) *reinterpret_cast<f32x4*>(    \
-            &xs[tl][il + q]) = f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};                \
-      }                                                                                  \
-    }                                                                                    \
-    _Pragma("unroll") for (int r = 0; r < WR; ++r) {                                     \
-      const int idx = tid + 256 * r;                                                     \
-      if (idx < WCH) {                                                                   \
-        const int il = idx / (TE / EPC), el = (idx % (TE / EPC)) * EPC;                  \
-        const int i = (I0) + il;                                                         \
-        float v[EPC];                                                                    \
-        if (wvec[r]) {                                                                   \
-          if (BF16) {                                                                    \
-            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                              \
-              v[2 * q] = __uint_as_float(wr[r][q] << 16);                                \
-              v[2 * q + 1] = __uint_as_float(wr[r][q] & 0xffff0000u);                    \
-            }                                                                            \
-          } else {                                                                       \
-            _Pragma("unroll") for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(wr[r][q]); \
-          }                                                                              \
-        } else {                                                                         \
-          _Pragma("unroll") for (int q = 0; q < EPC; ++q) {                              \
-            const int eq = e0 + el + q;                                                  \
-            float val = 0.0f;                                                            \
-            if (i < d && eq < E) {                                                       \
-              const size_t o = static_cast<size_t>(i) * E + eq;                          \
-              val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])              \
-                         : static_cast<const float*>(wv)[o];                             \
-            }                                                                            \
-            v[q] = val;                                                                  \
-          }                                                                              \
-        }                                                                                \
-        _Pragma("unroll") for (int q = 0; q < EPC; ++q) ws[el + q][il] = v[q];           \
-      }                                                                                  \
-    }                                                                                    \
-  } while (0)
-
-  MOE_RLOAD(0);
-  for (int i0 = 0; i0 < d; i0 += KB) {
-    MOE_RSTORE(i0);
-    __syncthreads();
-    if (i0 + KB < d) MOE_RLOAD(i0 + KB);  // in flight during this chunk's FMAs
-    const int iend = min(KB, d - i0);     // d % 8 == 0, so iend % 4 == 0
-#define MOE_GATE_STEP(IL)                                                                 \
-  do {                                                                                    \
-    f32x4 xv4[RT], wv4[RE];                                                               \
-    _Pragma("unroll") for (int a = 0; a < RT; ++a) xv4[a] =                               \
-        *reinterpret_cast<const f32x4*>(&xs[ty * RT + a][(IL)]);                          \
-    _Pragma("unroll") for (int b = 0; b < RE; ++b) wv4[b] =                               \
-        *reinterpret_cast<const f32x4*>(&ws[tx * RE + b][(IL)]);                          \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                         \
-    _Pragma("unroll") for (int a = 0; a < RT; ++a)                                        \
-    _Pragma("unroll") for (int b = 0; b < RE; ++b) acc[a][b] =                            \
-        __builtin_fmaf(xv4[a][u], wv4[b][u], acc[a][b]);                                  \
-  } while (0)
-    if (UNR > 1 && iend == KB) {
-      // whole chunk: a compile-time trip count, unrolled so that the LDS
-      // reads of the next steps are issued ahead of this step's fma chain
-      // (the fma order of every chain stays i ascending)
-#pragma unroll UNR
-      for (int il = 0; il < KB; il += 4) MOE_GATE_STEP(il);
-    } else {
-      for (int il = 0; il < iend; il += 4) MOE_GATE_STEP(il);
-    }
-#undef MOE_GATE_STEP
-    __syncthreads();
-  }
-#undef MOE_RLOAD
-#undef MOE_RSTORE
-#pragma unroll
-  for (int a = 0; a < RT; ++a) {
-    const int t = t0 + ty * RT + a;
-    if (t >= T) continue;
-#pragma unroll
-    for (int b = 0; b < RE; ++b) {
-      const int e = e0 + tx * RE + b;
-      if (e >= E) continue;
-      float l = acc[a][b];
-      if (bias) l = l + bias[e];
-      logits[static_cast<size_t>(t) * E + e] = l;
-    }
-  }
-}
-
-// One wavefront per token: k rounds of a wave-wide argmax ordered by
-// (logit descending, expert index ascending), then fp64 softmax over the k
-// selected logits.  E <= 1024 (16 logits per lane).
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
-                                                   int32_t* __restrict__ ids,
-                                                   float* __restrict__ w, int T,
-                                                   int E, int k) {
-  constexpr int kMaxPerLane = 16;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* l = logits + static_cast<size_t>(t) * E;
-  float v[kMaxPerLane];
-#pragma unroll
-  for (int s = 0; s < kMaxPerLane; ++s) {
+  for (int s = 0; s < SLOTS; ++s) {
     int e = lane + 64 * s;
     v[s] = (e < E) ? l[e] : -INFINITY;
   }
-  int32_t* out_ids = ids + static_cast<size_t>(t) * k;
-  float* out_w = w + static_cast<size_t>(t) * k;
   // selection j is kept by lane (j mod 64) in slot j / 64
-  int sel_e[kMaxPerLane];
-  float sel_v[kMaxPerLane];
+  int sel_e[SLOTS];
+  float sel_v[SLOTS];
   float top0 = 0.0f;
-  double sum = 0.0;
   uint32_t taken = 0;  // bit s set: v[s] of this lane already selected
   for (int j = 0; j < k; ++j) {
     // local best among untaken entries (ties: smaller e, i.e. smaller s)
     float bv = 0.0f;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int s = 0; s < kMaxPerLane; ++s) {
+    for (int s = 0; s < SLOTS; ++s) {
       int e = lane + 64 * s;
       bool ok = e < E && !((taken >> s) & 1u);
       if (ok && (be == 0x7fffffff || v[s] > bv || (v[s] == bv && e < be))) {
@@ -229,74 +61,396 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     }
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     if (j == 0) top0 = bv;
-    sum += exp(static_cast<double>(bv) - static_cast<double>(top0));
 #pragma unroll
-    for (int s = 0; s < kMaxPerLane; ++s)
+    for (int s = 0; s < SLOTS; ++s)
       if (j == lane + 64 * s) {
         sel_e[s] = be;
         sel_v[s] = bv;
       }
   }
+  double u[SLOTS];
+  double part = 0.0;
 #pragma unroll
-  for (int s = 0; s < kMaxPerLane; ++s) {
+  for (int s = 0; s < SLOTS; ++s) {
+    u[s] = 0.0;
+    if (lane + 64 * s < k) {
+      u[s] = exp(static_cast<double>(sel_v[s]) - static_cast<double>(top0));
+      part += u[s];
+    }
+  }
+  const double sum = wave_sum(part);
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
     int j = lane + 64 * s;
     if (j < k) {
-      double u = exp(static_cast<double>(sel_v[s]) - static_cast<double>(top0));
       out_ids[j] = sel_e[s];
-      out_w[j] = static_cast<float>(u / sum);
+      out_w[j] = static_cast<float>(u[s] / sum);
     }
+  }
+}
+
+// One wavefront per token.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ w, int T,
+                                                   int E, int k) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_row<16>(logits + static_cast<size_t>(t) * E, E, k, ids + static_cast<size_t>(t) * k,
+               w + static_cast<size_t>(t) * k, threadIdx.x & 63);
+}
+
+// (value, index) a ranks before (value, index) b: larger logit first, equal
+// logits by lower expert index.
+__device__ __forceinline__ bool gate_before(float av, int ae, float bv, int be) {
+  return av > bv || (av == bv && ae < be);
+}
+
+// Top-k (k <= min(G, 8)) of one token's E logits row[0..E) by G consecutive
+// lanes (G = 4 or 8): each lane keeps its own sorted list of the 8 best of
+// experts part, part + G, ... (a compare-exchange chain per expert), the G
+// lists are merged pairwise (the 8 best of two sorted lists are the larger
+// of a_i and b_{7-i}, a bitonic sequence that three half-cleaner stages
+// sort), and lane j < k writes selection j with weight
+// exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0) in fp64, the sum in i order.
+template <int G>
+__device__ __forceinline__ void topk_group(const float* row, int E, int k, int32_t* out_ids,
+                                           float* out_w, int part, int lane) {
+  float lv[8];
+  int le[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    lv[p] = -INFINITY;
+    le[p] = 0x7fffffff;
+  }
+  for (int e = part; e < E; e += G) {
+    float xv = row[e];
+    int xe = e;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      if (gate_before(xv, xe, lv[p], le[p])) {
+        const float tv = lv[p];
+        const int te = le[p];
+        lv[p] = xv;
+        le[p] = xe;
+        xv = tv;
+        xe = te;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) {
+    float ov[8];
+    int oe[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      ov[p] = __shfl_xor(lv[p], o, 64);
+      oe[p] = __shfl_xor(le[p], o, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (gate_before(ov[7 - i], oe[7 - i], lv[i], le[i])) {
+        lv[i] = ov[7 - i];
+        le[i] = oe[7 - i];
+      }
+#pragma unroll
+    for (int dist = 4; dist > 0; dist >>= 1)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((i & dist) == 0 && gate_before(lv[i + dist], le[i + dist], lv[i], le[i])) {
+          const float tv = lv[i];
+          const int te = le[i];
+          lv[i] = lv[i + dist];
+          le[i] = le[i + dist];
+          lv[i + dist] = tv;
+          le[i + dist] = te;
+        }
+  }
+  float mv = lv[0];
+  int me = le[0];
+#pragma unroll
+  for (int p = 1; p < 8; ++p)
+    if (part == p) {
+      mv = lv[p];
+      me = le[p];
+    }
+  const double u = exp(static_cast<double>(mv) - static_cast<double>(lv[0]));
+  const int base = lane - part;
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += __shfl(u, base + j, 64);
+  if (part < k) {
+    out_ids[part] = me;
+    out_w[part] = static_cast<float>(u / sum);
+  }
+}
+
+// Router logits on the fp32 MFMA.  v_mfma_f32_16x16x4_f32 adds its four
+// products to the accumulator as four sequential fused multiply-adds, k = 0..3
+// in order (measured bit for bit on gfx950 against fmaf over 5 million
+// outputs, mixed magnitudes and subnormals), so a chain of these MFMAs over
+// hidden steps of four, ascending, is exactly the fixed fma order of every
+// logit.  Lane group lg of an operand therefore holds hidden index 4s + lg of
+// step s.
+//
+// Workgroup: 64 tokens x 16 TEF experts, 4 WS waves; wave w owns tokens
+// 16 (w % 4).. and TEF / WS fragments of 16 experts (the weight fragment is
+// MFMA operand A, so the accumulator is D[expert][token]: lane l holds experts
+// 4(l/16) + r of token l % 16).  Chunks of KB hidden elements are staged in
+// LDS as fp32, double-buffered: x rows as four groups (i mod 4) of KB/4
+// consecutive steps, so a lane reads four steps of its token with one 16-byte
+// load; gate_w in its own [i][e] order (row stride = 16 banks mod 32, so the
+// four lane groups' rows never collide).  The next chunk's global loads are
+// in flight while a chunk is multiplied.  With FUSE (one workgroup covers all
+// E <= 256 experts) the workgroup then runs the top-k of its 64 tokens.
+constexpr int kGateGroupPad = 4;  // floats of padding per x step group (LDS banks)
+
+template <int TEF, int KB>
+struct GateLds {
+  static constexpr int GS = KB / 4 + kGateGroupPad;  // floats per x step group
+  static constexpr int LDR = 4 * GS + 4;             // floats per staged x row
+  static constexpr int WE = 16 * TEF + 16;           // floats per staged gate_w row
+  static constexpr int BUF = 64 * LDR + KB * WE;     // floats per buffer
+};
+
+template <int TEF, int WS, int KB, bool BF16, bool FUSE>
+__global__ __launch_bounds__(256 * WS) void gate_kernel(const void* __restrict__ xv,
+                                                        const void* __restrict__ wv,
+                                                        const float* __restrict__ bias,
+                                                        float* __restrict__ logits,
+                                                        int32_t* __restrict__ ids,
+                                                        float* __restrict__ wts, int T, int d,
+                                                        int E, int k) {
+  using GL = GateLds<TEF, KB>;
+  constexpr int GS = GL::GS, LDR = GL::LDR, WE = GL::WE, BUF = GL::BUF;
+  constexpr int NT = 256 * WS;                       // threads
+  constexpr int XROWS = 64, WROWS = 16 * TEF, FPW = TEF / WS;
+  constexpr int EPC = BF16 ? 8 : 4;                  // elements per 16-byte load
+  constexpr int XCH = XROWS * (KB / EPC), WCH = KB * (WROWS / EPC);
+  constexpr int XR = (XCH + NT - 1) / NT, WR = (WCH + NT - 1) / NT;
+  static_assert(KB % 32 == 0 && WROWS % EPC == 0 && TEF % WS == 0, "chunk shape");
+  extern __shared__ __attribute__((aligned(16))) float gate_lds[];  // [2][BUF]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int tg = wave & 3, fr0 = (wave >> 2) * FPW;  // token group, first fragment
+  const int t0 = blockIdx.x * XROWS, e0 = blockIdx.y * WROWS;
+
+  u32x4 xr[XR], wr[WR];
+  bool wvec[WR];
+  // raw 16-byte pieces of chunk i0 (zero outside x / gate_w)
+  auto load = [&](int i0) {
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+      const int idx = tid + NT * r;
+      const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
+      const int t = t0 + tl, i = i0 + il;
+      xr[r] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < XCH && t < T && i < d) {
+        const size_t o = static_cast<size_t>(t) * d + i;
+        xr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xv) + o)
+                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(xv) + o);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int idx = tid + NT * r;
+      const int il = idx / (WROWS / EPC), el = (idx % (WROWS / EPC)) * EPC;
+      const int e = e0 + el, i = i0 + il;
+      wr[r] = u32x4{0u, 0u, 0u, 0u};
+      wvec[r] = idx < WCH && i < d && E % EPC == 0 && e + EPC <= E;
+      if (wvec[r]) {
+        const size_t o = static_cast<size_t>(i) * E + e;
+        wr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wv) + o)
+                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(wv) + o);
+      }
+    }
+  };
+  // widen to fp32 and store into buffer b
+  auto store = [&](int b, int i0) {
+    float* Lx = gate_lds + b * BUF;
+    float* Lw = Lx + 64 * LDR;
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+      const int idx = tid + NT * r;
+      if (idx < XCH) {
+        const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
+        float v[EPC];
+        if (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __uint_as_float(xr[r][q] << 16);
+            v[2 * q + 1] = __uint_as_float(xr[r][q] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(xr[r][q]);
+        }
+        float* row = Lx + tl * LDR;  // element i of the chunk at group i % 4, step i / 4
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) row[q % 4 * GS + (il + q) / 4] = v[q];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int idx = tid + NT * r;
+      if (idx < WCH) {
+        const int il = idx / (WROWS / EPC), el = (idx % (WROWS / EPC)) * EPC;
+        const int i = i0 + il;
+        float v[EPC];
+        if (wvec[r]) {
+          if (BF16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v[2 * q] = __uint_as_float(wr[r][q] << 16);
+              v[2 * q + 1] = __uint_as_float(wr[r][q] & 0xffff0000u);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(wr[r][q]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < EPC; ++q) {
+            const int eq = e0 + el + q;
+            float val = 0.0f;
+            if (i < d && eq < E) {
+              const size_t o = static_cast<size_t>(i) * E + eq;
+              val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])
+                         : static_cast<const float*>(wv)[o];
+            }
+            v[q] = val;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < EPC; q += 4)
+          *reinterpret_cast<f32x4*>(Lw + il * WE + el + q) =
+              f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
+      }
+    }
+  };
+
+  f32x4 acc[FPW];
+#pragma unroll
+  for (int f = 0; f < FPW; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int b, int i0) {
+    const float* Lx = gate_lds + b * BUF;
+    const float* xrow = Lx + (16 * tg + l16) * LDR + lg * GS;
+    const float* wcol = Lx + 64 * LDR + lg * WE + 16 * fr0 + l16;  // row 4s + lg
+    const int steps = min(KB, d - i0) / 4;  // d % 32 == 0: a multiple of 8
+    for (int s = 0; s < steps; s += 4) {
+      const f32x4 xb = *reinterpret_cast<const f32x4*>(xrow + s);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int f = 0; f < FPW; ++f)
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(wcol[4 * (s + u) * WE + 16 * f], xb[u],
+                                                        acc[f], 0, 0, 0);
+    }
+  };
+
+  load(0);
+  store(0, 0);
+  if (KB < d) load(KB);
+  __syncthreads();
+  int buf = 0;
+  for (int i0 = 0; i0 < d; i0 += KB) {
+    compute(buf, i0);
+    if (i0 + KB < d) {
+      store(buf ^ 1, i0 + KB);                 // the other buffer is free
+      if (i0 + 2 * KB < d) load(i0 + 2 * KB);  // in flight during the next chunk
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // logits (+ bias, one fp32 add) of this wave's 16 tokens x 16 FPW experts
+  const int t = t0 + 16 * tg + l16;
+  float* tile = gate_lds;  // FUSE: [64][E + 1] logits of the workgroup
+#pragma unroll
+  for (int f = 0; f < FPW; ++f) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + 16 * (fr0 + f) + 4 * lg + r;
+      if (e < E) {
+        float l = acc[f][r];
+        if (bias) l = l + bias[e];
+        if (t < T) logits[static_cast<size_t>(t) * E + e] = l;
+        if (FUSE) tile[(16 * tg + l16) * (E + 1) + e] = l;
+      }
+    }
+  }
+  if constexpr (FUSE) {
+    // top-k of the workgroup's 64 tokens, 4 WS consecutive lanes per token
+    constexpr int G = 4 * WS;
+    __syncthreads();
+    const int row = tid / G, tj = t0 + row;
+    if (tj < T)
+      topk_group<G>(tile + row * (E + 1), E, k, ids + static_cast<size_t>(tj) * k,
+                    wts + static_cast<size_t>(tj) * k, tid % G, lane);
   }
 }
 
 }  // namespace
 
-void launch_logits(const void* x, const void* gate_w, const float* bias, float* logits,
-                   int T, int d, int E, bool bf16, hipStream_t s) {
-  // Largest register blocking that still gives the chip >= 1024 workgroups
-  // (four per CU: the chains are latency-bound, measured) and does not leave
-  // most expert lanes idle.
-  struct Cfg {
-    int rt, re, tyl, txl;
-  };
-  // KB (hidden chunk per LDS tile) is 64 for the most blocked shapes (more
-  // FMAs per chunk) and 128 otherwise, so a chunk's FMAs cover the global
-  // load latency of the next one.
-  static constexpr Cfg cfgs[] = {{8, 4, 16, 16}, {4, 4, 16, 16}, {2, 4, 32, 8},
-                                 {2, 2, 16, 16}, {1, 2, 32, 8},  {1, 1, 16, 16}};
-  int pick = 5;
-  for (int c = 0; c < 5; ++c) {
-    const int TT = cfgs[c].tyl * cfgs[c].rt, TE = cfgs[c].txl * cfgs[c].re;
-    const long long wgs = static_cast<long long>((T + TT - 1) / TT) * ((E + TE - 1) / TE);
-    if (TE <= E && wgs >= 1024) {  // four or more workgroups per CU
-      pick = c;
-      break;
-    }
-  }
-  auto go = [&](auto kern, int TT, int TE, int KB) {
-    dim3 grid((T + TT - 1) / TT, (E + TE - 1) / TE);
-    const size_t lds = sizeof(float) * static_cast<size_t>(TT + TE) * (KB + kRoutePad);
-    kern<<<grid, 256, lds, s>>>(x, gate_w, bias, logits, T, d, E);
-  };
-#define MOE_L(C, RT, RE, TYL, TXL, KB)                                                    \
-  if (pick == C) {                                                                        \
-    if (bf16)                                                                             \
-      go(logits_kernel<RT, RE, TYL, TXL, KB, true>, TYL * RT, TXL * RE, KB);              \
-    else                                                                                  \
-      go(logits_kernel<RT, RE, TYL, TXL, KB, false>, TYL * RT, TXL * RE, KB);             \
-    return;                                                                               \
-  }
-  MOE_L(0, 8, 4, 16, 16, 64)
-  MOE_L(1, 4, 4, 16, 16, 64)
-  MOE_L(2, 2, 4, 32, 8, 128)
-  MOE_L(3, 2, 2, 16, 16, 128)
-  MOE_L(4, 1, 2, 32, 8, 128)
-  MOE_L(5, 1, 1, 16, 16, 128)
-#undef MOE_L
-}
-
 void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
                  hipStream_t s) {
   topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, T, E, k);
+}
+
+// Gate: logits on the MFMA, then top-k -- inside the same workgroup when one
+// workgroup covers every expert (E <= 256), k <= 8 and the tokens alone give
+// the chip >= 1024 waves; otherwise experts are split across workgroups (as many
+// fragments per wave as still give >= 1024 waves) and a top-k kernel follows.
+// Two waves share each token group where the fragments allow, so that one
+// wave's staging overlaps the other's MFMAs.  d % 32 == 0.
+void launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
+                 int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s) {
+  if (T <= 0) return;
+  const long long tw = (T + 15) / 16;  // token waves
+  const int ef = (E + 15) / 16;        // expert fragments
+  int tef = 1;
+  bool fuse = ef <= 16 && tw >= 1024 && k <= 8;
+  if (fuse) {
+    tef = ef <= 1 ? 1 : ef <= 2 ? 2 : ef <= 4 ? 4 : ef <= 8 ? 8 : 16;
+    if (tef == 1 && k > 4) fuse = false;  // 4 lanes per token with one wave per group
+  }
+  if (!fuse) {
+    tef = 1;
+    for (int c : {4, 2}) {
+      if (c <= ef && tw * ((ef + c - 1) / c) >= 1024) {
+        tef = c;
+        break;
+      }
+    }
+  }
+  auto go = [&](auto kern, int TEF, int WS, int KB, bool fused) {
+    dim3 grid((T + 63) / 64, fused ? 1 : (E + 16 * TEF - 1) / (16 * TEF));
+    size_t lds = sizeof(float) * 2 *
+                 static_cast<size_t>(64 * (4 * (KB / 4 + kGateGroupPad) + 4) + KB * (16 * TEF + 16));
+    if (fused) lds = std::max(lds, sizeof(float) * 64 * static_cast<size_t>(E + 1));
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        160 * 1024);  // once per kernel: every configuration fits in 160 KB
+    (void)attr;
+    kern<<<grid, 256 * WS, lds, s>>>(x, gate_w, bias, logits, ids, w, T, d, E, k);
+  };
+#define MOE_G(TEF_, WS_, KB_)                                                             \
+  if (tef == TEF_) {                                                                      \
+    if (fuse) {                                                                           \
+      if (bf16) go(gate_kernel<TEF_, WS_, KB_, true, true>, TEF_, WS_, KB_, true);        \
+      else go(gate_kernel<TEF_, WS_, KB_, false, true>, TEF_, WS_, KB_, true);            \
+    } else {                                                                              \
+      if (bf16) go(gate_kernel<TEF_, WS_, KB_, true, false>, TEF_, WS_, KB_, false);      \
+      else go(gate_kernel<TEF_, WS_, KB_, false, false>, TEF_, WS_, KB_, false);          \
+    }                                                                                     \
+  }
+  MOE_G(1, 1, 128)
+  MOE_G(2, 2, 128)
+  MOE_G(4, 2, 64)
+  MOE_G(8, 2, 64)
+  MOE_G(16, 2, 32)
+#undef MOE_G
+  if (!fuse) launch_topk(logits, ids, w, T, E, k, s);
 }
 
 }  // namespace moe

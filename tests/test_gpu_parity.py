@@ -56,6 +56,25 @@ def test_route_bit_exact(name):
     assert f32_ulps(w.cpu().numpy(), ref_w) <= 4
 
 
+@pytest.mark.parametrize("E,k,act", [(20, 1, BF16), (32, 2, BF16), (40, 3, F32),
+                                     (256, 8, BF16), (200, 5, BF16), (256, 9, BF16)])
+def test_route_large_T_bit_exact(E, k, act):
+    # T >= 16384: the gate runs the top-k inside the logits workgroup when
+    # E <= 256 and k <= 8 (and a separate top-k kernel otherwise); duplicated
+    # gate columns make exact logit ties, which must go to the lower index
+    cfg = MoEConfig("route_T", 16400, 128, 128, E, k, act, act, act)
+    say("route large T", E, k, act)
+    inp = gpu_inputs(cfg)
+    inp["gate_w"][:, 7] = inp["gate_w"][:, 3]
+    inp["gate_w"][:, E - 1] = inp["gate_w"][:, 0]
+    logits, ids, w = gpu_route(cfg, inp)
+    ref_l, ref_ids, ref_w = oracle_route_rows(cfg, inp, np.arange(cfg.T))
+    assert np.array_equal(logits.cpu().numpy(), ref_l)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert f32_ulps(w.cpu().numpy(), ref_w) <= 4
+    assert (ref_ids == 3).any() and not ((ref_ids == 7) & ~(ref_ids == 3).any(1)[:, None]).any()
+
+
 @pytest.mark.parametrize("name", list(REDUCED))
 @pytest.mark.parametrize("block_m", [0, 16, 128])
 def test_permute_bit_exact(name, block_m):
