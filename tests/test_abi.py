@@ -82,3 +82,33 @@ def test_null_pointers_rejected_before_launch():
     rc = lib.moe_pack_weight(1, 4, 4, 3, None, None, None)
     assert rc == 1
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value > 0
+
+
+def test_mxfp4_sizes():
+    # FP4 codes are half a byte per weight; MX FP8 x / h take one byte per
+    # element plus one E8M0 byte per 32
+    _lib()
+    p = B.problem(1024, 512, 256, 8, 2, 1, B.MOE_MXFP4, 1)
+    assert B.weight_bytes(p) == 8 * 512 * 256 // 2
+    bf = B.problem(1024, 512, 256, 8, 2, 1, 1, 1)
+    assert B.workspace_size(p) != B.workspace_size(bf)
+    for bad in (B.problem(16, 96, 256, 8, 2, 1, B.MOE_MXFP4, 1),     # d % 128
+                B.problem(16, 128, 192, 8, 2, 1, B.MOE_MXFP4, 1)):   # f % 128
+        lib = _lib()
+        rc = lib.moe_forward(ctypes.byref(bad), None, None, None, None, None, None, None, None,
+                             None, None, None, 0, None, None)
+        assert rc == 2  # valid, but not a supported shape
+    with pytest.raises(B.MoEError) as e:  # MXFP4 weights need bf16 activations
+        B.workspace_size(B.problem(16, 128, 128, 8, 2, 0, B.MOE_MXFP4, 0))
+    assert e.value.code == 1
+
+
+def test_route_shape_rule():
+    # the gate runs hidden chunks of 32: other d are unsupported, reported
+    # before any pointer is looked at or any kernel launched
+    lib = _lib()
+    p = B.problem(4, 48, 64, 4, 2, 1, 1, 1)
+    rc = lib.moe_route(ctypes.byref(p), None, None, None, None, None, None, None, 0, None)
+    assert rc == 2
+    rc = lib.moe_quantize_mx(4, 40, None, None, None, None)  # cols % 32
+    assert rc == 1
