@@ -371,3 +371,35 @@ def test_abi_errors_launch_nothing():
     assert e.value.code == 1
     torch.cuda.synchronize()
     assert (out.float() == 7.0).all()  # nothing was written
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16_r", "decode_bf16_r", "prefill_mxfp4_r"])
+def test_forward_graph_replay(name):
+    # moe_forward reads no size back to the host, so it can be captured into
+    # a HIP graph; every replay (with eager work and synchronisations in
+    # between) must reproduce the eager output bit for bit
+    cfg = REDUCED[name]
+    say("graph", name)
+    inp = gpu_inputs(cfg)
+    packed = B.pack_weights(inp)
+    p = B.problem_of(cfg)
+    ws = B.alloc_workspace(p)
+    out = B.out_tensor(cfg)
+    ref = B.forward(cfg, inp, packed, out=torch.empty_like(out), ws=torch.empty_like(ws))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        B.forward(cfg, inp, packed, out=out, ws=ws, stream=s)  # warm-up on the capture stream
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            B.forward(cfg, inp, packed, out=out, ws=ws, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(0)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), (name, rep)
+        del junk
