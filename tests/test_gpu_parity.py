@@ -56,14 +56,16 @@ def test_route_bit_exact(name):
     assert f32_ulps(w.cpu().numpy(), ref_w) <= 4
 
 
-@pytest.mark.parametrize("E,k,act", [(20, 1, BF16), (32, 2, BF16), (40, 3, F32),
-                                     (256, 8, BF16), (200, 5, BF16), (256, 9, BF16)])
-def test_route_large_T_bit_exact(E, k, act):
+@pytest.mark.parametrize("E,k,act,d", [(20, 1, BF16, 128), (32, 2, BF16, 128), (40, 3, F32, 128),
+                                       (256, 8, BF16, 128), (200, 5, BF16, 128),
+                                       (256, 9, BF16, 128), (32, 2, BF16, 160), (256, 8, BF16, 96)])
+def test_route_large_T_bit_exact(E, k, act, d):
     # T >= 16384: the gate runs the top-k inside the logits workgroup when
     # E <= 256 and k <= 8 (and a separate top-k kernel otherwise); duplicated
-    # gate columns make exact logit ties, which must go to the lower index
-    cfg = MoEConfig("route_T", 16400, 128, 128, E, k, act, act, act)
-    say("route large T", E, k, act)
+    # gate columns make exact logit ties, which must go to the lower index;
+    # d = 160 and 96 end on a partial hidden chunk
+    cfg = MoEConfig("route_T", 16400, d, 128, E, k, act, act, act)
+    say("route large T", E, k, act, d)
     inp = gpu_inputs(cfg)
     inp["gate_w"][:, 7] = inp["gate_w"][:, 3]
     inp["gate_w"][:, E - 1] = inp["gate_w"][:, 0]
