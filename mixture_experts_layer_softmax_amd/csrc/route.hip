@@ -192,8 +192,8 @@ __device__ __forceinline__ void topk_group(const float* row, int E, int k, int32
 // logit.  Lane group lg of an operand therefore holds hidden index 4s + lg of
 // step s.
 //
-// Workgroup: 64 tokens x 16 TEF experts, 4 WS waves; wave w owns tokens
-// 16 (w % 4).. and TEF / WS fragments of 16 experts (the weight fragment is
+// Workgroup: 16 TG tokens x 16 TEF experts, TG WS waves; wave w owns tokens
+// 16 (w % TG).. and TEF / WS fragments of 16 experts (the weight fragment is
 // MFMA operand A, so the accumulator is D[expert][token]: lane l holds experts
 // 4(l/16) + r of token l % 16).  Chunks of KB hidden elements are staged in
 // LDS as fp32, double-buffered: x rows as four groups (i mod 4) of KB/4
@@ -204,26 +204,26 @@ __device__ __forceinline__ void topk_group(const float* row, int E, int k, int32
 // E <= 256 experts) the workgroup then runs the top-k of its 64 tokens.
 constexpr int kGateGroupPad = 4;  // floats of padding per x step group (LDS banks)
 
-template <int TEF, int KB>
+template <int TEF, int KB, int TG>
 struct GateLds {
   static constexpr int GS = KB / 4 + kGateGroupPad;  // floats per x step group
   static constexpr int LDR = 4 * GS + 4;             // floats per staged x row
   static constexpr int WE = 16 * TEF + 16;           // floats per staged gate_w row
-  static constexpr int BUF = 64 * LDR + KB * WE;     // floats per buffer
+  static constexpr int BUF = 16 * TG * LDR + KB * WE;  // floats per buffer
 };
 
-template <int TEF, int WS, int KB, bool BF16, bool FUSE>
-__global__ __launch_bounds__(256 * WS) void gate_kernel(const void* __restrict__ xv,
+template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE>
+__global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restrict__ xv,
                                                         const void* __restrict__ wv,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ logits,
                                                         int32_t* __restrict__ ids,
                                                         float* __restrict__ wts, int T, int d,
                                                         int E, int k) {
-  using GL = GateLds<TEF, KB>;
+  using GL = GateLds<TEF, KB, TG>;
   constexpr int GS = GL::GS, LDR = GL::LDR, WE = GL::WE, BUF = GL::BUF;
-  constexpr int NT = 256 * WS;                       // threads
-  constexpr int XROWS = 64, WROWS = 16 * TEF, FPW = TEF / WS;
+  constexpr int NT = 64 * TG * WS;                   // threads
+  constexpr int XROWS = 16 * TG, WROWS = 16 * TEF, FPW = TEF / WS;
   constexpr int EPC = BF16 ? 8 : 4;                  // elements per 16-byte load
   constexpr int XCH = XROWS * (KB / EPC), WCH = KB * (WROWS / EPC);
   constexpr int XR = (XCH + NT - 1) / NT, WR = (WCH + NT - 1) / NT;
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256 * WS) void gate_kernel(const void* __restrict__
   extern __shared__ __attribute__((aligned(16))) float gate_lds[];  // [2][BUF]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int tg = wave & 3, fr0 = (wave >> 2) * FPW;  // token group, first fragment
+  const int tg = wave % TG, fr0 = (wave / TG) * FPW;  // token group, first fragment
   const int t0 = blockIdx.x * XROWS, e0 = blockIdx.y * WROWS;
 
   u32x4 xr[XR], wr[WR];
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256 * WS) void gate_kernel(const void* __restrict__
   // widen to fp32 and store into buffer b
   auto store = [&](int b, int i0) {
     float* Lx = gate_lds + b * BUF;
-    float* Lw = Lx + 64 * LDR;
+    float* Lw = Lx + XROWS * LDR;
 #pragma unroll
     for (int r = 0; r < XR; ++r) {
       const int idx = tid + NT * r;
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256 * WS) void gate_kernel(const void* __restrict__
   auto compute = [&](int b, int i0) {
     const float* Lx = gate_lds + b * BUF;
     const float* xrow = Lx + (16 * tg + l16) * LDR + lg * GS;
-    const float* wcol = Lx + 64 * LDR + lg * WE + 16 * fr0 + l16;  // row 4s + lg
+    const float* wcol = Lx + XROWS * LDR + lg * WE + 16 * fr0 + l16;  // row 4s + lg
     const int steps = min(KB, d - i0) / 4;  // d % 32 == 0: a multiple of 8
     for (int s = 0; s < steps; s += 4) {
       const f32x4 xb = *reinterpret_cast<const f32x4*>(xrow + s);
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256 * WS) void gate_kernel(const void* __restrict__
 
   // logits (+ bias, one fp32 add) of this wave's 16 tokens x 16 FPW experts
   const int t = t0 + 16 * tg + l16;
-  float* tile = gate_lds;  // FUSE: [64][E + 1] logits of the workgroup
+  float* tile = gate_lds;  // FUSE: [16 TG][E + 1] logits of the workgroup
 #pragma unroll
   for (int f = 0; f < FPW; ++f) {
 #pragma unroll
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256 * WS) void gate_kernel(const void* __restrict__
     }
   }
   if constexpr (FUSE) {
-    // top-k of the workgroup's 64 tokens, 4 WS consecutive lanes per token
+    // top-k of the workgroup's tokens, 4 WS consecutive lanes per token
     constexpr int G = 4 * WS;
     __syncthreads();
     const int row = tid / G, tj = t0 + row;
@@ -423,32 +423,35 @@ void launch_gate(const void* x, const void* gate_w, const float* bias, float* lo
       }
     }
   }
-  auto go = [&](auto kern, int TEF, int WS, int KB, bool fused) {
-    dim3 grid((T + 63) / 64, fused ? 1 : (E + 16 * TEF - 1) / (16 * TEF));
+  auto go = [&](auto kern, int TEF, int WS, int KB, int TG, bool fused) {
+    dim3 grid((T + 16 * TG - 1) / (16 * TG), fused ? 1 : (E + 16 * TEF - 1) / (16 * TEF));
     size_t lds = sizeof(float) * 2 *
-                 static_cast<size_t>(64 * (4 * (KB / 4 + kGateGroupPad) + 4) + KB * (16 * TEF + 16));
-    if (fused) lds = std::max(lds, sizeof(float) * 64 * static_cast<size_t>(E + 1));
+                 static_cast<size_t>(16 * TG * (4 * (KB / 4 + kGateGroupPad) + 4) +
+                                     KB * (16 * TEF + 16));
+    if (fused) lds = std::max(lds, sizeof(float) * 16 * TG * static_cast<size_t>(E + 1));
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         160 * 1024);  // once per kernel: every configuration fits in 160 KB
     (void)attr;
-    kern<<<grid, 256 * WS, lds, s>>>(x, gate_w, bias, logits, ids, w, T, d, E, k);
+    kern<<<grid, 64 * TG * WS, lds, s>>>(x, gate_w, bias, logits, ids, w, T, d, E, k);
   };
-#define MOE_G(TEF_, WS_, KB_)                                                             \
+  // (TEF, WS, KB, TG): the widest expert tiles stage 128 tokens per
+  // workgroup, which halves the gate_w traffic per token
+#define MOE_G(TEF_, WS_, KB_, TG_)                                                        \
   if (tef == TEF_) {                                                                      \
     if (fuse) {                                                                           \
-      if (bf16) go(gate_kernel<TEF_, WS_, KB_, true, true>, TEF_, WS_, KB_, true);        \
-      else go(gate_kernel<TEF_, WS_, KB_, false, true>, TEF_, WS_, KB_, true);            \
+      if (bf16) go(gate_kernel<TEF_, WS_, KB_, TG_, true, true>, TEF_, WS_, KB_, TG_, true); \
+      else go(gate_kernel<TEF_, WS_, KB_, TG_, false, true>, TEF_, WS_, KB_, TG_, true);  \
     } else {                                                                              \
-      if (bf16) go(gate_kernel<TEF_, WS_, KB_, true, false>, TEF_, WS_, KB_, false);      \
-      else go(gate_kernel<TEF_, WS_, KB_, false, false>, TEF_, WS_, KB_, false);          \
+      if (bf16) go(gate_kernel<TEF_, WS_, KB_, TG_, true, false>, TEF_, WS_, KB_, TG_, false); \
+      else go(gate_kernel<TEF_, WS_, KB_, TG_, false, false>, TEF_, WS_, KB_, TG_, false); \
     }                                                                                     \
   }
-  MOE_G(1, 1, 128)
-  MOE_G(2, 2, 128)
-  MOE_G(4, 2, 64)
-  MOE_G(8, 2, 64)
-  MOE_G(16, 2, 32)
+  MOE_G(1, 1, 128, 4)
+  MOE_G(2, 2, 128, 4)
+  MOE_G(4, 2, 64, 4)
+  MOE_G(8, 2, 64, 4)
+  MOE_G(16, 2, 32, 8)
 #undef MOE_G
   if (!fuse) launch_topk(logits, ids, w, T, E, k, s);
 }
