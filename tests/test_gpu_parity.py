@@ -405,3 +405,37 @@ def test_forward_graph_replay(name):
         torch.cuda.synchronize()
         assert torch.equal(out, ref), (name, rep)
         del junk
+
+
+def _random_configs(n=40, seed=1234):
+    """Seeded random small layers over the supported space: dtype, E, k,
+    hidden sizes (multiples of the dtype's contraction row), T, bias, shared
+    experts and tile height."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        wdt = [F32, BF16, FP8, MXFP4][i % 4]
+        act = F32 if wdt == F32 else BF16
+        m = {F32: 32, BF16: 64, FP8: 128, MXFP4: 128}[wdt]
+        E = int(rng.choice([1, 2, 3, 7, 16, 33, 64, 130]))
+        k = int(rng.integers(1, min(E, 9) + 1))
+        d = m * int(rng.integers(1, 5))
+        f = m * int(rng.integers(1, 4))
+        T = int(rng.choice([1, 5, 63, 64, 65, 200, 513]))
+        cfg = MoEConfig(f"rand{i}", T, d, f, E, k, act, wdt, act, skew_bias=bool(rng.integers(0, 2)),
+                        seed=i, n_shared=int(rng.choice([0, 0, 1, 2])))
+        out.append((cfg, int(rng.choice([0, 16, 32, 64, 128, 256]))))
+    return out
+
+
+@pytest.mark.parametrize("cfg,block_m", _random_configs(), ids=lambda v: getattr(v, "name", str(v)))
+def test_random_config_parity(cfg, block_m):
+    say("random", cfg, block_m)
+    inp = gpu_inputs(cfg)
+    n = cfg.T * cfg.k
+    dbg = {"topk_ids": torch.empty(n, dtype=torch.int32, device="cuda")}
+    ref, ref_ids, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
+    out = _forward(cfg, inp, out_dtype=F32, block_m=block_m, dbg=dbg)
+    assert np.array_equal(dbg["topk_ids"].view(cfg.T, cfg.k).cpu().numpy(), ref_ids)
+    _outputs_ok(cfg, out, ref, f"fp32 out bm={block_m}")
+    _outputs_ok(cfg, _forward(cfg, inp, block_m=block_m), ref, "native out")
