@@ -7,6 +7,8 @@
 // back through the per-slot source record (MegaMoE-vs-MoE-systems page,
 // section 2.4).  Each output element has exactly one writer, so there are no
 // floating-point atomics and the result is bitwise reproducible.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -14,42 +16,79 @@ namespace moe {
 
 namespace {
 
-// One workgroup per token row; each thread owns 4 consecutive columns.
+// One workgroup per token row; each thread owns 8 consecutive columns (two
+// 16-byte pieces) per pass, so d must be a multiple of 8 (the forward's shape
+// rule already asks for 32).  The launch sizes the workgroup to d/8 lanes
+// (up to 1024), so rows up to 8192 wide take one pass with no idle tail.  The slots are read in groups of up to 8 whose
+// loads are all issued before their fmas, so more Y bytes are in flight per
+// CU; the accumulation itself stays j ascending, then the shared experts.
+constexpr int kCombineGroup = 8;
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
+__global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ Y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ token_slot,
                                                       void* __restrict__ out, int T, int d, int k,
                                                       int S) {
   const int t = blockIdx.x;
-  __shared__ int32_t s_slot[1024];
-  __shared__ float s_w[1024];
-  for (int j = threadIdx.x; j < k; j += 256) {
-    s_slot[j] = token_slot[static_cast<size_t>(t) * k + j];
-    s_w[j] = w[static_cast<size_t>(t) * k + j];
+  __shared__ int32_t s_slot[1024 + 8];
+  __shared__ float s_w[1024 + 8];
+  const int n = k + S;  // terms: k routed (weight w), then S shared (weight 1)
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    if (j < k) {
+      s_slot[j] = token_slot[static_cast<size_t>(t) * k + j];
+      s_w[j] = w[static_cast<size_t>(t) * k + j];
+    } else {
+      s_slot[j] = static_cast<int32_t>(static_cast<int64_t>(T) * k +
+                                       static_cast<int64_t>(j - k) * T + t);
+      s_w[j] = 1.0f;
+    }
   }
   __syncthreads();
-  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const f32x4 y = *reinterpret_cast<const f32x4*>(Y + static_cast<size_t>(s_slot[j]) * d + c);
-      const float g = s_w[j];
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < n; j0 += kCombineGroup) {
+      f32x4 y0[kCombineGroup], y1[kCombineGroup];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(g, y[r], acc[r]);
-    }
-    for (int sh = 0; sh < S; ++sh) {
-      const size_t slot = static_cast<size_t>(T) * k + static_cast<size_t>(sh) * T + t;
-      const f32x4 y = *reinterpret_cast<const f32x4*>(Y + slot * d + c);
+      for (int u = 0; u < kCombineGroup; ++u) {
+        if (j0 + u < n) {
+          const float* row = Y + static_cast<size_t>(s_slot[j0 + u]) * d + c;
+          y0[u] = *reinterpret_cast<const f32x4*>(row);
+          y1[u] = *reinterpret_cast<const f32x4*>(row + 4);
+        }
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] += y[r];
+      for (int u = 0; u < kCombineGroup; ++u) {
+        if (j0 + u < n) {
+          const int j = j0 + u;
+          if (j < k) {
+            const float g = s_w[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              a0[r] = __builtin_fmaf(g, y0[u][r], a0[r]);
+              a1[r] = __builtin_fmaf(g, y1[u][r], a1[r]);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              a0[r] += y0[u][r];
+              a1[r] += y1[u][r];
+            }
+          }
+        }
+      }
     }
     if (OUT_BF16) {
-      uint2 v;
-      v.x = f32_to_bf16_rne(acc[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[1])) << 16);
-      v.y = f32_to_bf16_rne(acc[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[3])) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + static_cast<size_t>(t) * d + c) = v;
+      uint16_t* o = static_cast<uint16_t*>(out) + static_cast<size_t>(t) * d + c;
+      auto pk = [](float lo, float hi) {
+        return f32_to_bf16_rne(lo) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+      };
+      *reinterpret_cast<uint4*>(o) =
+          uint4{pk(a0[0], a0[1]), pk(a0[2], a0[3]), pk(a1[0], a1[1]), pk(a1[2], a1[3])};
     } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + static_cast<size_t>(t) * d + c) = acc;
+      float* o = static_cast<float*>(out) + static_cast<size_t>(t) * d + c;
+      *reinterpret_cast<f32x4*>(o) = a0;
+      *reinterpret_cast<f32x4*>(o + 4) = a1;
     }
   }
 }
@@ -59,10 +98,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 void launch_combine(const float* Y, const float* w, const int32_t* token_slot, void* out,
                     int T, int d, int k, int S, bool out_bf16, hipStream_t s) {
   if (T <= 0) return;
+  const int threads = std::min(1024, std::max(64, (d / 8 + 63) / 64 * 64));
   if (out_bf16)
-    combine_kernel<true><<<T, 256, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
+    combine_kernel<true><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
   else
-    combine_kernel<false><<<T, 256, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
+    combine_kernel<false><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
 }
 
 }  // namespace moe
