@@ -84,8 +84,10 @@ struct Geo {
   static constexpr int STAGE = BM * KRB + BN * KRBW + SCALE_BYTES;
   static constexpr int RED = (DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0;
   static constexpr int NS0 = (kLdsBytes - RED) / STAGE;
-  // small tiles (decode: HBM bound) keep more stages in flight
-  static constexpr int NS_CAP = BM <= 32 ? 8 : 6;
+  // small tiles (decode: HBM bound) keep more stages in flight; 16-row MX
+  // tiles are small enough that two workgroups of 4 stages share a CU, which
+  // streams better than one of 8 (one refills while the other starts a task)
+  static constexpr int NS_CAP = BM <= 32 ? ((MX && BM == 16) ? 4 : 8) : 6;
   static constexpr int NS = NS0 > NS_CAP ? NS_CAP : NS0;
   static constexpr int EPI =  // output staging, one pass per wave row
       (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : 4);
