@@ -236,95 +236,100 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
 
   u32x4 xr[XR], wr[WR];
   bool wvec[WR];
-  // raw 16-byte pieces of chunk i0 (zero outside x / gate_w)
-  auto load = [&](int i0) {
-#pragma unroll
-    for (int r = 0; r < XR; ++r) {
-      const int idx = tid + NT * r;
-      const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
-      const int t = t0 + tl, i = i0 + il;
-      xr[r] = u32x4{0u, 0u, 0u, 0u};
-      if (idx < XCH && t < T && i < d) {
-        const size_t o = static_cast<size_t>(t) * d + i;
-        xr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xv) + o)
-                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(xv) + o);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < WR; ++r) {
-      const int idx = tid + NT * r;
-      const int il = idx / (WROWS / EPC), el = (idx % (WROWS / EPC)) * EPC;
-      const int e = e0 + el, i = i0 + il;
-      wr[r] = u32x4{0u, 0u, 0u, 0u};
-      wvec[r] = idx < WCH && i < d && E % EPC == 0 && e + EPC <= E;
-      if (wvec[r]) {
-        const size_t o = static_cast<size_t>(i) * E + e;
-        wr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wv) + o)
-                     : *reinterpret_cast<const u32x4*>(static_cast<const float*>(wv) + o);
-      }
+  // raw 16-byte piece r of chunk i0 (zero outside x / gate_w)
+  auto load_x = [&](int i0, int r) {
+    const int idx = tid + NT * r;
+    const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
+    const int t = t0 + tl, i = i0 + il;
+    xr[r] = u32x4{0u, 0u, 0u, 0u};
+    if (idx < XCH && t < T && i < d) {
+      const size_t o = static_cast<size_t>(t) * d + i;
+      xr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xv) + o)
+                   : *reinterpret_cast<const u32x4*>(static_cast<const float*>(xv) + o);
     }
   };
-  // widen to fp32 and store into buffer b
-  auto store = [&](int b, int i0) {
+  auto load_w = [&](int i0, int r) {
+    const int idx = tid + NT * r;
+    const int il = idx / (WROWS / EPC), el = (idx % (WROWS / EPC)) * EPC;
+    const int e = e0 + el, i = i0 + il;
+    wr[r] = u32x4{0u, 0u, 0u, 0u};
+    wvec[r] = idx < WCH && i < d && E % EPC == 0 && e + EPC <= E;
+    if (wvec[r]) {
+      const size_t o = static_cast<size_t>(i) * E + e;
+      wr[r] = BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wv) + o)
+                   : *reinterpret_cast<const u32x4*>(static_cast<const float*>(wv) + o);
+    }
+  };
+  // widen piece r to fp32 and store it into buffer b
+  auto store_x = [&](int b, int r) {
     float* Lx = gate_lds + b * BUF;
-    float* Lw = Lx + XROWS * LDR;
+    const int idx = tid + NT * r;
+    if (idx < XCH) {
+      const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
+      float v[EPC];
+      if (BF16) {
 #pragma unroll
-    for (int r = 0; r < XR; ++r) {
-      const int idx = tid + NT * r;
-      if (idx < XCH) {
-        const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
-        float v[EPC];
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = __uint_as_float(xr[r][q] << 16);
+          v[2 * q + 1] = __uint_as_float(xr[r][q] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(xr[r][q]);
+      }
+      float* row = Lx + tl * LDR;  // element i of the chunk at group i % 4, step i / 4
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) row[q % 4 * GS + (il + q) / 4] = v[q];
+    }
+  };
+  auto store_w = [&](int b, int i0, int r) {
+    float* Lw = gate_lds + b * BUF + XROWS * LDR;
+    const int idx = tid + NT * r;
+    if (idx < WCH) {
+      const int il = idx / (WROWS / EPC), el = (idx % (WROWS / EPC)) * EPC;
+      const int i = i0 + il;
+      float v[EPC];
+      if (wvec[r]) {
         if (BF16) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            v[2 * q] = __uint_as_float(xr[r][q] << 16);
-            v[2 * q + 1] = __uint_as_float(xr[r][q] & 0xffff0000u);
+            v[2 * q] = __uint_as_float(wr[r][q] << 16);
+            v[2 * q + 1] = __uint_as_float(wr[r][q] & 0xffff0000u);
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(xr[r][q]);
+          for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(wr[r][q]);
         }
-        float* row = Lx + tl * LDR;  // element i of the chunk at group i % 4, step i / 4
+      } else {
 #pragma unroll
-        for (int q = 0; q < EPC; ++q) row[q % 4 * GS + (il + q) / 4] = v[q];
+        for (int q = 0; q < EPC; ++q) {
+          const int eq = e0 + el + q;
+          float val = 0.0f;
+          if (i < d && eq < E) {
+            const size_t o = static_cast<size_t>(i) * E + eq;
+            val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])
+                       : static_cast<const float*>(wv)[o];
+          }
+          v[q] = val;
+        }
       }
+#pragma unroll
+      for (int q = 0; q < EPC; q += 4)
+        *reinterpret_cast<f32x4*>(Lw + il * WE + el + q) =
+            f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
     }
-#pragma unroll
-    for (int r = 0; r < WR; ++r) {
-      const int idx = tid + NT * r;
-      if (idx < WCH) {
-        const int il = idx / (WROWS / EPC), el = (idx % (WROWS / EPC)) * EPC;
-        const int i = i0 + il;
-        float v[EPC];
-        if (wvec[r]) {
-          if (BF16) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[2 * q] = __uint_as_float(wr[r][q] << 16);
-              v[2 * q + 1] = __uint_as_float(wr[r][q] & 0xffff0000u);
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < EPC; ++q) v[q] = __uint_as_float(wr[r][q]);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < EPC; ++q) {
-            const int eq = e0 + el + q;
-            float val = 0.0f;
-            if (i < d && eq < E) {
-              const size_t o = static_cast<size_t>(i) * E + eq;
-              val = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(wv)[o])
-                         : static_cast<const float*>(wv)[o];
-            }
-            v[q] = val;
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < EPC; q += 4)
-          *reinterpret_cast<f32x4*>(Lw + il * WE + el + q) =
-              f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
-      }
+  };
+  // piece p of the staging (x pieces, then gate_w pieces): store the loaded
+  // piece of chunk i0 into buffer b, then (if i2 < d) load the same piece of
+  // chunk i2 into the registers it frees
+  constexpr int NP = XR + WR;
+  auto stage = [&](int p, int b, int i0, int i2) {
+    if (p < XR) {
+      store_x(b, p);
+      if (i2 < d) load_x(i2, p);
+    } else {
+      store_w(b, i0, p - XR);
+      if (i2 < d) load_w(i2, p - XR);
     }
   };
 
@@ -332,33 +337,87 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
 #pragma unroll
   for (int f = 0; f < FPW; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int b, int i0) {
+  // the MFMA chain over chunk i0 in buffer b, four steps at a time.  With up
+  // to four fragments per wave, the LDS operands of the next four steps are
+  // read before the MFMAs of the current ones, so their latency hides behind
+  // the chain, and when the chunk is full and another follows, the staging
+  // of chunk i0 + KB into buffer b ^ 1 (with the loads of chunk i0 + 2 KB) is
+  // spread over the chain, one piece after each four steps, where it issues
+  // while the next MFMA waits for the previous result.  Eight fragments
+  // (eight independent chains per wave) have no registers for a second
+  // operand set; their staging follows the chain.
+  struct Ops {
+    f32x4 x;
+    float w[4][FPW];
+  };
+  auto compute = [&](int b, int i0, bool staged) {
+    const int i2 = i0 + 2 * KB;  // chunk loaded into the registers staging frees
     const float* Lx = gate_lds + b * BUF;
     const float* xrow = Lx + (16 * tg + l16) * LDR + lg * GS;
     const float* wcol = Lx + XROWS * LDR + lg * WE + 16 * fr0 + l16;  // row 4s + lg
-    const int steps = min(KB, d - i0) / 4;  // d % 32 == 0: a multiple of 8
-    for (int s = 0; s < steps; s += 4) {
-      const f32x4 xb = *reinterpret_cast<const f32x4*>(xrow + s);
+    auto ops = [&](int s, Ops& o) {
+      o.x = *reinterpret_cast<const f32x4*>(xrow + s);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int f = 0; f < FPW; ++f) o.w[u][f] = wcol[4 * (s + u) * WE + 16 * f];
+    };
+    auto mm = [&](const Ops& o) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int f = 0; f < FPW; ++f)
-          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(wcol[4 * (s + u) * WE + 16 * f], xb[u],
-                                                        acc[f], 0, 0, 0);
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.w[u][f], o.x[u], acc[f], 0, 0, 0);
+    };
+    Ops o0, o1;
+    if (FPW >= 8) {  // two operand sets would not fit in the registers
+      const int steps = min(KB, d - i0) / 4;
+      for (int s = 0; s < steps; s += 4) {
+        ops(s, o0);
+        mm(o0);
+      }
+      if (staged) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) stage(p, b ^ 1, i0 + KB, i2);
+      }
+      return;
+    }
+    ops(0, o0);
+    if (staged) {
+      constexpr int NI = KB / 16;  // groups of four steps in a full chunk (even)
+#pragma unroll
+      for (int it = 0; it < NI; it += 2) {
+        ops(4 * it + 4, o1);
+        mm(o0);
+        if (it < NP) stage(it, b ^ 1, i0 + KB, i2);
+        if (it + 2 < NI) ops(4 * it + 8, o0);
+        mm(o1);
+        if (it + 1 < NP) stage(it + 1, b ^ 1, i0 + KB, i2);
+      }
+#pragma unroll
+      for (int p = NI; p < NP; ++p) stage(p, b ^ 1, i0 + KB, i2);
+    } else {
+      const int steps = min(KB, d - i0) / 4;  // d % 32 == 0: a multiple of 8
+      for (int s = 0; s < steps; s += 8) {
+        ops(s + 4, o1);
+        mm(o0);
+        if (s + 8 < steps) ops(s + 8, o0);
+        mm(o1);
+      }
     }
   };
 
-  load(0);
-  store(0, 0);
-  if (KB < d) load(KB);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (p < XR) load_x(0, p);
+    else load_w(0, p - XR);
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) stage(p, 0, 0, KB);
   __syncthreads();
   int buf = 0;
   for (int i0 = 0; i0 < d; i0 += KB) {
-    compute(buf, i0);
-    if (i0 + KB < d) {
-      store(buf ^ 1, i0 + KB);                 // the other buffer is free
-      if (i0 + 2 * KB < d) load(i0 + 2 * KB);  // in flight during the next chunk
-    }
+    compute(buf, i0, i0 + KB < d);
     __syncthreads();
     buf ^= 1;
   }
