@@ -19,7 +19,10 @@ namespace {
 // One workgroup per token row; each thread owns 8 consecutive columns (two
 // 16-byte pieces) per pass, so d must be a multiple of 8 (the forward's shape
 // rule already asks for 32).  The launch sizes the workgroup to d/8 lanes
-// (up to 1024), so rows up to 8192 wide take one pass with no idle tail.  The slots are read in groups of up to 8 whose
+// (up to 1024), so rows up to 8192 wide take one pass with no idle tail.
+// The output is stored non-temporally: this layer never reads it back
+// (measured: FP8 prefill combine 1.50 -> 1.44 ms; the same hint on the Y
+// loads made it slower).  The slots are read in groups of up to 8 whose
 // loads are all issued before their fmas, so more Y bytes are in flight per
 // CU; the accumulation itself stays j ascending, then the shared experts.
 constexpr int kCombineGroup = 8;
@@ -83,12 +86,13 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
       auto pk = [](float lo, float hi) {
         return f32_to_bf16_rne(lo) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
       };
-      *reinterpret_cast<uint4*>(o) =
-          uint4{pk(a0[0], a0[1]), pk(a0[2], a0[3]), pk(a1[0], a1[1]), pk(a1[2], a1[3])};
+      __builtin_nontemporal_store(
+          u32x4{pk(a0[0], a0[1]), pk(a0[2], a0[3]), pk(a1[0], a1[1]), pk(a1[2], a1[3])},
+          reinterpret_cast<u32x4*>(o));
     } else {
       float* o = static_cast<float*>(out) + static_cast<size_t>(t) * d + c;
-      *reinterpret_cast<f32x4*>(o) = a0;
-      *reinterpret_cast<f32x4*>(o + 4) = a1;
+      __builtin_nontemporal_store(a0, reinterpret_cast<f32x4*>(o));
+      __builtin_nontemporal_store(a1, reinterpret_cast<f32x4*>(o + 4));
     }
   }
 }
