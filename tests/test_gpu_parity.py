@@ -158,6 +158,10 @@ EDGE = {
     "fp8_small": MoEConfig("fp8_small", 20, 128, 128, 4, 2, BF16, FP8, BF16),
     "mx_small": MoEConfig("mx_small", 20, 128, 128, 4, 2, BF16, MXFP4, BF16),
     "mx_T1": MoEConfig("mx_T1", 1, 256, 384, 8, 2, BF16, MXFP4, BF16),
+    # hidden sizes above 8192: the combine takes a second pass over the row
+    # (1024 lanes of 8 columns) and the gate a partial last chunk
+    "wide_d": MoEConfig("wide_d", 9, 8256, 64, 4, 2, BF16, BF16, BF16),
+    "wide_fp8": MoEConfig("wide_fp8", 7, 8320, 128, 4, 2, BF16, FP8, BF16),
 }
 
 
