@@ -89,15 +89,16 @@ __device__ __forceinline__ void topk_row(const float* l, int E, int k, int32_t* 
   }
 }
 
-// One wavefront per token.
+// One wavefront per token; SLOTS = the logits each lane holds (E <= 64 SLOTS).
+template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w, int T,
                                                    int E, int k) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_row<16>(logits + static_cast<size_t>(t) * E, E, k, ids + static_cast<size_t>(t) * k,
-               w + static_cast<size_t>(t) * k, threadIdx.x & 63);
+  topk_row<SLOTS>(logits + static_cast<size_t>(t) * E, E, k, ids + static_cast<size_t>(t) * k,
+                  w + static_cast<size_t>(t) * k, threadIdx.x & 63);
 }
 
 // (value, index) a ranks before (value, index) b: larger logit first, equal
@@ -453,7 +454,12 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
 
 void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
                  hipStream_t s) {
-  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, T, E, k);
+  const dim3 grid((T + 3) / 4);
+  if (E <= 64) topk_kernel<1><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
+  else if (E <= 128) topk_kernel<2><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
+  else if (E <= 256) topk_kernel<4><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
+  else if (E <= 512) topk_kernel<8><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
+  else topk_kernel<16><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
 }
 
 // Gate: logits on the MFMA, then top-k -- inside the same workgroup when one

@@ -77,6 +77,22 @@ def test_route_large_T_bit_exact(E, k, act, d):
     assert (ref_ids == 3).any() and not ((ref_ids == 7) & ~(ref_ids == 3).any(1)[:, None]).any()
 
 
+@pytest.mark.parametrize("E,k", [(300, 8), (512, 33), (1000, 64), (1024, 70)])
+def test_route_wide_E_bit_exact(E, k):
+    # E above 256: the separate top-k kernel with 8 or 16 logits per lane,
+    # k above one wave's 64 selections included; exact ties as above
+    cfg = MoEConfig("route_E", 70, 128, 128, E, k, BF16, BF16, BF16)
+    say("route wide E", E, k)
+    inp = gpu_inputs(cfg)
+    inp["gate_w"][:, 7] = inp["gate_w"][:, 3]
+    inp["gate_w"][:, E - 1] = inp["gate_w"][:, 0]
+    logits, ids, w = gpu_route(cfg, inp)
+    ref_l, ref_ids, ref_w = oracle_route_rows(cfg, inp, np.arange(cfg.T))
+    assert np.array_equal(logits.cpu().numpy(), ref_l)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert f32_ulps(w.cpu().numpy(), ref_w) <= 4
+
+
 @pytest.mark.parametrize("name", list(REDUCED))
 @pytest.mark.parametrize("block_m", [0, 16, 128])
 def test_permute_bit_exact(name, block_m):
