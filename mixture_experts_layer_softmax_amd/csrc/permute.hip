@@ -11,7 +11,9 @@
 // No global atomics: each chunk of consecutive pairs is counted by one
 // wavefront into a [chunks x E] table; one workgroup scans it in (expert,
 // chunk) order; the scatter wavefront of each chunk re-ranks its pairs with
-// ballots so equal experts keep increasing q = t*k + j order.
+// ballots so equal experts keep increasing q = t*k + j order.  When all the
+// pairs fit one chunk (decode), one workgroup does the three steps in a
+// single launch.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -42,31 +44,20 @@ __global__ __launch_bounds__(64) void hist_kernel(const int32_t* __restrict__ id
   for (int e = lane; e < E; e += 64) table[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
-// One workgroup of 1024 threads.  table [nchunk x E] in, becomes the base slot
-// of each (chunk, expert).  Also writes counts/offsets, the m-tile map for
-// tile height bm and zeroes the GEMM work-queue counters.  The S shared
-// experts (every token, after the routed slots) get their slot records and
-// m-tiles here too.  When the table
-// fits (LDS_TABLE), it is scanned in LDS: loaded and stored back coalesced by
-// all threads, each expert's column summed by one thread from LDS.
-template <bool LDS_TABLE>
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table, int nchunk,
-                                                    int E, int bm, int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    TileMap tm, int T, int k, int S,
-                                                    int32_t* __restrict__ slot_token,
-                                                    int32_t* __restrict__ slot_k) {
-  __shared__ int32_t s_cnt[1024];
+// Body of the scan for one workgroup of 1024 threads: tab [nchunk x E] (LDS
+// or global) holds the per-(chunk, expert) counts and becomes, per cell, the
+// slot base of that chunk inside its expert (without the expert's offset,
+// which s_cnt[e] holds on return).  Also writes counts/offsets, the m-tile
+// map for tile height bm and zeroes the GEMM work-queue counters.  The S
+// shared experts (every token, after the routed slots) get their slot
+// records and m-tiles here too.
+__device__ void scan_core(int32_t* tab, int nchunk, int E, int bm, int32_t* __restrict__ counts,
+                          int32_t* __restrict__ offsets, TileMap tm, int T, int k, int S,
+                          int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_k,
+                          int32_t* s_cnt) {
   __shared__ int32_t s_tiles[1024];
   __shared__ int32_t s_shared_tile0;  // first m-tile of the shared experts
-  extern __shared__ int32_t s_tab[];  // [nchunk][E] when LDS_TABLE
-  int32_t* tab = LDS_TABLE ? s_tab : table;
   const int tid = threadIdx.x;
-  const int cells = nchunk * E;
-  if (LDS_TABLE) {
-    for (int i = tid; i < cells; i += 1024) s_tab[i] = table[i];
-    __syncthreads();
-  }
   int total = 0;
   if (tid < E) {
     // running sum down this expert's column; loads go out 8 at a time
@@ -107,8 +98,6 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
     const int off = s_cnt[tid];
     counts[tid] = total;
     offsets[tid] = off;
-    if (!LDS_TABLE)
-      for (int c = 0; c < nchunk; ++c) table[static_cast<size_t>(c) * E + tid] += off;
     const int t0 = s_tiles[tid];
     for (int m = 0; m < tiles; ++m) {
       tm.e[t0 + m] = tid;
@@ -116,14 +105,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
       tm.rows[t0 + m] = min(bm, total - m * bm);
     }
   }
-  if (LDS_TABLE) {
-    __syncthreads();  // column sums and s_cnt (expert offsets) are final
-    for (int i = tid; i < cells; i += 1024) table[i] = s_tab[i] + s_cnt[i % E];
-  }
   if (S > 0) {
     // shared experts: slot T*k + s*T + t holds (token t, k-slot k + s); their
     // m-tiles follow the routed ones, expert index E + s
-    __syncthreads();
     const int mt_per = (T + bm - 1) / bm, t_sh0 = s_shared_tile0;
     const int64_t base = static_cast<int64_t>(T) * k;
     for (int64_t i = tid; i < static_cast<int64_t>(S) * T; i += 1024) {
@@ -137,20 +121,41 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table,
       tm.rows[t_sh0 + i] = min(bm, T - m * bm);
     }
   }
+  __syncthreads();  // s_cnt (expert offsets) is final for the caller
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int n,
-                                                     int k, int E, int nbits, int chunk,
-                                                     const int32_t* __restrict__ table,
-                                                     int32_t* __restrict__ slot_token,
-                                                     int32_t* __restrict__ slot_k,
-                                                     int32_t* __restrict__ token_slot) {
-  extern __shared__ int32_t base[];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) base[e] = table[static_cast<size_t>(blockIdx.x) * E + e];
-  __syncthreads();
-  const int q0 = blockIdx.x * chunk;
-  const int q1 = min(n, q0 + chunk);
+// One workgroup of 1024 threads.  table [nchunk x E] in, becomes the base slot
+// of each (chunk, expert); see scan_core for the rest.  When the table fits
+// (LDS_TABLE), it is scanned in LDS: loaded and stored back coalesced by all
+// threads, each expert's column summed by one thread from LDS.
+template <bool LDS_TABLE>
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ table, int nchunk,
+                                                    int E, int bm, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    TileMap tm, int T, int k, int S,
+                                                    int32_t* __restrict__ slot_token,
+                                                    int32_t* __restrict__ slot_k) {
+  __shared__ int32_t s_cnt[1024];
+  extern __shared__ int32_t s_tab[];  // [nchunk][E] when LDS_TABLE
+  const int tid = threadIdx.x;
+  const int cells = nchunk * E;
+  if (LDS_TABLE) {
+    for (int i = tid; i < cells; i += 1024) s_tab[i] = table[i];
+    __syncthreads();
+  }
+  scan_core(LDS_TABLE ? s_tab : table, nchunk, E, bm, counts, offsets, tm, T, k, S, slot_token,
+            slot_k, s_cnt);
+  for (int i = tid; i < cells; i += 1024)
+    table[i] = (LDS_TABLE ? s_tab[i] : table[i]) + s_cnt[i % E];
+}
+
+// Stable scatter of pairs [q0, q1) by one wavefront: base[e] is the next slot
+// of expert e; ballots over the expert bits rank the lanes holding the same
+// expert, so equal experts keep increasing q = t*k + j order.
+__device__ void scatter_run(const int32_t* __restrict__ ids, int q0, int q1, int k, int nbits,
+                            int32_t* base, int32_t* __restrict__ slot_token,
+                            int32_t* __restrict__ slot_k, int32_t* __restrict__ token_slot) {
+  const int lane = threadIdx.x & 63;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int qb = q0; qb < q1; qb += 64) {
     const int q = qb + lane;
@@ -161,15 +166,52 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
     const int cnt = __popcll(peers);
     int slot = 0;
     if (active) slot = base[e] + rank;
-    __syncthreads();  // every lane has read base[] before it moves
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // every lane has read base[]
     if (active && rank == cnt - 1) base[e] += cnt;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (active) {
       slot_token[slot] = q / k;
       slot_k[slot] = q % k;
       token_slot[q] = slot;
     }
   }
+}
+
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int n,
+                                                     int k, int E, int nbits, int chunk,
+                                                     const int32_t* __restrict__ table,
+                                                     int32_t* __restrict__ slot_token,
+                                                     int32_t* __restrict__ slot_k,
+                                                     int32_t* __restrict__ token_slot) {
+  extern __shared__ int32_t base[];
+  for (int e = threadIdx.x; e < E; e += 64)
+    base[e] = table[static_cast<size_t>(blockIdx.x) * E + e];
+  __syncthreads();
+  const int q0 = blockIdx.x * chunk;
+  scatter_run(ids, q0, min(n, q0 + chunk), k, nbits, base, slot_token, slot_k, token_slot);
+}
+
+// All of the permutation when the pairs fit one chunk (decode-sized T*k):
+// histogram, scan and scatter in one workgroup, with the same results as the
+// three kernels.
+__global__ __launch_bounds__(1024) void permute_one_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int nbits, int bm, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, TileMap tm, int T, int k, int S,
+    int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_k,
+    int32_t* __restrict__ token_slot) {
+  __shared__ int32_t s_cnt[1024];
+  __shared__ int32_t s_tab[1024];  // the one-chunk table: counts, then slot bases
+  const int tid = threadIdx.x;
+  if (tid < E) s_tab[tid] = 0;
+  __syncthreads();
+  for (int q = tid; q < n; q += 1024) atomicAdd(&s_tab[ids[q]], 1);  // LDS integer add
+  __syncthreads();
+  scan_core(s_tab, 1, E, bm, counts, offsets, tm, T, k, S, slot_token, slot_k, s_cnt);
+  if (tid < E) s_tab[tid] += s_cnt[tid];
+  __syncthreads();
+  if (tid < 64) scatter_run(ids, 0, n, k, nbits, s_tab, slot_token, slot_k, token_slot);
 }
 
 }  // namespace
@@ -183,6 +225,11 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int S, int bm, int3
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   const size_t lds = sizeof(int32_t) * static_cast<size_t>(E);
+  if (nchunk == 1) {
+    permute_one_kernel<<<1, 1024, 0, s>>>(ids, n, E, nbits, bm, counts, offsets, tm, T, k, S,
+                                          slot_token, slot_k, token_slot);
+    return;
+  }
   if (nchunk > 0) hist_kernel<<<nchunk, 64, lds, s>>>(ids, n, E, chunk, table);
   // the table in LDS when it fits next to the kernel's 8 KB of static LDS
   constexpr size_t kMaxTab = 144 * 1024;
