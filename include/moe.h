@@ -36,7 +36,8 @@
  *  - Slots are ordered by expert, and inside an expert by q = t*k + j.
  *  - SwiGLU expert: h = SiLU(x W1) * (x W3), SiLU(a) = a / (1 + e^-a),
  *    y = h W2, fp32 accumulation; h is rounded to the activation format
- *    (fp32, bf16 RNE, or FP8 1x128 groups) before W2; y stays fp32.
+ *    (fp32, bf16 RNE, FP8 1x128 groups, or MX FP8 blocks of 32 for
+ *    MOE_MXFP4) before W2; y stays fp32.
  *  - FP8 groups: activations per 1x128 group along the contraction axis with
  *    scale s = amax / 448 (1 when amax == 0) and code e4m3_rne_sat(v / s)
  *    (both quotients fp32 IEEE); weights per 128x128 (K, N) block.
@@ -112,7 +113,7 @@ typedef struct {
  * Any pointer may be NULL.  Sizes as in moe_route / moe_permute.
  * stage_events: caller-created HIP events (or NULL); event i is recorded on
  * the call's stream at stage boundary i: 0 start, 1 after the gate, 2 after
- * the FP8 quantisation of x, 3 after histogram/scan/scatter, 4 after the
+ * the FP8 / MX FP8 quantisation of x, 3 after histogram/scan/scatter, 4 after the
  * W1/W3 GEMM, 5 after the W2 GEMM, 6 after the combine.  Used to time each
  * kernel inside the whole-layer call.
  * gemm_clock: [2][2] uint64 device buffer, or NULL: for the W1/W3 (row 0) and
