@@ -77,6 +77,23 @@ def test_route_large_T_bit_exact(E, k, act, d):
     assert (ref_ids == 3).any() and not ((ref_ids == 7) & ~(ref_ids == 3).any(1)[:, None]).any()
 
 
+@pytest.mark.parametrize("E,k,act", [(40, 3, BF16), (64, 6, BF16), (64, 8, BF16), (48, 2, F32)])
+def test_route_mid_T_bit_exact(E, k, act):
+    # 8192 <= T < 16384 with 33..64 experts (the skewed workload's regime):
+    # experts split over two workgroups, then the top-k kernel; exact ties as
+    # above
+    cfg = MoEConfig("route_mid", 9000, 128, 128, E, k, act, act, act)
+    say("route mid T", E, k, act)
+    inp = gpu_inputs(cfg)
+    inp["gate_w"][:, 7] = inp["gate_w"][:, 3]
+    inp["gate_w"][:, E - 1] = inp["gate_w"][:, 0]
+    logits, ids, w = gpu_route(cfg, inp)
+    ref_l, ref_ids, ref_w = oracle_route_rows(cfg, inp, np.arange(cfg.T))
+    assert np.array_equal(logits.cpu().numpy(), ref_l)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert f32_ulps(w.cpu().numpy(), ref_w) <= 4
+
+
 @pytest.mark.parametrize("E,k", [(300, 8), (512, 33), (1000, 64), (1024, 70)])
 def test_route_wide_E_bit_exact(E, k):
     # E above 256: the separate top-k kernel with 8 or 16 logits per lane,
