@@ -257,6 +257,29 @@ def test_forward_is_deterministic():
         assert torch.equal(o, outs[0])
 
 
+def test_concurrent_calls_on_two_streams():
+    # the library keeps no per-call state outside the workspace: two layers
+    # (different shapes, dtypes and workspaces) enqueued alternately on two
+    # streams give the same bits as when run one after the other
+    cfgs = [REDUCED["skewed_bf16_r"], REDUCED["prefill_mxfp4_r"]]
+    say("two streams", [c.name for c in cfgs])
+    inps = [gpu_inputs(c) for c in cfgs]
+    packs = [B.pack_weights(i) for i in inps]
+    ref = [B.forward(c, i, p, out_dtype=F32) for c, i, p in zip(cfgs, inps, packs)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    for rep in range(3):
+        for j in (0, 1):
+            with torch.cuda.stream(streams[j]):
+                outs[j].append(B.forward(cfgs[j], inps[j], packs[j], out_dtype=F32,
+                                         stream=streams[j]))
+    torch.cuda.synchronize()
+    for j in (0, 1):
+        for o in outs[j]:
+            assert torch.equal(o, ref[j]), (cfgs[j].name)
+
+
 def test_gemm_clock_record():
     """moe_debug.gemm_clock receives, per GEMM launch, the shader-clock and
     100 MHz reference ticks of the first workgroup; the implied clock lies in
