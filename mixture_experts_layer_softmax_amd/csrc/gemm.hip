@@ -201,8 +201,15 @@ struct TaskQueue {
   }
 };
 
-template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_>
-__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
+// One task of the grouped GEMM: m-tile mt (rows of one expert, from the tile
+// map) times column tile nt -- the K loop through the LDS ring, then the
+// epilogue.  kpull() runs a few k-steps before the end (the next task's
+// queue request); pre_epi() runs between the main loop and the epilogue.
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, class KPull,
+          class PreEpi>
+__device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const int nt,
+                                          const int64_t hrow_base, KPull&& kpull,
+                                          PreEpi&& pre_epi) {
   using G = Geo<DT, PHASE, BM, BN, WM, WN, KRB_>;
   constexpr int kThreads = G::kThreads, ES = G::ES, KRB = G::KRB, NS = G::NS;
   constexpr int NW = G::NW, RPD = G::ROWS_PER_DMA, RPDW = G::ROWS_PER_DMAW, KRBW = G::KRBW;
@@ -218,20 +225,503 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
   // the epilogue staging; then (FP8 phase 1) the per-wave row maxima.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds + (G::RING > G::EPI ? G::RING : G::EPI));
-  // the task hand-over slot lives in the last bytes of the ring: it is
-  // written after every wave is done with the ring and read before the
-  // first DMA of the task can reach that stage slot
-  int& s_task = *reinterpret_cast<int*>(lds + G::RING - 16);
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint64_t clk0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
   const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, lg = lane >> 4;
   const int64_t K = g.K, N = g.N;
   const int ksteps = static_cast<int>(K * ES / KRB);
   const int kblocks = static_cast<int>(K / 128);  // FP8 scale blocks along K
   const int nblocks = static_cast<int>(N / 128);
+
+  const int k_pull = max(0, ksteps - 4);
+  const int e = __builtin_amdgcn_readfirstlane(g.tm.e[mt]);
+  const int row0 = __builtin_amdgcn_readfirstlane(g.tm.row0[mt]);
+  // rows of the A operand (when not gathered) and of C: the slot rows, or
+  // hrow_base.. when the caller places this m-tile elsewhere
+  const int64_t hrow = hrow_base >= 0 ? hrow_base : row0;
+  const int rows = __builtin_amdgcn_readfirstlane(g.tm.rows[mt]);
+  const int64_t n0 = static_cast<int64_t>(nt) * BN;
+
+  // ---- DMA sources of this lane: 32-bit byte offsets from wave-uniform
+  // bases (the host checks that x, h and one expert's weight matrix each
+  // span less than 2^31 bytes).  A wave-wide DMA fills RPD rows of KRB
+  // bytes; lane L fills row L / (KRB/16), physical chunk L % (KRB/16), so it
+  // loads the logical chunk that the swizzle maps there. ----
+  const int64_t w_row = MX ? K / 2 : K * ES;  // weight row bytes (FP4: two per byte)
+  const int64_t w_bytes = N * w_row;
+  const uint8_t* b0 = g.B0 + static_cast<int64_t>(e) * w_bytes;
+  const uint8_t* b1 = (PHASE == 1) ? g.B1 + static_cast<int64_t>(e) * w_bytes : b0;
+  constexpr int CPRK = KRB / 16;    // 16-byte chunks per activation LDS row
+  constexpr int CPRKW = KRBW / 16;  // and per weight LDS row
+  const int lrow = lane / CPRK, lphys = lane % CPRK;
+  const int lroww = lane / CPRKW, lphysw = lane % CPRKW;
+  uint32_t oa[G::AW], ob[G::BW];
+  uint32_t up_mask = 0;  // bit j: B block j of this wave comes from W3 (up)
+  int my_loads = 0;      // DMA instructions this wave issues per stage
+#pragma unroll
+  for (int j = 0; j < G::AW; ++j) {
+    const int q = wave + NW * j;
+    const int r = q * RPD + lrow;
+    const int logical = lphys ^ swz_key<KRB>(r);
+    const int rr = min(r, rows - 1);  // padding rows re-read a valid row
+    const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(hrow + rr);
+    oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + logical * 16);
+    if (q < G::ABLK) ++my_loads;
+  }
+#pragma unroll
+  for (int j = 0; j < G::BW; ++j) {
+    const int q = wave + NW * j;
+    const int r = q * RPDW + lroww;
+    const int logical = lphysw ^ swz_key<KRBW>(r);
+    const int64_t n = n0 + r;
+    int64_t col;
+    if (PHASE == 1) {  // combined rows: 16 gate rows, then 16 up rows, per f block
+      // the RPD rows of one DMA lie in one 16-row block (RPD divides 16 and
+      // n0 is a multiple of 32), so the gate/up choice is wave-uniform
+      static_assert(16 % RPDW == 0, "DMA rows inside one gate/up block");
+      col = (n >> 5) * 16 + (n & 15);
+      if ((q * RPDW) & 16) up_mask |= 1u << j;
+    } else {
+      col = n;
+    }
+    col = min(col, N - 1);
+    ob[j] = static_cast<uint32_t>(col * w_row + logical * 16);
+    if (q < G::BBLK) ++my_loads;
+  }
+  const float* sa_src = g.sa;  // FP8: this lane's A-row scale row
+  if constexpr (DT == kFP8) {
+    const int rr = min(wave * 64 + lane, rows - 1);
+    const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
+    sa_src = g.sa + src * kblocks;
+    if (wave < G::SA_DMA) ++my_loads;
+  }
+  // MX: E8M0 scale dwords of this lane (4 blocks of 32 = one stage).
+  // Scale DMA number c < SA_DMA covers activation rows 64c.. ([rows][K/32]
+  // bytes: the next stage's dword follows), the others weight rows
+  // 64(c - SA_DMA).. of the tile (packed [E][K/128][N] dwords: a stage's
+  // dwords of consecutive rows are contiguous, the next stage is N dwords
+  // on); wave w issues c = w, w + NW, ...
+  const uint8_t* msc[G::SCW > 0 ? G::SCW : 1];
+  uint32_t mstep[G::SCW > 0 ? G::SCW : 1];
+  if constexpr (MX) {
+    const int64_t kb32 = K / 32;
+#pragma unroll
+    for (int u = 0; u < G::SCW; ++u) {
+      const int c = wave + NW * u;
+      msc[u] = nullptr;
+      mstep[u] = 4;
+      if (c < G::SA_DMA) {
+        const int rr = min(c * 64 + lane, rows - 1);
+        const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
+        msc[u] = reinterpret_cast<const uint8_t*>(g.sa) + src * kb32;
+        ++my_loads;
+      } else if (c < G::SA_DMA + G::SB_DMA) {
+        const int64_t n = n0 + (c - G::SA_DMA) * 64 + lane;
+        int64_t col = (PHASE == 1) ? (n >> 5) * 16 + (n & 15) : n;
+        col = min(col, N - 1);
+        const float* sb = (PHASE == 1 && (n & 16)) ? g.sb1 : g.sb0;
+        msc[u] = reinterpret_cast<const uint8_t*>(sb) + (static_cast<int64_t>(e) * N * kb32 + col * 4);
+        mstep[u] = static_cast<uint32_t>(N * 4);
+        ++my_loads;
+      }
+    }
+  }
+
+// DMA of stage KS: the activation rows (and FP8 row scales) when DO_A, the
+// weight rows when DO_B
+#define MOE_ISSUE_PART(KS, DO_A, DO_B)                                                   \
+do {                                                                                   \
+  uint8_t* st_ = lds + ((KS) % NS) * G::STAGE;                                         \
+  const uint32_t ko_ = static_cast<uint32_t>(KS) * KRB;                                \
+  if (DO_A) {                                                                          \
+    _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                \
+      const int q = wave + NW * j;                                                     \
+      if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024); \
+    }                                                                                  \
+    if (DT == kFP8 && wave < G::SA_DMA)                                                \
+      dma4(sa_src + (KS), st_ + BM * KRB + BN * KRBW + wave * 256);                    \
+  }                                                                                    \
+  if (DO_B) {                                                                          \
+    const uint32_t kw_ = static_cast<uint32_t>(KS) * KRBW;                             \
+    _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                \
+      const int q = wave + NW * j;                                                     \
+      if (G::BBLK % NW == 0 || q < G::BBLK)                                            \
+        dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + kw_), st_ + BM * KRB + q * 1024); \
+    }                                                                                  \
+    if (MX) {                                                                          \
+      _Pragma("unroll") for (int u = 0; u < G::SCW; ++u) {                             \
+        const int c = wave + NW * u;                                                   \
+        if (c < G::SA_DMA + G::SB_DMA)                                                 \
+          dma4(msc[u] + (KS) * mstep[u], st_ + BM * KRB + BN * KRBW + c * 256);        \
+      }                                                                                \
+    }                                                                                  \
+  }                                                                                    \
+} while (0)
+#define MOE_ISSUE(KS) MOE_ISSUE_PART(KS, true, true)
+
+  // FP8: the weight block scales of this tile are wave-uniform and
+  // read-only; they are loaded through the scalar cache (constant address
+  // space) one k-step ahead, off the vector-memory counter that orders the
+  // DMA ring.
+  typedef __attribute__((address_space(4))) const float cfloat;
+  const cfloat* sbp0 = nullptr;
+  const cfloat* sbp1 = nullptr;
+  float sb_cur0 = 0.f, sb_cur1 = 0.f, sb_nxt0 = 0.f, sb_nxt1 = 0.f;
+  if constexpr (DT == kFP8) {
+    const int nb = (PHASE == 1) ? static_cast<int>(n0 / 256)  // 128 f columns per tile
+                                : static_cast<int>((n0 + wn * WTN) / 128);
+    const int64_t base = static_cast<int64_t>(e) * kblocks * nblocks + nb;
+    sbp0 = (const cfloat*)(g.sb0) + base;
+    sbp1 = (PHASE == 1) ? (const cfloat*)(g.sb1) + base : sbp0;
+    sb_nxt0 = sbp0[0];
+    sb_nxt1 = (PHASE == 1) ? sbp1[0] : 0.f;
+  }
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < ksteps) MOE_ISSUE(p);
+
+  for (int ks = 0; ks < ksteps; ++ks) {
+    // my loads of stage ks have landed once at most `ahead` later stages
+    // are still in flight; the barrier then publishes everyone's loads and
+    // guarantees every wave is done with the slot reloaded below
+    const int ahead = min(NS - 2, ksteps - 1 - ks);
+    wait_vmcnt(ahead * my_loads);
+    ring_barrier();
+    if (ks == k_pull) kpull();
+    // bf16 stages hold two MFMA k-steps: the weight rows of the next stage
+    // are requested after the first one, which spreads the DMA's LDS writes
+    // over the stage instead of piling them onto its first fragment reads
+    constexpr bool kSplitDma = (DT == kBF16) && (KRB / 64 == 2);
+    const bool refill = ks + NS - 1 < ksteps;
+    if (refill) MOE_ISSUE_PART(ks + NS - 1, true, !kSplitDma);
+    if constexpr (DT == kFP8) {
+      sb_cur0 = sb_nxt0;
+      sb_cur1 = sb_nxt1;
+      if (ks + 1 < ksteps) {
+        sb_nxt0 = sbp0[static_cast<int64_t>(ks + 1) * nblocks];
+        if (PHASE == 1) sb_nxt1 = sbp1[static_cast<int64_t>(ks + 1) * nblocks];
+      }
+    }
+    const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
+    const uint8_t* Bb = Ab + BM * KRB;
+    const uint8_t* Sb = Bb + BN * KRBW;  // per-stage scale dwords
+    // A wave whose rows are all padding skips the step; a partly valid
+    // wave computes its padding rows too (their results are never stored),
+    // which keeps the fragment loop free of branches.
+    const bool compute = wm * WTM < rows;
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int kk = 0; kk < KRB / 64; ++kk) {
+        if (kSplitDma && kk == 1 && refill) MOE_ISSUE_PART(ks + NS - 1, false, true);
+        if (!compute) continue;
+        bf16x8 wf[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          wf[j] = *reinterpret_cast<const bf16x8*>(
+              Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
+#define MOE_BF16_ROWS(SKIP)                                                               \
+bf16x8 xf[TM];                                                                          \
+_Pragma("unroll") for (int i = 0; i < TM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>( \
+    Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));                               \
+_Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+  if (SKIP) break;                                                                      \
+  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0); \
+}                                                                                       \
+/* issue every fragment read of the step before the MFMAs (LDS latency  */              \
+/* then overlaps the MFMAs instead of stalling each pair of fragments)  */              \
+__builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                                \
+__builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        MOE_BF16_ROWS(false)
+#undef MOE_BF16_ROWS
+      }
+    } else if constexpr (DT == kF32) {
+      if (!compute) continue;
+      f32x4 wf[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz<KRB>(wn * WTN + 16 * j + l16, lg));
+#define MOE_F32_ROWS(SKIP)                                                                \
+_Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
+  if (SKIP) break;                                                                      \
+  const f32x4 xf =                                                                      \
+      *reinterpret_cast<const f32x4*>(Ab + swz<KRB>(wm * WTM + 16 * i + l16, lg));      \
+  _Pragma("unroll") for (int u = 0; u < 4; ++u)                                         \
+  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[u], acc[i][j], 0, 0, 0); \
+}
+      MOE_F32_ROWS(false)
+#undef MOE_F32_ROWS
+    } else if constexpr (MX) {
+      // FP4 weights x MX FP8 activations: one scaled 16x16x128 MFMA per
+      // fragment pair; the E8M0 block scales are MFMA operands.  Measured
+      // operand layout: FP4 lane group lg holds 32 elements in its 16 bytes
+      // (low nibble first) and, in both operands, lane group lg's scale
+      // byte governs exactly those 32 elements; FP8 lane group lg pairs its
+      // bytes 0-15 and 16-31 with half (lg & 1) of FP4 groups lg >> 1 and
+      // (lg >> 1) + 2.  So contraction block lg (32 elements) of the step
+      // goes to FP4 lane group lg in order, the FP8 lanes take 16-byte
+      // chunks lg and lg + 4 of the activation row, and each lane passes
+      // its own row's scale byte of block lg.
+      if (!compute) continue;
+      const uint32_t* sa_st = reinterpret_cast<const uint32_t*>(Sb);
+      const uint32_t* sw_st = sa_st + G::SA_DMA * 64;
+      i32x8 wf[TN];
+      int wsc[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WTN + 16 * j + l16;
+        const i32x4 c = *reinterpret_cast<const i32x4*>(Bb + swz<KRBW>(r, lg));
+        wf[j] = i32x8{c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+        wsc[j] = static_cast<int>((sw_st[r] >> (8 * lg)) & 0xffu);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WTM + 16 * i + l16;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, lg));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, lg + 4));
+        const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int xsc = static_cast<int>((sa_st[r] >> (8 * lg)) & 0xffu);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 4, 0,
+                                                                       0, wsc[j], 0, xsc);
+      }
+    } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
+      if (!compute) continue;
+      i32x8 wf[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WTN + 16 * j + l16;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
+        wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      const float* sa_st = reinterpret_cast<const float*>(Sb);
+      const float s_b0 = sb_cur0, s_b1 = sb_cur1;
+      if constexpr (PHASE == 1) {
+        // Row by row: the TN block products of row i are issued before the
+        // scaled accumulation of row i-1, so the fp32 fmas overlap MFMAs.
+        f32x4 pp[TN];
+        float spg = 0.f, spu = 0.f;
+#pragma unroll
+        for (int i = 0; i <= TM; ++i) {
+          f32x4 pc[TN];
+          float scg = 0.f, scu = 0.f;
+          if (i < TM) {
+            const int r = wm * WTM + 16 * i + l16;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
+            const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const float s_a = sa_st[r];
+            scg = s_a * s_b0;
+            scu = s_a * s_b1;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          }
+          if (i > 0) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const float sc = (PHASE == 1 && (j & 1)) ? spu : spg;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[i - 1][j][q] = __builtin_fmaf(pp[j][q], sc, acc[i - 1][j][q]);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < TN; ++j) pp[j] = pc[j];
+          spg = scg;
+          spu = scu;
+        }
+      } else {  // (measured: the lagged form loses here, to register pressure)
+        // per row of fragments: the TN block products first (independent
+        // MFMAs in flight), then their scaled accumulation
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int r = wm * WTM + 16 * i + l16;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
+          const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const float s_a = sa_st[r];
+          const float sg = s_a * s_b0, su = s_a * s_b1;
+          f32x4 p[TN];
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const float sc = (PHASE == 1 && (j & 1)) ? su : sg;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(p[j][q], sc, acc[i][j][q]);
+          }
+        }
+      }
+    }
+  }
+#undef MOE_ISSUE
+#undef MOE_ISSUE_PART
+
+  pre_epi();
+
+  // ---------------- epilogue ----------------
+  // Output rows are staged in LDS (free after the main loop's last
+  // barrier) so that every global store is a 16-byte piece of a contiguous
+  // row segment: the whole tile in one pass when it fits in the ring, else
+  // one pass per wave row.  Staged rows are XOR-swizzled by 16-byte chunk to
+  // keep the fragment writes off a single bank group.
+  {
+    constexpr int OUT_COLS = (PHASE == 1) ? BN / 2 : BN;
+    constexpr int OUT_ES = (PHASE == 1) ? ES : 4;
+    constexpr int ROWB = OUT_COLS * OUT_ES;
+    constexpr int CPR = ROWB / 16;
+    constexpr int XM = (CPR >= 16 ? 16 : CPR) - 1;
+    constexpr int PASSES = (BM * ROWB <= G::RING - 16) ? 1 : WM;
+    constexpr int PROWS = BM / PASSES;  // rows per pass
+    static_assert(PROWS * ROWB <= (G::RING > G::EPI ? G::RING : G::EPI), "staging fits");
+    uint8_t* stage = lds;
+    auto st_off = [&](int r, int cbyte) {
+      return r * ROWB + ((((cbyte >> 4) ^ (r & XM)) << 4) | (cbyte & 15));
+    };
+    const int64_t col0 = (PHASE == 1) ? n0 / 2 : n0;
+
+    if constexpr (PHASE == 1 && DT == kFP8) {
+      // h = SiLU(gate) * up in fp32 (in place), then the row amax over the
+      // tile's 128 f columns: lanes, then the WN waves through LDS
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float m = 0.f;
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[i][2 * p][r] = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
+            m = fmaxf(m, fabsf(acc[i][2 * p][r]));
+          }
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (lg == 0) red[wn * BM + wm * WTM + 16 * i + l16] = m;
+      }
+    }
+    __syncthreads();  // every wave is done with the ring (and the row maxima are in)
+
+    for (int pass = 0; pass < PASSES; ++pass) {
+      if ((wm * WTM) / PROWS == pass) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int lr = wm * WTM + 16 * i + l16;  // row within the tile
+          const int r = lr - pass * PROWS;          // row within this pass
+          if constexpr (PHASE == 2) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
+                  acc[i][j];
+          } else if constexpr (MX) {
+            // h = SiLU(gate) * up; each block of 32 h columns (two 16-column
+            // fragments, held by the four lanes of this row) gets its MX FP8
+            // exponent from the block amax, then E4M3 codes of h * 2^-X
+#pragma unroll
+            for (int qb = 0; qb < TN / 4; ++qb) {
+              float h[2][4];
+              float m = 0.f;
+#pragma unroll
+              for (int pp = 0; pp < 2; ++pp) {
+                const int p = 2 * qb + pp;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                  h[pp][q4] = silu(acc[i][2 * p][q4]) * acc[i][2 * p + 1][q4];
+                  m = fmaxf(m, fabsf(h[pp][q4]));
+                }
+              }
+              m = fmaxf(m, __shfl_xor(m, 16, 64));
+              m = fmaxf(m, __shfl_xor(m, 32, 64));
+              const int x = mx_exponent_e4m3(m);
+#pragma unroll
+              for (int pp = 0; pp < 2; ++pp) {
+                uint32_t packed = 0;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                  packed |= f32_to_e4m3(__builtin_ldexpf(h[pp][q4], -x)) << (8 * q4);
+                *reinterpret_cast<uint32_t*>(
+                    stage + st_off(r, wn * (WTN / 2) + 16 * (2 * qb + pp) + 4 * lg)) = packed;
+              }
+              if (lg == 0 && lr < rows)
+                reinterpret_cast<uint8_t*>(g.sc)[static_cast<int64_t>(row0 + lr) * (N / 32) +
+                                                 (col0 + wn * (WTN / 2) + 32 * qb) / 32] =
+                    static_cast<uint8_t>(x + 127);
+            }
+          } else if constexpr (DT == kFP8) {
+            float amax = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + lr]);
+            const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
+#pragma unroll
+            for (int p = 0; p < TN / 2; ++p) {
+              uint32_t packed = 0;
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4)
+                packed |= f32_to_e4m3(__fdiv_rn(acc[i][2 * p][q4], sc)) << (8 * q4);
+              *reinterpret_cast<uint32_t*>(stage + st_off(r, wn * (WTN / 2) + 16 * p + 4 * lg)) =
+                  packed;
+            }
+            if (wn == 0 && lg == 0 && lr < rows)
+              g.sc[static_cast<int64_t>(row0 + lr) * (N / 128) + n0 / 256] = sc;
+          } else {
+#pragma unroll
+            for (int p = 0; p < TN / 2; ++p) {
+              float h[4];
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4)
+                h[q4] = silu(acc[i][2 * p][q4]) * acc[i][2 * p + 1][q4];
+              const int cb = (wn * (WTN / 2) + 16 * p + 4 * lg) * ES;
+              if constexpr (DT == kBF16) {
+                u32x2 v;
+                v.x = f32_to_bf16_rne(h[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[1])) << 16);
+                v.y = f32_to_bf16_rne(h[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[3])) << 16);
+                *reinterpret_cast<u32x2*>(stage + st_off(r, cb)) = v;
+              } else {
+                *reinterpret_cast<f32x4*>(stage + st_off(r, cb)) = f32x4{h[0], h[1], h[2], h[3]};
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      for (int idx = tid; idx < PROWS * CPR; idx += kThreads) {
+        const int r = idx / CPR, c = idx - r * CPR;
+        const int lr = pass * PROWS + r;
+        const int64_t col = col0 + c * (16 / OUT_ES);
+        if (lr < rows && col < N)
+          *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(hrow + lr) * N + col) * OUT_ES) =
+              *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
+      }
+      if (pass + 1 < PASSES) __syncthreads();
+    }
+  }
+
+}
+
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_>
+__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
+  using G = Geo<DT, PHASE, BM, BN, WM, WN, KRB_>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  // the task hand-over slot lives in the last bytes of the ring: it is
+  // written after every wave is done with the ring and read before the
+  // first DMA of the task can reach that stage slot
+  int& s_task = *reinterpret_cast<int*>(lds + G::RING - 16);
+
+  const int tid = threadIdx.x;
+  const uint64_t clk0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
 
   // XCD-aware work queue.  Each workgroup reads the XCD it runs on from the
   // XCC_ID hardware register and shares that XCD's L2 with the workgroups
@@ -262,477 +752,14 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     // k-steps while keeping the reservation short, so that the tail of the
     // queue still spreads over all workgroups.
     int next_v = -1;
-    const int k_pull = max(0, ksteps - 4);
     const int mt = task / NT;
     const int nt = task - mt * NT;
-    const int e = __builtin_amdgcn_readfirstlane(g.tm.e[mt]);
-    const int row0 = __builtin_amdgcn_readfirstlane(g.tm.row0[mt]);
-    const int rows = __builtin_amdgcn_readfirstlane(g.tm.rows[mt]);
-    const int64_t n0 = static_cast<int64_t>(nt) * BN;
-
-    // ---- DMA sources of this lane: 32-bit byte offsets from wave-uniform
-    // bases (the host checks that x, h and one expert's weight matrix each
-    // span less than 2^31 bytes).  A wave-wide DMA fills RPD rows of KRB
-    // bytes; lane L fills row L / (KRB/16), physical chunk L % (KRB/16), so it
-    // loads the logical chunk that the swizzle maps there. ----
-    const int64_t w_row = MX ? K / 2 : K * ES;  // weight row bytes (FP4: two per byte)
-    const int64_t w_bytes = N * w_row;
-    const uint8_t* b0 = g.B0 + static_cast<int64_t>(e) * w_bytes;
-    const uint8_t* b1 = (PHASE == 1) ? g.B1 + static_cast<int64_t>(e) * w_bytes : b0;
-    constexpr int CPRK = KRB / 16;    // 16-byte chunks per activation LDS row
-    constexpr int CPRKW = KRBW / 16;  // and per weight LDS row
-    const int lrow = lane / CPRK, lphys = lane % CPRK;
-    const int lroww = lane / CPRKW, lphysw = lane % CPRKW;
-    uint32_t oa[G::AW], ob[G::BW];
-    uint32_t up_mask = 0;  // bit j: B block j of this wave comes from W3 (up)
-    int my_loads = 0;      // DMA instructions this wave issues per stage
-#pragma unroll
-    for (int j = 0; j < G::AW; ++j) {
-      const int q = wave + NW * j;
-      const int r = q * RPD + lrow;
-      const int logical = lphys ^ swz_key<KRB>(r);
-      const int rr = min(r, rows - 1);  // padding rows re-read a valid row
-      const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
-      oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + logical * 16);
-      if (q < G::ABLK) ++my_loads;
-    }
-#pragma unroll
-    for (int j = 0; j < G::BW; ++j) {
-      const int q = wave + NW * j;
-      const int r = q * RPDW + lroww;
-      const int logical = lphysw ^ swz_key<KRBW>(r);
-      const int64_t n = n0 + r;
-      int64_t col;
-      if (PHASE == 1) {  // combined rows: 16 gate rows, then 16 up rows, per f block
-        // the RPD rows of one DMA lie in one 16-row block (RPD divides 16 and
-        // n0 is a multiple of 32), so the gate/up choice is wave-uniform
-        static_assert(16 % RPDW == 0, "DMA rows inside one gate/up block");
-        col = (n >> 5) * 16 + (n & 15);
-        if ((q * RPDW) & 16) up_mask |= 1u << j;
-      } else {
-        col = n;
-      }
-      col = min(col, N - 1);
-      ob[j] = static_cast<uint32_t>(col * w_row + logical * 16);
-      if (q < G::BBLK) ++my_loads;
-    }
-    const float* sa_src = g.sa;  // FP8: this lane's A-row scale row
-    if constexpr (DT == kFP8) {
-      const int rr = min(wave * 64 + lane, rows - 1);
-      const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
-      sa_src = g.sa + src * kblocks;
-      if (wave < G::SA_DMA) ++my_loads;
-    }
-    // MX: E8M0 scale dwords of this lane (4 blocks of 32 = one stage).
-    // Scale DMA number c < SA_DMA covers activation rows 64c.. ([rows][K/32]
-    // bytes: the next stage's dword follows), the others weight rows
-    // 64(c - SA_DMA).. of the tile (packed [E][K/128][N] dwords: a stage's
-    // dwords of consecutive rows are contiguous, the next stage is N dwords
-    // on); wave w issues c = w, w + NW, ...
-    const uint8_t* msc[G::SCW > 0 ? G::SCW : 1];
-    uint32_t mstep[G::SCW > 0 ? G::SCW : 1];
-    if constexpr (MX) {
-      const int64_t kb32 = K / 32;
-#pragma unroll
-      for (int u = 0; u < G::SCW; ++u) {
-        const int c = wave + NW * u;
-        msc[u] = nullptr;
-        mstep[u] = 4;
-        if (c < G::SA_DMA) {
-          const int rr = min(c * 64 + lane, rows - 1);
-          const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
-          msc[u] = reinterpret_cast<const uint8_t*>(g.sa) + src * kb32;
-          ++my_loads;
-        } else if (c < G::SA_DMA + G::SB_DMA) {
-          const int64_t n = n0 + (c - G::SA_DMA) * 64 + lane;
-          int64_t col = (PHASE == 1) ? (n >> 5) * 16 + (n & 15) : n;
-          col = min(col, N - 1);
-          const float* sb = (PHASE == 1 && (n & 16)) ? g.sb1 : g.sb0;
-          msc[u] = reinterpret_cast<const uint8_t*>(sb) + (static_cast<int64_t>(e) * N * kb32 + col * 4);
-          mstep[u] = static_cast<uint32_t>(N * 4);
-          ++my_loads;
-        }
-      }
-    }
-
-// DMA of stage KS: the activation rows (and FP8 row scales) when DO_A, the
-// weight rows when DO_B
-#define MOE_ISSUE_PART(KS, DO_A, DO_B)                                                   \
-  do {                                                                                   \
-    uint8_t* st_ = lds + ((KS) % NS) * G::STAGE;                                         \
-    const uint32_t ko_ = static_cast<uint32_t>(KS) * KRB;                                \
-    if (DO_A) {                                                                          \
-      _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                \
-        const int q = wave + NW * j;                                                     \
-        if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024); \
-      }                                                                                  \
-      if (DT == kFP8 && wave < G::SA_DMA)                                                \
-        dma4(sa_src + (KS), st_ + BM * KRB + BN * KRBW + wave * 256);                    \
-    }                                                                                    \
-    if (DO_B) {                                                                          \
-      const uint32_t kw_ = static_cast<uint32_t>(KS) * KRBW;                             \
-      _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                \
-        const int q = wave + NW * j;                                                     \
-        if (G::BBLK % NW == 0 || q < G::BBLK)                                            \
-          dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + kw_), st_ + BM * KRB + q * 1024); \
-      }                                                                                  \
-      if (MX) {                                                                          \
-        _Pragma("unroll") for (int u = 0; u < G::SCW; ++u) {                             \
-          const int c = wave + NW * u;                                                   \
-          if (c < G::SA_DMA + G::SB_DMA)                                                 \
-            dma4(msc[u] + (KS) * mstep[u], st_ + BM * KRB + BN * KRBW + c * 256);        \
-        }                                                                                \
-      }                                                                                  \
-    }                                                                                    \
-  } while (0)
-#define MOE_ISSUE(KS) MOE_ISSUE_PART(KS, true, true)
-
-    // FP8: the weight block scales of this tile are wave-uniform and
-    // read-only; they are loaded through the scalar cache (constant address
-    // space) one k-step ahead, off the vector-memory counter that orders the
-    // DMA ring.
-    typedef __attribute__((address_space(4))) const float cfloat;
-    const cfloat* sbp0 = nullptr;
-    const cfloat* sbp1 = nullptr;
-    float sb_cur0 = 0.f, sb_cur1 = 0.f, sb_nxt0 = 0.f, sb_nxt1 = 0.f;
-    if constexpr (DT == kFP8) {
-      const int nb = (PHASE == 1) ? static_cast<int>(n0 / 256)  // 128 f columns per tile
-                                  : static_cast<int>((n0 + wn * WTN) / 128);
-      const int64_t base = static_cast<int64_t>(e) * kblocks * nblocks + nb;
-      sbp0 = (const cfloat*)(g.sb0) + base;
-      sbp1 = (PHASE == 1) ? (const cfloat*)(g.sb1) + base : sbp0;
-      sb_nxt0 = sbp0[0];
-      sb_nxt1 = (PHASE == 1) ? sbp1[0] : 0.f;
-    }
-
-    f32x4 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < ksteps) MOE_ISSUE(p);
-
-    for (int ks = 0; ks < ksteps; ++ks) {
-      // my loads of stage ks have landed once at most `ahead` later stages
-      // are still in flight; the barrier then publishes everyone's loads and
-      // guarantees every wave is done with the slot reloaded below
-      const int ahead = min(NS - 2, ksteps - 1 - ks);
-      wait_vmcnt(ahead * my_loads);
-      ring_barrier();
-      if (ks == k_pull && tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
-      // bf16 stages hold two MFMA k-steps: the weight rows of the next stage
-      // are requested after the first one, which spreads the DMA's LDS writes
-      // over the stage instead of piling them onto its first fragment reads
-      constexpr bool kSplitDma = (DT == kBF16) && (KRB / 64 == 2);
-      const bool refill = ks + NS - 1 < ksteps;
-      if (refill) MOE_ISSUE_PART(ks + NS - 1, true, !kSplitDma);
-      if constexpr (DT == kFP8) {
-        sb_cur0 = sb_nxt0;
-        sb_cur1 = sb_nxt1;
-        if (ks + 1 < ksteps) {
-          sb_nxt0 = sbp0[static_cast<int64_t>(ks + 1) * nblocks];
-          if (PHASE == 1) sb_nxt1 = sbp1[static_cast<int64_t>(ks + 1) * nblocks];
-        }
-      }
-      const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
-      const uint8_t* Bb = Ab + BM * KRB;
-      const uint8_t* Sb = Bb + BN * KRBW;  // per-stage scale dwords
-      // A wave whose rows are all padding skips the step; a partly valid
-      // wave computes its padding rows too (their results are never stored),
-      // which keeps the fragment loop free of branches.
-      const bool compute = wm * WTM < rows;
-      if constexpr (DT == kBF16) {
-#pragma unroll
-        for (int kk = 0; kk < KRB / 64; ++kk) {
-          if (kSplitDma && kk == 1 && refill) MOE_ISSUE_PART(ks + NS - 1, false, true);
-          if (!compute) continue;
-          bf16x8 wf[TN];
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            wf[j] = *reinterpret_cast<const bf16x8*>(
-                Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
-#define MOE_BF16_ROWS(SKIP)                                                               \
-  bf16x8 xf[TM];                                                                          \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>( \
-      Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));                               \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
-    if (SKIP) break;                                                                      \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0); \
-  }                                                                                       \
-  /* issue every fragment read of the step before the MFMAs (LDS latency  */              \
-  /* then overlaps the MFMAs instead of stalling each pair of fragments)  */              \
-  __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                                \
-  __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-          MOE_BF16_ROWS(false)
-#undef MOE_BF16_ROWS
-        }
-      } else if constexpr (DT == kF32) {
-        if (!compute) continue;
-        f32x4 wf[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz<KRB>(wn * WTN + 16 * j + l16, lg));
-#define MOE_F32_ROWS(SKIP)                                                                \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
-    if (SKIP) break;                                                                      \
-    const f32x4 xf =                                                                      \
-        *reinterpret_cast<const f32x4*>(Ab + swz<KRB>(wm * WTM + 16 * i + l16, lg));      \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                         \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j][u], xf[u], acc[i][j], 0, 0, 0); \
-  }
-        MOE_F32_ROWS(false)
-#undef MOE_F32_ROWS
-      } else if constexpr (MX) {
-        // FP4 weights x MX FP8 activations: one scaled 16x16x128 MFMA per
-        // fragment pair; the E8M0 block scales are MFMA operands.  Measured
-        // operand layout: FP4 lane group lg holds 32 elements in its 16 bytes
-        // (low nibble first) and, in both operands, lane group lg's scale
-        // byte governs exactly those 32 elements; FP8 lane group lg pairs its
-        // bytes 0-15 and 16-31 with half (lg & 1) of FP4 groups lg >> 1 and
-        // (lg >> 1) + 2.  So contraction block lg (32 elements) of the step
-        // goes to FP4 lane group lg in order, the FP8 lanes take 16-byte
-        // chunks lg and lg + 4 of the activation row, and each lane passes
-        // its own row's scale byte of block lg.
-        if (!compute) continue;
-        const uint32_t* sa_st = reinterpret_cast<const uint32_t*>(Sb);
-        const uint32_t* sw_st = sa_st + G::SA_DMA * 64;
-        i32x8 wf[TN];
-        int wsc[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int r = wn * WTN + 16 * j + l16;
-          const i32x4 c = *reinterpret_cast<const i32x4*>(Bb + swz<KRBW>(r, lg));
-          wf[j] = i32x8{c[0], c[1], c[2], c[3], 0, 0, 0, 0};
-          wsc[j] = static_cast<int>((sw_st[r] >> (8 * lg)) & 0xffu);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = wm * WTM + 16 * i + l16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, lg));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, lg + 4));
-          const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const int xsc = static_cast<int>((sa_st[r] >> (8 * lg)) & 0xffu);
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 4, 0,
-                                                                         0, wsc[j], 0, xsc);
-        }
-      } else {  // FP8: one 16x16x128 MFMA per fragment pair and 128-K block
-        if (!compute) continue;
-        i32x8 wf[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int r = wn * WTN + 16 * j + l16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
-          wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        const float* sa_st = reinterpret_cast<const float*>(Sb);
-        const float s_b0 = sb_cur0, s_b1 = sb_cur1;
-        if constexpr (PHASE == 1) {
-          // Row by row: the TN block products of row i are issued before the
-          // scaled accumulation of row i-1, so the fp32 fmas overlap MFMAs.
-          f32x4 pp[TN];
-          float spg = 0.f, spu = 0.f;
-#pragma unroll
-          for (int i = 0; i <= TM; ++i) {
-            f32x4 pc[TN];
-            float scg = 0.f, scu = 0.f;
-            if (i < TM) {
-              const int r = wm * WTM + 16 * i + l16;
-              const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
-              const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
-              const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              const float s_a = sa_st[r];
-              scg = s_a * s_b0;
-              scu = s_a * s_b1;
-#pragma unroll
-              for (int j = 0; j < TN; ++j)
-                pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            }
-            if (i > 0) {
-#pragma unroll
-              for (int j = 0; j < TN; ++j) {
-                const float sc = (PHASE == 1 && (j & 1)) ? spu : spg;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  acc[i - 1][j][q] = __builtin_fmaf(pp[j][q], sc, acc[i - 1][j][q]);
-              }
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) pp[j] = pc[j];
-            spg = scg;
-            spu = scu;
-          }
-        } else {  // (measured: the lagged form loses here, to register pressure)
-          // per row of fragments: the TN block products first (independent
-          // MFMAs in flight), then their scaled accumulation
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const int r = wm * WTM + 16 * i + l16;
-            const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
-            const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
-            const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const float s_a = sa_st[r];
-            const float sg = s_a * s_b0, su = s_a * s_b1;
-            f32x4 p[TN];
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const float sc = (PHASE == 1 && (j & 1)) ? su : sg;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(p[j][q], sc, acc[i][j][q]);
-            }
-          }
-        }
-      }
-    }
-#undef MOE_ISSUE
-#undef MOE_ISSUE_PART
-
-    // ---------------- epilogue ----------------
-    // Output rows are staged in LDS (free after the main loop's last
-    // barrier) so that every global store is a 16-byte piece of a contiguous
-    // row segment: the whole tile in one pass when it fits in the ring, else
-    // one pass per wave row.  Staged rows are XOR-swizzled by 16-byte chunk to
-    // keep the fragment writes off a single bank group.
-    {
-      constexpr int OUT_COLS = (PHASE == 1) ? BN / 2 : BN;
-      constexpr int OUT_ES = (PHASE == 1) ? ES : 4;
-      constexpr int ROWB = OUT_COLS * OUT_ES;
-      constexpr int CPR = ROWB / 16;
-      constexpr int XM = (CPR >= 16 ? 16 : CPR) - 1;
-      constexpr int PASSES = (BM * ROWB <= G::RING - 16) ? 1 : WM;
-      constexpr int PROWS = BM / PASSES;  // rows per pass
-      static_assert(PROWS * ROWB <= (G::RING > G::EPI ? G::RING : G::EPI), "staging fits");
-      uint8_t* stage = lds;
-      auto st_off = [&](int r, int cbyte) {
-        return r * ROWB + ((((cbyte >> 4) ^ (r & XM)) << 4) | (cbyte & 15));
-      };
-      const int64_t col0 = (PHASE == 1) ? n0 / 2 : n0;
-
-      if constexpr (PHASE == 1 && DT == kFP8) {
-        // h = SiLU(gate) * up in fp32 (in place), then the row amax over the
-        // tile's 128 f columns: lanes, then the WN waves through LDS
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          float m = 0.f;
-#pragma unroll
-          for (int p = 0; p < TN / 2; ++p)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              acc[i][2 * p][r] = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
-              m = fmaxf(m, fabsf(acc[i][2 * p][r]));
-            }
-          m = fmaxf(m, __shfl_xor(m, 16, 64));
-          m = fmaxf(m, __shfl_xor(m, 32, 64));
-          if (lg == 0) red[wn * BM + wm * WTM + 16 * i + l16] = m;
-        }
-      }
-      __syncthreads();  // every wave is done with the ring (and the row maxima are in)
-
-      for (int pass = 0; pass < PASSES; ++pass) {
-        if ((wm * WTM) / PROWS == pass) {
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const int lr = wm * WTM + 16 * i + l16;  // row within the tile
-            const int r = lr - pass * PROWS;          // row within this pass
-            if constexpr (PHASE == 2) {
-#pragma unroll
-              for (int j = 0; j < TN; ++j)
-                *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
-                    acc[i][j];
-            } else if constexpr (MX) {
-              // h = SiLU(gate) * up; each block of 32 h columns (two 16-column
-              // fragments, held by the four lanes of this row) gets its MX FP8
-              // exponent from the block amax, then E4M3 codes of h * 2^-X
-#pragma unroll
-              for (int qb = 0; qb < TN / 4; ++qb) {
-                float h[2][4];
-                float m = 0.f;
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                  const int p = 2 * qb + pp;
-#pragma unroll
-                  for (int q4 = 0; q4 < 4; ++q4) {
-                    h[pp][q4] = silu(acc[i][2 * p][q4]) * acc[i][2 * p + 1][q4];
-                    m = fmaxf(m, fabsf(h[pp][q4]));
-                  }
-                }
-                m = fmaxf(m, __shfl_xor(m, 16, 64));
-                m = fmaxf(m, __shfl_xor(m, 32, 64));
-                const int x = mx_exponent_e4m3(m);
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                  uint32_t packed = 0;
-#pragma unroll
-                  for (int q4 = 0; q4 < 4; ++q4)
-                    packed |= f32_to_e4m3(__builtin_ldexpf(h[pp][q4], -x)) << (8 * q4);
-                  *reinterpret_cast<uint32_t*>(
-                      stage + st_off(r, wn * (WTN / 2) + 16 * (2 * qb + pp) + 4 * lg)) = packed;
-                }
-                if (lg == 0 && lr < rows)
-                  reinterpret_cast<uint8_t*>(g.sc)[static_cast<int64_t>(row0 + lr) * (N / 32) +
-                                                   (col0 + wn * (WTN / 2) + 32 * qb) / 32] =
-                      static_cast<uint8_t>(x + 127);
-              }
-            } else if constexpr (DT == kFP8) {
-              float amax = 0.f;
-#pragma unroll
-              for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + lr]);
-              const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
-#pragma unroll
-              for (int p = 0; p < TN / 2; ++p) {
-                uint32_t packed = 0;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                  packed |= f32_to_e4m3(__fdiv_rn(acc[i][2 * p][q4], sc)) << (8 * q4);
-                *reinterpret_cast<uint32_t*>(stage + st_off(r, wn * (WTN / 2) + 16 * p + 4 * lg)) =
-                    packed;
-              }
-              if (wn == 0 && lg == 0 && lr < rows)
-                g.sc[static_cast<int64_t>(row0 + lr) * (N / 128) + n0 / 256] = sc;
-            } else {
-#pragma unroll
-              for (int p = 0; p < TN / 2; ++p) {
-                float h[4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                  h[q4] = silu(acc[i][2 * p][q4]) * acc[i][2 * p + 1][q4];
-                const int cb = (wn * (WTN / 2) + 16 * p + 4 * lg) * ES;
-                if constexpr (DT == kBF16) {
-                  u32x2 v;
-                  v.x = f32_to_bf16_rne(h[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[1])) << 16);
-                  v.y = f32_to_bf16_rne(h[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(h[3])) << 16);
-                  *reinterpret_cast<u32x2*>(stage + st_off(r, cb)) = v;
-                } else {
-                  *reinterpret_cast<f32x4*>(stage + st_off(r, cb)) = f32x4{h[0], h[1], h[2], h[3]};
-                }
-              }
-            }
-          }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < PROWS * CPR; idx += kThreads) {
-          const int r = idx / CPR, c = idx - r * CPR;
-          const int lr = pass * PROWS + r;
-          const int64_t col = col0 + c * (16 / OUT_ES);
-          if (lr < rows && col < N)
-            *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(row0 + lr) * N + col) * OUT_ES) =
-                *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
-        }
-        if (pass + 1 < PASSES) __syncthreads();
-      }
-    }
+    gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_>(
+        g, mt, nt, -1,
+        [&] {
+          if (tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
+        },
+        [] {});
 
     // hand over the next task; the barriers also separate this task's last
     // LDS reads from the hand-over slot write and from the next task's
