@@ -237,6 +237,29 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
                        const void *W2s, void *out, void *ws, size_t ws_bytes,
                        const moe_debug *dbg, hipStream_t stream);
 
+/* The same layer forward with both expert GEMMs in ONE persistent launch
+ * that hands h from the W1/W3 tasks to the W2 tasks through a bounded ring:
+ * the ring of in-flight blocks (sized by blocks in flight, not by routed
+ * tokens) and the L1/L2 full and empty counters of the MegaMoE-vs-MoE-systems
+ * page, sections 2.3 and 2.7.  Each XCD's task queue runs, step by step, the
+ * W1/W3 tasks of one work chunk and then the W2 tasks of the previous chunk;
+ * a W2 task waits until every W1/W3 task of its chunk has published its h
+ * columns, and a W1/W3 task waits for its ring slot to be empty before
+ * storing h.  h therefore needs 24 chunk-sized slots instead of T*k rows
+ * (moe_ring_workspace_size); Y and everything else are as in moe_forward,
+ * and the outputs are bit-identical to moe_forward's.
+ * Supported: act_dtype = w_dtype = MOE_BF16 with 256-row tiles (block_m 256,
+ * or block_m 0 when T*top_k/E picks 256); otherwise MOE_ERR_UNSUPPORTED.
+ * Arguments as in moe_forward (no weight scales); ws must hold
+ * moe_ring_workspace_size() bytes.  The waits inside the launch are bounded:
+ * a wait that exceeds its poll limit (seconds) gives up, so the call cannot
+ * hang the device, but its output is then wrong. */
+moe_status moe_ring_workspace_size(const moe_problem *p, size_t *bytes);
+moe_status moe_forward_ring(const moe_problem *p, const void *x, const void *gate_w,
+                            const float *bias, const void *W1t, const void *W3t,
+                            const void *W2t, void *out, void *ws, size_t ws_bytes,
+                            const moe_debug *dbg, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

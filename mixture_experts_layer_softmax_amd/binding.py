@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ["moe_status_string", "moe_last_hip_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_quantize_fp8", "moe_quantize_mx", "moe_weight_bytes",
-           "moe_pack_weight", "moe_forward"]
+           "moe_pack_weight", "moe_forward", "moe_ring_workspace_size", "moe_forward_ring"]
 
 
 class MoEProblem(ctypes.Structure):
@@ -78,6 +78,8 @@ def load(path: str = LIB_PATH):
                                     ctypes.c_int32, P, P, P]
     lib.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, S,
                                 ctypes.POINTER(MoEDebug), P]
+    lib.moe_ring_workspace_size.argtypes = [PP, ctypes.POINTER(S)]
+    lib.moe_forward_ring.argtypes = [PP, P, P, P, P, P, P, P, P, S, ctypes.POINTER(MoEDebug), P]
     for fn in EXPORTS:
         if fn not in ("moe_status_string", "moe_last_hip_error"):
             getattr(lib, fn).restype = ctypes.c_int
@@ -132,6 +134,13 @@ def alloc_workspace(p: MoEProblem, device="cuda") -> torch.Tensor:
     return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
 
 
+def ring_workspace_size(p: MoEProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_ring_workspace_size",
+           load().moe_ring_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
 def moe_route(p, x, gate_w, bias, logits, topk_ids, topk_w, ws=None, stream=None):
     rc = load().moe_route(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(logits),
                           _p(topk_ids), _p(topk_w), _p(ws),
@@ -169,18 +178,30 @@ def moe_pack_weight(src, dst, stream=None):
 
 def moe_forward(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, dbg=None,
                 stream=None):
-    dbg_s = None
-    if dbg is not None:
-        dbg_s = MoEDebug(*[None if dbg.get(n) is None else dbg[n].data_ptr()
-                           for n in DEBUG_BUFFERS])
-        for i, ev in enumerate(dbg.get("stage_events") or []):
-            dbg_s.stage_events[i] = ev
-        if dbg.get("gemm_clock") is not None:  # int64 tensor [2][2]
-            dbg_s.gemm_clock = dbg["gemm_clock"].data_ptr()
+    dbg_s = _debug_struct(dbg)
     rc = load().moe_forward(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(W1t), _p(W3t),
                             _p(W2t), _p(W1s), _p(W3s), _p(W2s), _p(out), _p(ws), ws.numel(),
                             None if dbg_s is None else ctypes.byref(dbg_s), _stream(stream))
     _check("moe_forward", rc)
+
+
+def _debug_struct(dbg):
+    if dbg is None:
+        return None
+    dbg_s = MoEDebug(*[None if dbg.get(n) is None else dbg[n].data_ptr() for n in DEBUG_BUFFERS])
+    for i, ev in enumerate(dbg.get("stage_events") or []):
+        dbg_s.stage_events[i] = ev
+    if dbg.get("gemm_clock") is not None:
+        dbg_s.gemm_clock = dbg["gemm_clock"].data_ptr()
+    return dbg_s
+
+
+def moe_forward_ring(p, x, gate_w, bias, W1t, W3t, W2t, out, ws, dbg=None, stream=None):
+    dbg_s = _debug_struct(dbg)
+    rc = load().moe_forward_ring(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(W1t),
+                                 _p(W3t), _p(W2t), _p(out), _p(ws), ws.numel(),
+                                 None if dbg_s is None else ctypes.byref(dbg_s), _stream(stream))
+    _check("moe_forward_ring", rc)
 
 
 # ---------------------------------------------------------------------------
@@ -220,15 +241,21 @@ def out_tensor(cfg, T=None, device="cuda", out_dtype=None):
 
 
 def forward(cfg, inp: dict, packed: dict, out=None, ws=None, dbg=None, out_dtype=None,
-            block_m=0, stream=None):
-    """Whole-layer forward of cfg on resident inputs; returns the output tensor."""
+            block_m=0, stream=None, ring=False):
+    """Whole-layer forward of cfg on resident inputs; returns the output tensor.
+    ring=True runs moe_forward_ring (both GEMMs in one launch, h in a ring)."""
     T = inp["x"].shape[0]
     p = problem_of(cfg, T=T, block_m=block_m, out_dtype=out_dtype)
     if out is None:
         out = out_tensor(cfg, T=T, device=inp["x"].device, out_dtype=out_dtype)
     if ws is None:
-        ws = alloc_workspace(p, inp["x"].device)
-    moe_forward(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"], packed["W3t"],
-                packed["W2t"], packed.get("W1s"), packed.get("W3s"), packed.get("W2s"), out,
-                ws, dbg=dbg, stream=stream)
+        size = ring_workspace_size(p) if ring else workspace_size(p)
+        ws = torch.empty(size, dtype=torch.uint8, device=inp["x"].device)
+    if ring:
+        moe_forward_ring(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"],
+                         packed["W3t"], packed["W2t"], out, ws, dbg=dbg, stream=stream)
+    else:
+        moe_forward(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"], packed["W3t"],
+                    packed["W2t"], packed.get("W1s"), packed.get("W3s"), packed.get("W2s"), out,
+                    ws, dbg=dbg, stream=stream)
     return out

@@ -97,12 +97,20 @@ struct Layout {
   size_t logits, ids, w, table, counts, offsets, slot_token, slot_k, token_slot;
   size_t tm_e, tm_row0, tm_rows, tm_misc;
   size_t xq, sx, hs, h, y;
+  size_t ring_ctrl;  // ring layout: queue[8], l1_done[max_mtiles], l2_done[max_mtiles], err
   size_t total;
   int bm;
   int64_t max_mtiles;
 };
 
-Layout make_layout(const moe_problem& p) {
+// Ring slots per XCD of the single-launch pipeline: chunk j's h waits in slot
+// j % kRingSlots until its W2 tasks are done (two steps of the queue later at
+// the earliest), so two slots already never block; a third absorbs W2 tasks
+// that finish late.
+constexpr int kRingSlots = 3;
+int64_t ring_ctrl_words(int64_t max_mtiles) { return 8 + 2 * max_mtiles + 1; }
+
+Layout make_layout(const moe_problem& p, bool ring = false) {
   Layout L{};
   const int64_t n = p.T * p.top_k;
   const int64_t nchunk = ceil_div(n, moe::permute_chunk(n));
@@ -134,8 +142,13 @@ Layout make_layout(const moe_problem& p) {
   L.xq = take(fp8 || mx ? static_cast<size_t>(p.T) * p.d : 0);
   L.sx = take(fp8 ? sizeof(float) * p.T * (p.d / 128) : (mx ? p.T * (p.d / 32) : 0));
   L.hs = take(fp8 ? sizeof(float) * rows * (p.f / 128) : (mx ? rows * (p.f / 32) : 0));
-  L.h = take(static_cast<size_t>(rows) * p.f * (fp8 || mx ? 1 : esize(p.act_dtype)));
+  if (ring)  // h only for the chunks in flight: 8 XCDs x kRingSlots x group_m tiles
+    L.h = take(static_cast<size_t>(8 * kRingSlots) * group_m(p, L.bm) * L.bm * p.f *
+               esize(p.act_dtype));
+  else
+    L.h = take(static_cast<size_t>(rows) * p.f * (fp8 || mx ? 1 : esize(p.act_dtype)));
   L.y = take(sizeof(float) * rows * p.d);
+  L.ring_ctrl = take(ring ? sizeof(int32_t) * ring_ctrl_words(L.max_mtiles) : 0);
   L.total = off;
   return L;
 }
@@ -270,18 +283,33 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes, 
   return hip_status();
 }
 
-moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, const float* bias,
-                       const void* W1t, const void* W3t, const void* W2t, const void* W1s,
-                       const void* W3s, const void* W2s, void* out, void* ws, size_t ws_bytes,
-                       const moe_debug* dbg, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The single-launch pipeline covers bf16 layers with 256-row tiles (and task
+// codes below 2^24: queue << 24 | pull index).
+bool ring_supported(const moe_problem& p) {
+  if (p.act_dtype != MOE_BF16 || p.w_dtype != MOE_BF16 || pick_bm(p) != 256) return false;
+  const int64_t gm = group_m(p, 256);
+  const int64_t tiles = (gemm_rows(p) + static_cast<int64_t>(p.E + p.n_shared) * 255) / 256 + 1;
+  const int64_t per_step = gm * (ceil_div(2 * p.f, 256) + ceil_div(p.d, 256));
+  return (ceil_div(ceil_div(tiles, gm), 8) + 1) * per_step < (1ll << 24);
+}
+
+moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
+                        const float* bias, const void* W1t, const void* W3t, const void* W2t,
+                        const void* W1s, const void* W3s, const void* W2s, void* out, void* ws,
+                        size_t ws_bytes, const moe_debug* dbg, hipStream_t stream, bool ring) {
   if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
   if (!supported_shape(p)) return MOE_ERR_UNSUPPORTED;
+  if (ring && !ring_supported(*p)) return MOE_ERR_UNSUPPORTED;
   if (p->T == 0) return MOE_OK;
   if (!x || !gate_w || !W1t || !W3t || !W2t || !out || !ws) return MOE_ERR_INVALID_ARG;
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3, mx = p->w_dtype == MOE_MXFP4;
   const bool q8 = fp8 || mx;  // the GEMMs read 1-byte activation codes + scales
   if (q8 && (!W1s || !W3s || !W2s)) return MOE_ERR_INVALID_ARG;
-  const Layout L = make_layout(*p);
+  const Layout L = make_layout(*p, ring);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
   const int T = static_cast<int>(p->T), d = static_cast<int>(p->d);
@@ -343,9 +371,11 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   g1.queue_idx = 0;
   g1.group_m = group_m(*p, L.bm);
   g1.clock = dbg ? dbg->gemm_clock : nullptr;
-  st = from_code(moe::launch_gemm(1, gdt, L.bm, g1, stream));
-  if (st != MOE_OK) return st;
-  mark(4);
+  if (!ring) {
+    st = from_code(moe::launch_gemm(1, gdt, L.bm, g1, stream));
+    if (st != MOE_OK) return st;
+    mark(4);
+  }
 
   // 5. W2
   moe::GemmArgs g2{};
@@ -366,8 +396,27 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
   g2.queue_idx = 1;
   g2.group_m = g1.group_m;
   g2.clock = (dbg && dbg->gemm_clock) ? dbg->gemm_clock + 2 : nullptr;
-  st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));
-  if (st != MOE_OK) return st;
+  if (!ring) {
+    st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));
+    if (st != MOE_OK) return st;
+  } else {
+    // both GEMMs in one launch; h lives in the ring, Y in full
+    moe::RingArgs r{};
+    int32_t* ctrl = at<int32_t>(ws, L.ring_ctrl);
+    r.h = at<uint8_t>(ws, L.h);
+    r.queue = ctrl;
+    r.l1_done = ctrl + 8;
+    r.l2_done = ctrl + 8 + L.max_mtiles;
+    r.err = ctrl + 8 + 2 * L.max_mtiles;
+    r.slots = kRingSlots;
+    g1.C = r.h;
+    g2.A = r.h;
+    g1.clock = g2.clock = nullptr;
+    moe::launch_zero(ctrl, ring_ctrl_words(L.max_mtiles), stream);
+    st = from_code(moe::launch_gemm_ring(g1, g2, r, stream));
+    if (st != MOE_OK) return st;
+    mark(4);
+  }
   mark(5);
 
   // 6. combine
@@ -388,6 +437,33 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
     cp(dbg->token_slot, token_slot, sizeof(int32_t) * n);
   }
   return hip_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, const float* bias,
+                       const void* W1t, const void* W3t, const void* W2t, const void* W1s,
+                       const void* W3s, const void* W2s, void* out, void* ws, size_t ws_bytes,
+                       const moe_debug* dbg, hipStream_t stream) {
+  return forward_impl(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, ws_bytes, dbg,
+                      stream, false);
+}
+
+moe_status moe_ring_workspace_size(const moe_problem* p, size_t* bytes) {
+  if (!bytes || !valid_problem(p)) return MOE_ERR_INVALID_ARG;
+  if (!supported_shape(p) || !ring_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  *bytes = make_layout(*p, true).total;
+  return MOE_OK;
+}
+
+moe_status moe_forward_ring(const moe_problem* p, const void* x, const void* gate_w,
+                            const float* bias, const void* W1t, const void* W3t, const void* W2t,
+                            void* out, void* ws, size_t ws_bytes, const moe_debug* dbg,
+                            hipStream_t stream) {
+  return forward_impl(p, x, gate_w, bias, W1t, W3t, W2t, nullptr, nullptr, nullptr, out, ws,
+                      ws_bytes, dbg, stream, true);
 }
 
 }  // extern "C"

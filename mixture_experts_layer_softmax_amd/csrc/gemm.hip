@@ -208,7 +208,8 @@ struct TaskQueue {
 template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, class KPull,
           class PreEpi>
 __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const int nt,
-                                          const int64_t hrow_base, KPull&& kpull,
+                                          const int64_t arow_base, const int64_t crow_base,
+                                          KPull&& kpull,
                                           PreEpi&& pre_epi) {
   using G = Geo<DT, PHASE, BM, BN, WM, WN, KRB_>;
   constexpr int kThreads = G::kThreads, ES = G::ES, KRB = G::KRB, NS = G::NS;
@@ -237,9 +238,11 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
   const int k_pull = max(0, ksteps - 4);
   const int e = __builtin_amdgcn_readfirstlane(g.tm.e[mt]);
   const int row0 = __builtin_amdgcn_readfirstlane(g.tm.row0[mt]);
-  // rows of the A operand (when not gathered) and of C: the slot rows, or
-  // hrow_base.. when the caller places this m-tile elsewhere
-  const int64_t hrow = hrow_base >= 0 ? hrow_base : row0;
+  // first row of the A operand (when not gathered) and of C: the slot row
+  // row0, or arow_base / crow_base when the caller places this m-tile's rows
+  // elsewhere (negative: row0)
+  const int64_t arow = arow_base >= 0 ? arow_base : row0;
+  const int64_t crow = crow_base >= 0 ? crow_base : row0;
   const int rows = __builtin_amdgcn_readfirstlane(g.tm.rows[mt]);
   const int64_t n0 = static_cast<int64_t>(nt) * BN;
 
@@ -265,7 +268,7 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
     const int r = q * RPD + lrow;
     const int logical = lphys ^ swz_key<KRB>(r);
     const int rr = min(r, rows - 1);  // padding rows re-read a valid row
-    const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(hrow + rr);
+    const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(arow + rr);
     oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + logical * 16);
     if (q < G::ABLK) ++my_loads;
   }
@@ -702,7 +705,7 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
         const int lr = pass * PROWS + r;
         const int64_t col = col0 + c * (16 / OUT_ES);
         if (lr < rows && col < N)
-          *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(hrow + lr) * N + col) * OUT_ES) =
+          *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(crow + lr) * N + col) * OUT_ES) =
               *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
       }
       if (pass + 1 < PASSES) __syncthreads();
@@ -755,7 +758,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     const int mt = task / NT;
     const int nt = task - mt * NT;
     gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_>(
-        g, mt, nt, -1,
+        g, mt, nt, -1, -1,
         [&] {
           if (tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
         },
@@ -783,6 +786,143 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     const uint64_t ref = __builtin_amdgcn_s_memrealtime() - ref0;
     g.clock[0] = clk;
     g.clock[1] = ref;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Single-launch pipeline: W1/W3 and W2 tasks in one persistent grid, h passed
+// through a bounded ring with full / empty counters per chunk (the ring of
+// in-flight blocks and the L1/L2 full and empty counters of the
+// MegaMoE-vs-MoE-systems page, sections 2.3 and 2.7).  h crosses XCDs (a
+// W1/W3 task may be stolen by another XCD), so the full count is published
+// with an agent-scope release after the h stores and awaited with an
+// agent-scope acquire before the W2 task's first h load: the L2 write-back
+// and invalidation those imply are what makes h coherent across the per-XCD
+// L2s.  Waits are bounded: a wait that exceeds kRingSpin polls gives up, sets
+// RingArgs::err and lets the task run on (its output is then wrong, never a
+// hang).
+constexpr int kRingSpin = 1 << 22;
+
+__device__ inline void ring_wait(int32_t* cnt, int need, bool acquire, int32_t* err) {
+  for (int it = 0;; ++it) {
+    const int v = acquire ? __hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+                          : __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v >= need) return;
+    if (it >= kRingSpin) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, GemmArgs g2,
+                                                                 RingArgs r) {
+  using G1 = Geo<kBF16, 1, BM, BN, WM, WN, 128>;
+  using G2 = Geo<kBF16, 2, BM, BN, WM, WN, 128>;
+  static_assert(G1::RING == G2::RING, "one LDS ring for both phases");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  int& s_task = *reinterpret_cast<int*>(lds + G1::RING - 16);  // as in grouped_gemm_kernel
+  const int tid = threadIdx.x;
+  const int M = *g1.tm.n_mtiles, GM = g1.group_m, NT1 = g1.n_tiles_n, NT2 = g2.n_tiles_n;
+  const int nchunks = (M + GM - 1) / GM;
+  const int xcd = static_cast<int>(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) &
+                                   (kXcd - 1));
+  const int per_step = GM * (NT1 + NT2);
+  auto owned = [&](int y) { return nchunks > y ? (nchunks - y + kXcd - 1) / kXcd : 0; };
+  auto limit = [&](int y) { return (owned(y) + 1) * per_step; };
+  // pull v of queue y -> (phase, chunk index j of that queue, m-tile, n-tile);
+  // false for a hole (no such chunk, or past the last m-tile)
+  auto decode = [&](int v, int y, int& phase, int& j, int& mt, int& nt) {
+    const int st = v / per_step, p = v - st * per_step;
+    int ml;
+    if (p < GM * NT1) {
+      phase = 1;
+      j = st;
+      ml = p % GM;
+      nt = p / GM;
+    } else {
+      phase = 2;
+      j = st - 1;
+      ml = (p - GM * NT1) % GM;
+      nt = (p - GM * NT1) / GM;
+    }
+    if (j < 0 || j >= owned(y)) return false;
+    mt = (y + kXcd * j) * GM + ml;
+    return mt < M;
+  };
+  // task codes: (queue << 24) | pull index
+  auto pull = [&](int s0) {
+    for (int s = s0; s < kXcd; ++s) {
+      const int y = (xcd + s) % kXcd;
+      const int lim = limit(y);
+      for (;;) {
+        if (__hip_atomic_load(&r.queue[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= lim)
+          break;
+        const int v = atomicAdd(&r.queue[y], 1);
+        if (v >= lim) break;
+        int ph, j, mt, nt;
+        if (decode(v, y, ph, j, mt, nt)) return (y << 24) | v;
+      }
+    }
+    return -1;
+  };
+  bool own_open = true;
+  if (tid == 0) s_task = pull(0);
+  __syncthreads();
+  for (;;) {
+    const int code = __builtin_amdgcn_readfirstlane(s_task);
+    if (code < 0) break;
+    const int y = code >> 24;
+    int phase, j, mt, nt;
+    decode(code & 0xffffff, y, phase, j, mt, nt);
+    const int c = y + kXcd * j;  // chunk of the tile map
+    const int64_t ring_row =
+        (static_cast<int64_t>(y * r.slots + j % r.slots) * GM + (mt - c * GM)) * BM;
+    int next_v = -1;
+    auto kpull = [&] {
+      if (tid == 0 && own_open) next_v = atomicAdd(&r.queue[xcd], 1);
+    };
+    if (phase == 1) {
+      // before the h stores: the W2 tasks of the chunk that used this ring
+      // slot before (slots steps earlier in the same queue) are all done
+      auto slot_free = [&] {
+        if (j >= r.slots) {
+          const int cp = y + kXcd * (j - r.slots);
+          if (tid == 0) ring_wait(&r.l2_done[cp], min(GM, M - cp * GM) * NT2, false, r.err);
+          __syncthreads();
+        }
+      };
+      gemm_task<kBF16, 1, BM, BN, WM, WN, 128>(g1, mt, nt, -1, ring_row, kpull, slot_free);
+      wait_vmcnt(0);  // this wave's h stores are done
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(&r.l1_done[c], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // every W1/W3 task of the chunk has published its h columns
+      if (tid == 0) ring_wait(&r.l1_done[c], min(GM, M - c * GM) * NT1, true, r.err);
+      __syncthreads();
+      gemm_task<kBF16, 2, BM, BN, WM, WN, 128>(g2, mt, nt, ring_row, -1, kpull, [] {});
+      __syncthreads();  // (the task's h loads all landed before its last stage)
+      if (tid == 0) __hip_atomic_fetch_add(&r.l2_done[c], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // hand over the next task
+    __syncthreads();
+    if (tid == 0) {
+      int t = -1;
+      if (next_v >= 0) {
+        int ph, jj, m2, n2;
+        if (next_v < limit(xcd)) {
+          if (decode(next_v, xcd, ph, jj, m2, n2)) t = (xcd << 24) | next_v;
+        } else {
+          own_open = false;
+        }
+      }
+      if (t < 0) t = pull(own_open ? 0 : 1);
+      s_task = t;
+    }
+    __syncthreads();
   }
 }
 
@@ -892,6 +1032,29 @@ int launch_gemm(int phase, int dtype, int bm, const GemmArgs& a, hipStream_t s) 
 
 int gemm_tile_n(int phase, int dtype, int bm) {
   return dispatch(phase, dtype, bm, [&](auto v) { return decltype(v)::tile_n(); });
+}
+
+int launch_gemm_ring(const GemmArgs& g1, const GemmArgs& g2, const RingArgs& r, hipStream_t s) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+  using G1 = Geo<kBF16, 1, BM, BN, WM, WN, 128>;
+  using G2 = Geo<kBF16, 2, BM, BN, WM, WN, 128>;
+  constexpr int lds = G1::LDS > G2::LDS ? G1::LDS : G2::LDS;
+  auto kern = ring_gemm_kernel<BM, BN, WM, WN>;
+  static int grid = 0;
+  static hipError_t attr_err = hipSuccess;
+  static std::once_flag once;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    int dev = 0, cus = 0, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WM * WN * 64, lds);
+    grid = max(1, cus) * max(1, per_cu);
+  });
+  if (attr_err != hipSuccess) return static_cast<int>(attr_err);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WM * WN * 64), lds, s, g1, g2, r);
+  return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace moe

@@ -58,6 +58,20 @@ struct GemmArgs {
   uint64_t* clock;        // [2] or null: ticks of workgroup 0 (shader, 100 MHz reference)
 };
 
+// Single-launch W1/W3 -> W2 pipeline (bf16, 256 x 256 tiles) through a
+// bounded ring of h.  XCD y's queue runs steps s = 0, 1, ..: the W1/W3 tasks
+// of its chunk s, then the W2 tasks of its chunk s - 1.  Chunk j of XCD y
+// writes its h into ring slot y * slots + j % slots (group_m * 256 rows).
+// All counters are zeroed before the launch.
+struct RingArgs {
+  uint8_t* h;        // [8 * slots][group_m * 256 rows][f] bf16
+  int32_t* queue;    // [8] pull counters
+  int32_t* l1_done;  // [chunks] finished W1/W3 tasks per chunk (full count)
+  int32_t* l2_done;  // [chunks] finished W2 tasks per chunk (empty count)
+  int32_t* err;      // [1] set to 1 when a bounded wait gave up
+  int slots;         // ring slots per XCD (>= 2)
+};
+
 // Gate: logits [T][E] (+ bias), top-k ids and renormalised weights [T][k].
 void launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
                  int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s);
@@ -74,6 +88,11 @@ void launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, 
                      hipStream_t st);
 // Grouped GEMMs.  bm = tile height; returns a hipError_t.
 int launch_gemm(int phase, int dtype, int bm, const GemmArgs& a, hipStream_t s);
+// Both GEMMs in one launch through the h ring (bf16 weights, bm = 256); g1.C
+// and g2.A point at r.h.  Returns a hipError_t.
+int launch_gemm_ring(const GemmArgs& g1, const GemmArgs& g2, const RingArgs& r, hipStream_t s);
+// Zero n int32 words with a kernel (also inside a captured graph).
+void launch_zero(int32_t* p, int64_t n, hipStream_t s);
 // Column tiles per m-tile for a phase (depends on the kernel variant).
 int gemm_tile_n(int phase, int dtype, int bm);
 void launch_combine(const float* Y, const float* w, const int32_t* token_slot, void* out,

@@ -14,6 +14,8 @@
 // ballots so equal experts keep increasing q = t*k + j order.  When all the
 // pairs fit one chunk (decode), one workgroup does the three steps in a
 // single launch.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -214,7 +216,17 @@ __global__ __launch_bounds__(1024) void permute_one_kernel(
   if (tid < 64) scatter_run(ids, 0, n, k, nbits, s_tab, slot_token, slot_k, token_slot);
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) p[i] = 0;
+}
+
 }  // namespace
+
+void launch_zero(int32_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  zero_kernel<<<static_cast<int>(blocks), 256, 0, s>>>(p, n);
+}
 
 void launch_permute(const int32_t* ids, int T, int k, int E, int S, int bm, int32_t* table,
                     int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_k,

@@ -499,3 +499,86 @@ def test_random_config_parity(cfg, block_m):
     assert np.array_equal(dbg["topk_ids"].view(cfg.T, cfg.k).cpu().numpy(), ref_ids)
     _outputs_ok(cfg, out, ref, f"fp32 out bm={block_m}")
     _outputs_ok(cfg, _forward(cfg, inp, block_m=block_m), ref, "native out")
+
+
+# ---------------------------------------------------------------------------
+# single-launch pipeline (moe_forward_ring): both GEMMs in one persistent
+# launch with h in a bounded ring; outputs must equal moe_forward's bit for bit
+# ---------------------------------------------------------------------------
+
+RING = {
+    "prefill_bf16_r": REDUCED["prefill_bf16_r"],
+    "skewed_bf16_r": REDUCED["skewed_bf16_r"],
+    "sh_bf16": SHARED["sh_bf16"],
+    # many chunks per XCD queue, so ring slots are reused several times
+    "many_chunks": MoEConfig("many_chunks", 8000, 256, 256, 64, 2, BF16, BF16, BF16),
+    "one_expert": MoEConfig("one_expert", 700, 256, 128, 1, 1, BF16, BF16, BF16),
+}
+
+
+@pytest.mark.parametrize("name", list(RING))
+def test_ring_forward_equals_forward(name):
+    cfg = RING[name]
+    say("ring", name)
+    inp = gpu_inputs(cfg)
+    packed = B.pack_weights(inp)
+    for out_dtype in (F32, BF16):
+        ref = B.forward(cfg, inp, packed, out_dtype=out_dtype, block_m=256)
+        for rep in range(2):
+            got = B.forward(cfg, inp, packed, out_dtype=out_dtype, block_m=256, ring=True)
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref), (name, out_dtype, rep)
+    ref64, _, _ = oracle_forward_rows(cfg, inp, np.arange(min(cfg.T, 64)))
+    out = B.forward(cfg, inp, packed, out_dtype=F32, block_m=256, ring=True)
+    torch.cuda.synchronize()
+    _outputs_ok(cfg, out[: ref64.shape[0]], ref64, "ring vs oracle")
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16", "skewed_bf16", "prefill_bf16_shared"])
+def test_ring_full_size_equals_forward(name):
+    cfg = CONFIGS[name]
+    say("ring full", name)
+    inp = gpu_inputs(cfg)
+    packed = B.pack_weights(inp)
+    ref = B.forward(cfg, inp, packed)
+    got = B.forward(cfg, inp, packed, ring=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref), name
+    del inp, packed, ref, got
+    free()
+
+
+def test_ring_unsupported_shapes_launch_nothing():
+    for name in ("decode_bf16", "prefill_fp8_r", "tiny_fp32"):
+        cfg = CONFIGS.get(name) or REDUCED[name]
+        p = B.problem_of(cfg, T=min(cfg.T, 64))
+        with pytest.raises(B.MoEError, match="UNSUPPORTED"):
+            B.ring_workspace_size(p)
+
+
+def test_ring_graph_replay():
+    cfg = RING["many_chunks"]
+    say("ring graph")
+    inp = gpu_inputs(cfg)
+    packed = B.pack_weights(inp)
+    p = B.problem_of(cfg, block_m=256)
+    ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
+    out = B.out_tensor(cfg)
+    ref = B.forward(cfg, inp, packed, block_m=256)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        B.forward(cfg, inp, packed, out=out, ws=ws, block_m=256, stream=s, ring=True)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            B.forward(cfg, inp, packed, out=out, ws=ws, block_m=256, stream=s, ring=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(0)
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        del junk
