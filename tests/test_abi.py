@@ -112,3 +112,36 @@ def test_route_shape_rule():
     assert rc == 2
     rc = lib.moe_quantize_mx(4, 40, None, None, None, None)  # cols % 32
     assert rc == 1
+
+
+def test_ring_pipeline_sizes_and_checks():
+    # moe_forward_ring: bf16 layers with 256-row tiles only; its workspace
+    # holds h for 24 chunk slots (chunks of up to 8 m-tiles) instead of T*k
+    # rows, so once chunks are at their 8 m-tiles h no longer grows with T
+    _lib()
+    small = B.problem(65536, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_BF16, B.MOE_BF16)
+    big = B.problem(131072, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_BF16, B.MOE_BF16)
+    h_full = lambda p: p.T * p.top_k * p.f * 2  # noqa: E731
+    grow_full = B.workspace_size(big) - B.workspace_size(small)
+    grow_ring = B.ring_workspace_size(big) - B.ring_workspace_size(small)
+    dh = h_full(big) - h_full(small)
+    # the ring saves all of h's growth but the per-chunk counters (8 bytes a tile)
+    assert 0.999 * dh <= grow_full - grow_ring <= dh
+    assert B.ring_workspace_size(small) < B.workspace_size(small) - 0.5 * h_full(small)
+    for bad in (B.problem(64, 7168, 2048, 256, 8, B.MOE_BF16, B.MOE_BF16, B.MOE_BF16),  # 16-row tiles
+                B.problem(16384, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_FP8_E4M3, B.MOE_BF16),
+                B.problem(16384, 256, 256, 32, 2, B.MOE_F32, B.MOE_F32, B.MOE_F32)):
+        with pytest.raises(B.MoEError, match="UNSUPPORTED"):
+            B.ring_workspace_size(bad)
+    lib = B.load()
+    n = ctypes.c_size_t(0)
+    small = B.problem(16384, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_BF16, B.MOE_BF16)
+    assert lib.moe_ring_workspace_size(ctypes.byref(small), None) == 1
+    assert lib.moe_ring_workspace_size(ctypes.byref(small), ctypes.byref(n)) == 0
+    # null operands are rejected before anything is launched
+    rc = lib.moe_forward_ring(ctypes.byref(small), None, None, None, None, None, None, None,
+                              None, n.value, None, None)
+    assert rc == 1
+    rc = lib.moe_forward_ring(ctypes.byref(bad), None, None, None, None, None, None, None,
+                              None, 0, None, None)
+    assert rc == 2
