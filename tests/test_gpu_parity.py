@@ -582,3 +582,22 @@ def test_ring_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), rep
         del junk
+
+
+def test_ring_repeated_runs_identical():
+    # the ring's counters order every h handoff: thirty back-to-back runs of
+    # the full-size skewed layer (hot expert: the longest chunk chains, most
+    # stealing) must each reproduce moe_forward bit for bit
+    cfg = CONFIGS["skewed_bf16"]
+    say("ring repeated", cfg.name)
+    inp = gpu_inputs(cfg)
+    packed = B.pack_weights(inp)
+    ref = B.forward(cfg, inp, packed)
+    p = B.problem_of(cfg)
+    ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
+    outs = [B.forward(cfg, inp, packed, ws=ws, ring=True) for _ in range(30)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref), i
+    del inp, packed, ref, outs
+    free()
