@@ -132,6 +132,16 @@ typedef struct {
     int32_t *token_slot;  /* [T*k]  */
     hipEvent_t stage_events[MOE_NUM_STAGE_EVENTS];
     uint64_t *gemm_clock; /* [2][2]: shader ticks, reference ticks per GEMM */
+    /* moe_forward_ring only (moe_forward ignores both): polls, each a short
+     * sleep, before a wait inside the launch gives up; 0 keeps the built-in
+     * limit (seconds of polling); negative is MOE_ERR_INVALID_ARG. */
+    int32_t ring_poll_limit;
+    /* moe_forward_ring only, for testing the failure report: nonzero puts
+     * every wait's target out of reach, so that each wait gives up after
+     * ring_poll_limit polls (which must then be 1..4096, else
+     * MOE_ERR_INVALID_ARG) and the error flag is set; the output is then
+     * meaningless. */
+    int32_t ring_force_timeout;
 } moe_debug;
 
 /* Human-readable name of a status code (static storage). */
@@ -252,13 +262,26 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
  * or block_m 0 when T*top_k/E picks 256); otherwise MOE_ERR_UNSUPPORTED.
  * Arguments as in moe_forward (no weight scales); ws must hold
  * moe_ring_workspace_size() bytes.  The waits inside the launch are bounded:
- * a wait that exceeds its poll limit (seconds) gives up, so the call cannot
- * hang the device, but its output is then wrong. */
+ * a wait that exceeds its poll limit (seconds of polling by default; see
+ * moe_debug) gives up, so the call cannot hang the device, but its output is
+ * then wrong and moe_ring_error_flag's word reads 1. */
 moe_status moe_ring_workspace_size(const moe_problem *p, size_t *bytes);
 moe_status moe_forward_ring(const moe_problem *p, const void *x, const void *gate_w,
                             const float *bias, const void *W1t, const void *W3t,
                             const void *W2t, void *out, void *ws, size_t ws_bytes,
                             const moe_debug *dbg, hipStream_t stream);
+
+/* Device address, inside ws, of the int32 error flag of moe_forward_ring:
+ * every moe_forward_ring call on ws clears it to 0 before its GEMM launch,
+ * and a wait inside that launch that gives up sets it to 1 (the call's
+ * output is then wrong).  Read it on the call's stream once the call is done
+ * (for instance hipMemcpyAsync to the host, then synchronise); the next call
+ * on ws overwrites it.  No device work is enqueued here.
+ * MOE_ERR_INVALID_ARG: p invalid, ws or flag NULL; MOE_ERR_UNSUPPORTED: as
+ * moe_ring_workspace_size; MOE_ERR_WORKSPACE_TOO_SMALL: ws_bytes below
+ * moe_ring_workspace_size(). */
+moe_status moe_ring_error_flag(const moe_problem *p, void *ws, size_t ws_bytes,
+                               int32_t **flag);
 
 #ifdef __cplusplus
 }

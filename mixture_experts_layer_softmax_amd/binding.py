@@ -21,7 +21,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ["moe_status_string", "moe_last_hip_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_quantize_fp8", "moe_quantize_mx", "moe_weight_bytes",
-           "moe_pack_weight", "moe_forward", "moe_ring_workspace_size", "moe_forward_ring"]
+           "moe_pack_weight", "moe_forward", "moe_ring_workspace_size", "moe_forward_ring",
+           "moe_ring_error_flag"]
 
 
 class MoEProblem(ctypes.Structure):
@@ -40,7 +41,8 @@ DEBUG_BUFFERS = ("topk_ids", "topk_w", "counts", "offsets", "slot_token", "slot_
 class MoEDebug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in DEBUG_BUFFERS] + [
         ("stage_events", ctypes.c_void_p * NUM_STAGE_EVENTS),
-        ("gemm_clock", ctypes.c_void_p)]
+        ("gemm_clock", ctypes.c_void_p),
+        ("ring_poll_limit", ctypes.c_int32), ("ring_force_timeout", ctypes.c_int32)]
 
 
 class MoEError(RuntimeError):
@@ -80,6 +82,7 @@ def load(path: str = LIB_PATH):
                                 ctypes.POINTER(MoEDebug), P]
     lib.moe_ring_workspace_size.argtypes = [PP, ctypes.POINTER(S)]
     lib.moe_forward_ring.argtypes = [PP, P, P, P, P, P, P, P, P, S, ctypes.POINTER(MoEDebug), P]
+    lib.moe_ring_error_flag.argtypes = [PP, P, S, ctypes.POINTER(P)]
     for fn in EXPORTS:
         if fn not in ("moe_status_string", "moe_last_hip_error"):
             getattr(lib, fn).restype = ctypes.c_int
@@ -193,6 +196,8 @@ def _debug_struct(dbg):
         dbg_s.stage_events[i] = ev
     if dbg.get("gemm_clock") is not None:
         dbg_s.gemm_clock = dbg["gemm_clock"].data_ptr()
+    dbg_s.ring_poll_limit = int(dbg.get("ring_poll_limit", 0))
+    dbg_s.ring_force_timeout = int(dbg.get("ring_force_timeout", 0))
     return dbg_s
 
 
@@ -202,6 +207,25 @@ def moe_forward_ring(p, x, gate_w, bias, W1t, W3t, W2t, out, ws, dbg=None, strea
                                  _p(W3t), _p(W2t), _p(out), _p(ws), ws.numel(),
                                  None if dbg_s is None else ctypes.byref(dbg_s), _stream(stream))
     _check("moe_forward_ring", rc)
+
+
+def moe_ring_error_flag(p, ws):
+    """Device address of the ring error flag inside the workspace tensor ws."""
+    addr = ctypes.c_void_p()
+    rc = load().moe_ring_error_flag(ctypes.byref(p), _p(ws), ws.numel(), ctypes.byref(addr))
+    _check("moe_ring_error_flag", rc)
+    return addr.value
+
+
+def ring_failed(p, ws, stream=None):
+    """The error flag of the last moe_forward_ring call on ws (waits for the
+    stream): True when one of its waits gave up."""
+    off = moe_ring_error_flag(p, ws) - ws.data_ptr()
+    if stream is not None:
+        stream.synchronize()
+    else:
+        torch.cuda.current_stream(ws.device).synchronize()
+    return bool(ws[off:off + 4].view(torch.int32).item())
 
 
 # ---------------------------------------------------------------------------

@@ -304,6 +304,12 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
   if (!supported_shape(p)) return MOE_ERR_UNSUPPORTED;
   if (ring && !ring_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  if (ring && dbg) {
+    if (dbg->ring_poll_limit < 0) return MOE_ERR_INVALID_ARG;
+    if (dbg->ring_force_timeout &&
+        (dbg->ring_poll_limit < 1 || dbg->ring_poll_limit > moe::kRingForcedPollMax))
+      return MOE_ERR_INVALID_ARG;
+  }
   if (p->T == 0) return MOE_OK;
   if (!x || !gate_w || !W1t || !W3t || !W2t || !out || !ws) return MOE_ERR_INVALID_ARG;
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3, mx = p->w_dtype == MOE_MXFP4;
@@ -409,6 +415,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
     r.l2_done = ctrl + 8 + L.max_mtiles;
     r.err = ctrl + 8 + 2 * L.max_mtiles;
     r.slots = kRingSlots;
+    r.poll_limit = (dbg && dbg->ring_poll_limit > 0) ? dbg->ring_poll_limit : moe::kRingPollLimit;
+    r.unreachable = (dbg && dbg->ring_force_timeout) ? (1 << 30) : 0;
     g1.C = r.h;
     g2.A = r.h;
     g1.clock = g2.clock = nullptr;
@@ -455,6 +463,15 @@ moe_status moe_ring_workspace_size(const moe_problem* p, size_t* bytes) {
   if (!bytes || !valid_problem(p)) return MOE_ERR_INVALID_ARG;
   if (!supported_shape(p) || !ring_supported(*p)) return MOE_ERR_UNSUPPORTED;
   *bytes = make_layout(*p, true).total;
+  return MOE_OK;
+}
+
+moe_status moe_ring_error_flag(const moe_problem* p, void* ws, size_t ws_bytes, int32_t** flag) {
+  if (!flag || !ws || !valid_problem(p)) return MOE_ERR_INVALID_ARG;
+  if (!supported_shape(p) || !ring_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  const Layout L = make_layout(*p, true);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  *flag = at<int32_t>(ws, L.ring_ctrl) + 8 + 2 * L.max_mtiles;
   return MOE_OK;
 }
 

@@ -798,17 +798,16 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 // with an agent-scope release after the h stores and awaited with an
 // agent-scope acquire before the W2 task's first h load: the L2 write-back
 // and invalidation those imply are what makes h coherent across the per-XCD
-// L2s.  Waits are bounded: a wait that exceeds kRingSpin polls gives up, sets
-// RingArgs::err and lets the task run on (its output is then wrong, never a
-// hang).
-constexpr int kRingSpin = 1 << 22;
-
-__device__ inline void ring_wait(int32_t* cnt, int need, bool acquire, int32_t* err) {
+// L2s.  Waits are bounded: a wait that exceeds RingArgs::poll_limit polls
+// gives up, sets RingArgs::err and lets the task run on (its output is then
+// wrong, never a hang).  RingArgs::unreachable lifts every target beyond any
+// count, so that the caller can exercise that failure report.
+__device__ inline void ring_wait(int32_t* cnt, int need, bool acquire, int32_t* err, int limit) {
   for (int it = 0;; ++it) {
     const int v = acquire ? __hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
                           : __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v >= need) return;
-    if (it >= kRingSpin) {
+    if (it >= limit) {
       __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
@@ -890,7 +889,9 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
       auto slot_free = [&] {
         if (j >= r.slots) {
           const int cp = y + kXcd * (j - r.slots);
-          if (tid == 0) ring_wait(&r.l2_done[cp], min(GM, M - cp * GM) * NT2, false, r.err);
+          if (tid == 0)
+            ring_wait(&r.l2_done[cp], min(GM, M - cp * GM) * NT2 + r.unreachable, false, r.err,
+                      r.poll_limit);
           __syncthreads();
         }
       };
@@ -901,7 +902,9 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
         __hip_atomic_fetch_add(&r.l1_done[c], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       // every W1/W3 task of the chunk has published its h columns
-      if (tid == 0) ring_wait(&r.l1_done[c], min(GM, M - c * GM) * NT1, true, r.err);
+      if (tid == 0)
+        ring_wait(&r.l1_done[c], min(GM, M - c * GM) * NT1 + r.unreachable, true, r.err,
+                  r.poll_limit);
       __syncthreads();
       gemm_task<kBF16, 2, BM, BN, WM, WN, 128>(g2, mt, nt, ring_row, -1, kpull, [] {});
       __syncthreads();  // (the task's h loads all landed before its last stage)

@@ -70,7 +70,14 @@ struct RingArgs {
   int32_t* l2_done;  // [chunks] finished W2 tasks per chunk (empty count)
   int32_t* err;      // [1] set to 1 when a bounded wait gave up
   int slots;         // ring slots per XCD (>= 2)
+  int poll_limit;    // polls (each a short sleep) before a wait gives up
+  int unreachable;   // 0, or 1 << 30 to put every wait's target out of reach
 };
+// Default poll limit of the ring waits: seconds of polling, far beyond any
+// wait of a healthy launch.
+constexpr int kRingPollLimit = 1 << 22;
+// Largest poll limit a caller may set together with unreachable targets.
+constexpr int kRingForcedPollMax = 4096;
 
 // Gate: logits [T][E] (+ bias), top-k ids and renormalised weights [T][k].
 void launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,

@@ -145,3 +145,30 @@ def test_ring_pipeline_sizes_and_checks():
     rc = lib.moe_forward_ring(ctypes.byref(bad), None, None, None, None, None, None, None,
                               None, 0, None, None)
     assert rc == 2
+
+
+def test_ring_error_flag_and_debug_checks():
+    # moe_ring_error_flag is pure address arithmetic on the workspace; the
+    # ring's debug knobs are checked before anything is launched
+    lib = _lib()
+    p = B.problem(16384, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_BF16, B.MOE_BF16)
+    n = B.ring_workspace_size(p)
+    ws = 1 << 40  # never dereferenced
+    flag = ctypes.c_void_p()
+    assert lib.moe_ring_error_flag(ctypes.byref(p), ws, n, ctypes.byref(flag)) == 0
+    assert ws <= flag.value <= ws + n - 4 and flag.value % 4 == 0
+    again = ctypes.c_void_p()
+    assert lib.moe_ring_error_flag(ctypes.byref(p), ws, n, ctypes.byref(again)) == 0
+    assert again.value == flag.value
+    assert lib.moe_ring_error_flag(ctypes.byref(p), ws, n - 1, ctypes.byref(flag)) == 3
+    assert lib.moe_ring_error_flag(ctypes.byref(p), None, n, ctypes.byref(flag)) == 1
+    assert lib.moe_ring_error_flag(ctypes.byref(p), ws, n, None) == 1
+    fp8 = B.problem(16384, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_FP8_E4M3, B.MOE_BF16)
+    assert lib.moe_ring_error_flag(ctypes.byref(fp8), ws, n, ctypes.byref(flag)) == 2
+    fake = 1 << 40
+    for limit, force in ((-1, 0), (0, 1), (4097, 1), (-5, 1)):
+        dbg = B.MoEDebug()
+        dbg.ring_poll_limit, dbg.ring_force_timeout = limit, force
+        rc = lib.moe_forward_ring(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake,
+                                  fake, n, ctypes.byref(dbg), None)
+        assert rc == 1, (limit, force)

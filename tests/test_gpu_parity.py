@@ -597,7 +597,36 @@ def test_ring_repeated_runs_identical():
     ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
     outs = [B.forward(cfg, inp, packed, ws=ws, ring=True) for _ in range(30)]
     torch.cuda.synchronize()
+    assert not B.ring_failed(p, ws)
     for i, o in enumerate(outs):
         assert torch.equal(o, ref), i
     del inp, packed, ref, outs
     free()
+
+
+def test_ring_error_flag_reports_a_wait_that_gave_up():
+    # the failure report of the bounded waits, forced from the host: with
+    # every target out of reach each wait gives up after 4 polls, the launch
+    # still drains its queues, and the flag reads 1; the next call on the same
+    # workspace clears it and is correct again
+    cfg = RING["many_chunks"]
+    say("ring error flag")
+    inp = gpu_inputs(cfg)
+    packed = B.pack_weights(inp)
+    p = B.problem_of(cfg, block_m=256)
+    ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ref = B.forward(cfg, inp, packed, block_m=256)
+    out = B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True)
+    assert not B.ring_failed(p, ws)
+    assert torch.equal(out, ref)
+    B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True,
+              dbg={"ring_poll_limit": 4, "ring_force_timeout": 1})
+    assert B.ring_failed(p, ws)
+    out = B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True)
+    assert not B.ring_failed(p, ws)
+    assert torch.equal(out, ref)
+    # a poll limit alone only bounds the waits: a generous one changes nothing
+    out = B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True,
+                    dbg={"ring_poll_limit": 1 << 20})
+    assert not B.ring_failed(p, ws)
+    assert torch.equal(out, ref)
