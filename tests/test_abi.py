@@ -172,3 +172,16 @@ def test_ring_error_flag_and_debug_checks():
         rc = lib.moe_forward_ring(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake,
                                   fake, n, ctypes.byref(dbg), None)
         assert rc == 1, (limit, force)
+
+
+@pytest.mark.parametrize("T,d,f,E,k", [(65535, 256, 16384, 8, 1), (131071, 8192, 64, 4, 1)])
+def test_offset_limit_is_one_token_past_the_largest_supported(T, d, f, E, k):
+    # h (T*k*f bf16) or x (T*d bf16) one row short of 2^31 bytes passes the
+    # shape check (null operands then give MOE_ERR_INVALID_ARG); one more
+    # token reaches 2^31 and is MOE_ERR_UNSUPPORTED, before any launch
+    lib = _lib()
+    for TT, want in ((T, 1), (T + 1, 2)):
+        p = B.problem(TT, d, f, E, k, B.MOE_BF16, B.MOE_BF16, B.MOE_BF16)
+        rc = lib.moe_forward(ctypes.byref(p), None, None, None, None, None, None, None, None,
+                             None, None, None, 0, None, None)
+        assert rc == want, (TT, rc)

@@ -198,6 +198,34 @@ EDGE = {
 }
 
 
+# the largest operands the 32-bit byte offsets of the GEMM loads allow: h
+# (T*k rows of f bf16) and x (T rows of d bf16) each one row short of 2^31
+# bytes (one more token is MOE_ERR_UNSUPPORTED, checked in test_abi)
+MAX_OFFSET = {
+    "max_h": MoEConfig("max_h", 65535, 256, 16384, 8, 1, BF16, BF16, BF16),
+    "max_x": MoEConfig("max_x", 131071, 8192, 64, 4, 1, BF16, BF16, BF16),
+}
+
+
+@pytest.mark.parametrize("name", list(MAX_OFFSET))
+def test_largest_supported_operands(name):
+    cfg = MAX_OFFSET[name]
+    say("max offsets", name)
+    assert max(cfg.T * cfg.k * cfg.f, cfg.T * cfg.d) * 2 >= (1 << 31) - 2 * max(cfg.f, cfg.d)
+    inp = gpu_inputs(cfg)
+    n = cfg.T * cfg.k
+    dbg = {"topk_ids": torch.empty(n, dtype=torch.int32, device="cuda")}
+    out = _forward(cfg, inp, dbg=dbg)
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(cfg.T, size=12, replace=False))
+    rows[0], rows[-1] = 0, cfg.T - 1  # the last token's rows sit at the top of x and h
+    ref, ref_ids, _ = oracle_forward_rows(cfg, inp, rows)
+    assert np.array_equal(dbg["topk_ids"].view(cfg.T, cfg.k).cpu().numpy()[rows], ref_ids)
+    _outputs_ok(cfg, out[torch.as_tensor(rows, device="cuda")], ref, "sampled")
+    del inp, out
+    free()
+
+
 @pytest.mark.parametrize("name", list(EDGE))
 def test_edge_shapes(name):
     cfg = EDGE[name]
