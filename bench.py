@@ -231,7 +231,7 @@ def main():
                     help="time moe_forward_ring (both GEMMs in one launch, h in a bounded ring)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
 
