@@ -401,6 +401,11 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g2.n_tiles_n = static_cast<int>(ceil_div(p->d, moe::gemm_tile_n(2, gdt, L.bm)));
   g2.queue_idx = 1;
   g2.group_m = g1.group_m;
+  // Y far larger than the 256 MB MALL is read back from HBM by the combine
+  // anyway: non-temporal stores keep it from displacing the operands cached
+  // for the GEMMs (measured 1-3 % on W2 and the combine for Y of 0.8-7.5 GB;
+  // for a 268 MB Y the combine lost what W2 gained)
+  g2.stream_c = static_cast<double>(gemm_rows(*p)) * p->d * 4 >= 512.0 * (1 << 20);
   g2.clock = (dbg && dbg->gemm_clock) ? dbg->gemm_clock + 2 : nullptr;
   if (!ring) {
     st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));

@@ -704,9 +704,15 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
         const int r = idx / CPR, c = idx - r * CPR;
         const int lr = pass * PROWS + r;
         const int64_t col = col0 + c * (16 / OUT_ES);
-        if (lr < rows && col < N)
-          *reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(crow + lr) * N + col) * OUT_ES) =
-              *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
+        if (lr < rows && col < N) {
+          u32x4* dst =
+              reinterpret_cast<u32x4*>(g.C + (static_cast<int64_t>(crow + lr) * N + col) * OUT_ES);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c ^ (r & XM)) << 4));
+          if (PHASE == 2 && g.stream_c)
+            __builtin_nontemporal_store(v, dst);
+          else
+            *dst = v;
+        }
       }
       if (pass + 1 < PASSES) __syncthreads();
     }

@@ -55,6 +55,7 @@ struct GemmArgs {
   int n_tiles_n;          // column tiles per m-tile
   int queue_idx;
   int group_m;            // m-tiles per XCD work chunk (1..8)
+  int stream_c;           // phase 2: store Y with non-temporal hints (Y far beyond the MALL)
   uint64_t* clock;        // [2] or null: ticks of workgroup 0 (shader, 100 MHz reference)
 };
 
