@@ -214,7 +214,8 @@ moe_status moe_weight_bytes(const moe_problem *p, size_t *bytes);
  * is contiguous for the MFMA operand loads.  src and dst must not overlap.
  * elem_bytes is 4 (fp32), 2 (bf16) or 1 (FP8 codes); E matrices of K x N.
  * MXFP4 weight codes are given already K-major and need no packing; their
- * E8M0 scales [E][N][K/32] are packed as E matrices of N x K/128 dwords. */
+ * E8M0 scales [E][N][K/32] are packed as E matrices of N x K/128 dwords.
+ * MOE_ERR_UNSUPPORTED for K > 65535*64, N > 2^24 or E > 65535. */
 moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
                            const void *src, void *dst, hipStream_t stream);
 

@@ -274,7 +274,9 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes, 
                            void* dst, hipStream_t stream) {
   if (E < 1 || K < 1 || N < 1 || !src || !dst) return MOE_ERR_INVALID_ARG;
   if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return MOE_ERR_INVALID_ARG;
-  if (K > (1ll << 24) || N > (1ll << 24)) return MOE_ERR_UNSUPPORTED;
+  // one workgroup per 64 x 64 tile: K / 64 and E index the grid's y and z
+  // dimensions (at most 65535 each)
+  if (K > 65535ll * 64 || N > (1ll << 24) || E > 65535) return MOE_ERR_UNSUPPORTED;
   const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
   const uintptr_t len = static_cast<uintptr_t>(E) * K * N * elem_bytes;
   if (a < b + len && b < a + len) return MOE_ERR_INVALID_ARG;  // overlap

@@ -185,3 +185,14 @@ def test_offset_limit_is_one_token_past_the_largest_supported(T, d, f, E, k):
         rc = lib.moe_forward(ctypes.byref(p), None, None, None, None, None, None, None, None,
                              None, None, None, 0, None, None)
         assert rc == want, (TT, rc)
+
+
+def test_pack_weight_grid_limits():
+    # 64 x 64 tiles: K / 64 and E index grid dimensions of at most 65535
+    lib = _lib()
+    a, b = 1 << 40, 1 << 41  # never dereferenced: rejected before any launch
+    assert lib.moe_pack_weight(1, 65535 * 64 + 1, 64, 2, a, b, None) == 2
+    assert lib.moe_pack_weight(65536, 64, 64, 2, a, b, None) == 2
+    assert lib.moe_pack_weight(1, 64, (1 << 24) + 1, 2, a, b, None) == 2
+    assert lib.moe_pack_weight(1, 64, 64, 3, a, b, None) == 1
+    assert lib.moe_pack_weight(2, 64, 64, 2, a, a + 100, None) == 1  # overlap

@@ -148,6 +148,42 @@ def test_forward_every_tile_height(name, block_m):
     _outputs_ok(cfg, out, ref, f"bm={block_m}")
 
 
+@pytest.mark.parametrize("E,K,N,dt", [(3, 130, 70, torch.uint8), (2, 64, 4100, torch.int16),
+                                      (1, 1000, 33, torch.int32), (5, 1, 1, torch.int16),
+                                      (4, 7168, 256, torch.int16)])
+def test_pack_weight_is_the_transpose(E, K, N, dt):
+    # moe_pack_weight is pure data movement: [E][K][N] -> [E][N][K], bit for
+    # bit, for 1-, 2- and 4-byte elements and ragged 64 x 64 tiles
+    say("pack", E, K, N, dt)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(K * 31 + N)
+    info = torch.iinfo(dt)
+    src = torch.randint(info.min, info.max, (E, K, N), generator=g, device="cuda", dtype=torch.int64
+                        ).to(dt)
+    dst = torch.full((E, N, K), -1, dtype=dt, device="cuda")
+    B.moe_pack_weight(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), src.cpu().transpose(1, 2).contiguous())
+
+
+def test_route_logits_in_the_workspace():
+    # moe_route with logits == NULL keeps them in the workspace: the same ids
+    # and weights, bit for bit, as with a caller's logits buffer
+    cfg = REDUCED["skewed_bf16_r"]
+    say("route ws", cfg.name)
+    inp = gpu_inputs(cfg)
+    _, ids, w = gpu_route(cfg, inp)
+    p = B.problem_of(cfg)
+    ids2 = torch.full_like(ids, -1)
+    w2 = torch.full_like(w, -1.0)
+    ws = B.alloc_workspace(p)
+    B.moe_route(p, inp["x"], inp["gate_w"], inp.get("bias"), None, ids2, w2, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids2, ids) and torch.equal(w2, w)
+    with pytest.raises(B.MoEError, match="WORKSPACE_TOO_SMALL"):
+        B.moe_route(p, inp["x"], inp["gate_w"], inp.get("bias"), None, ids2, w2, ws=ws[:16])
+
+
 def test_quantize_fp8_bit_exact():
     say("quant fp8")
     g = torch.Generator(device="cuda")
