@@ -231,6 +231,10 @@ EDGE = {
     # (1024 lanes of 8 columns) and the gate a partial last chunk
     "wide_d": MoEConfig("wide_d", 9, 8256, 64, 4, 2, BF16, BF16, BF16),
     "wide_fp8": MoEConfig("wide_fp8", 7, 8320, 128, 4, 2, BF16, FP8, BF16),
+    # the most experts a problem may have (1024), and a top-k of 64 (eight
+    # groups of slot loads per combine lane)
+    "E_max": MoEConfig("E_max", 300, 128, 128, 1024, 8, BF16, BF16, BF16),
+    "k64": MoEConfig("k64", 50, 128, 64, 128, 64, BF16, BF16, BF16),
 }
 
 
