@@ -336,6 +336,7 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
     roof["kernel"] = dom
+    roof["avg_launch_us"] = dom_s * 1e6  # HIP events around each launch of the timed loop
     roof["traffic"] = _traffic(cfg.name, dom)
     layer_flops = cfg.expert_flops
     layer = {
