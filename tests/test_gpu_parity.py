@@ -698,3 +698,29 @@ def test_ring_error_flag_reports_a_wait_that_gave_up():
                     dbg={"ring_poll_limit": 1 << 20})
     assert not B.ring_failed(p, ws)
     assert torch.equal(out, ref)
+
+
+def test_ring_concurrent_on_two_streams():
+    # every wait of the ring targets tasks pulled earlier from the same queue,
+    # so it needs no co-residency: two ring launches (own workspaces) on two
+    # streams, each sharing the GPU with the other, still match moe_forward
+    cfgs = [RING["many_chunks"], RING["prefill_bf16_r"]]
+    say("ring two streams", [c.name for c in cfgs])
+    inps = [gpu_inputs(c) for c in cfgs]
+    packs = [B.pack_weights(i) for i in inps]
+    ref = [B.forward(c, i, p, block_m=256) for c, i, p in zip(cfgs, inps, packs)]
+    probs = [B.problem_of(c, block_m=256) for c in cfgs]
+    wss = [torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda") for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    for rep in range(3):
+        for j in (0, 1):
+            with torch.cuda.stream(streams[j]):
+                outs[j].append(B.forward(cfgs[j], inps[j], packs[j], ws=wss[j], block_m=256,
+                                         stream=streams[j], ring=True))
+    torch.cuda.synchronize()
+    for j in (0, 1):
+        assert not B.ring_failed(probs[j], wss[j])
+        for o in outs[j]:
+            assert torch.equal(o, ref[j]), cfgs[j].name
