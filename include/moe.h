@@ -253,7 +253,8 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
  * the ring of in-flight blocks (sized by blocks in flight, not by routed
  * tokens) and the L1/L2 full and empty counters of the MegaMoE-vs-MoE-systems
  * page, sections 2.3 and 2.7.  Each XCD's task queue runs, step by step, the
- * W1/W3 tasks of one work chunk and then the W2 tasks of the previous chunk;
+ * W1/W3 tasks of one work chunk and then the W2 tasks of the chunk two steps
+ * back;
  * a W2 task waits until every W1/W3 task of its chunk has published its h
  * columns, and a W1/W3 task waits for its ring slot to be empty before
  * storing h.  h therefore needs 24 chunk-sized slots instead of T*k rows

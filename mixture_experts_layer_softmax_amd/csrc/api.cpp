@@ -104,10 +104,11 @@ struct Layout {
 };
 
 // Ring slots per XCD of the single-launch pipeline: chunk j's h waits in slot
-// j % kRingSlots until its W2 tasks are done (two steps of the queue later at
-// the earliest), so two slots already never block; a third absorbs W2 tasks
-// that finish late.
+// j % kRingSlots until its W2 tasks (kRingLag steps of the queue later) are
+// done; the chunk that reuses the slot must come after them in the queue, so
+// the slots must outnumber the lag.
 constexpr int kRingSlots = 3;
+static_assert(kRingSlots > moe::kRingLag, "slot reuse waits on earlier tasks only");
 int64_t ring_ctrl_words(int64_t max_mtiles) { return 8 + 2 * max_mtiles + 1; }
 
 Layout make_layout(const moe_problem& p, bool ring = false) {
@@ -296,7 +297,7 @@ bool ring_supported(const moe_problem& p) {
   const int64_t gm = group_m(p, 256);
   const int64_t tiles = (gemm_rows(p) + static_cast<int64_t>(p.E + p.n_shared) * 255) / 256 + 1;
   const int64_t per_step = gm * (ceil_div(2 * p.f, 256) + ceil_div(p.d, 256));
-  return (ceil_div(ceil_div(tiles, gm), 8) + 1) * per_step < (1ll << 24);
+  return (ceil_div(ceil_div(tiles, gm), 8) + moe::kRingLag) * per_step < (1ll << 24);
 }
 
 moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,

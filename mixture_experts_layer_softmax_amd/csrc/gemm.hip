@@ -836,7 +836,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
                                    (kXcd - 1));
   const int per_step = GM * (NT1 + NT2);
   auto owned = [&](int y) { return nchunks > y ? (nchunks - y + kXcd - 1) / kXcd : 0; };
-  auto limit = [&](int y) { return (owned(y) + 1) * per_step; };
+  auto limit = [&](int y) { return (owned(y) + kRingLag) * per_step; };
   // pull v of queue y -> (phase, chunk index j of that queue, m-tile, n-tile);
   // false for a hole (no such chunk, or past the last m-tile)
   auto decode = [&](int v, int y, int& phase, int& j, int& mt, int& nt) {
@@ -849,7 +849,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
       nt = p / GM;
     } else {
       phase = 2;
-      j = st - 1;
+      j = st - kRingLag;
       ml = (p - GM * NT1) % GM;
       nt = (p - GM * NT1) / GM;
     }
