@@ -161,8 +161,10 @@ def _stage_work(cfg, counts):
     return {"gemm_w13_swiglu": w13, "gemm_w2": w2, "hit_experts": hit}
 
 
-def _cpu_baseline(cfg, inp, out_gpu, target_s):
-    """The CPU oracle as it stands, timed on a bounded token sample."""
+def _cpu_baseline(cfg, inp, out_gpu, out32_gpu, target_s):
+    """The CPU oracle as it stands, timed on a bounded token sample; the same
+    sample checks the run's outputs (the workload's own output type, and the
+    fp32-output run when there is one)."""
     import numpy as np
     import torch
 
@@ -201,14 +203,18 @@ def _cpu_baseline(cfg, inp, out_gpu, target_s):
     n = int(min(cfg.T, max(n0, n0 * target_s / max(t_probe, 1e-3))))
     rows = np.sort(rng.choice(cfg.T, size=n, replace=False))
     ref, secs = run(rows)
-    got = out_gpu[torch.as_tensor(rows, device=out_gpu.device)].double().cpu().numpy()
+    sel = torch.as_tensor(rows, device=out_gpu.device)
+    got = out_gpu[sel].double().cpu().numpy()
     rms = math.sqrt(float(np.mean(ref ** 2))) or 1.0
     diff = np.abs(got - ref)
-    err = {"max_abs_err_over_rms": float(diff.max()) / rms}
+    err = {"tokens": int(n), "max_abs_err_over_rms": float(diff.max()) / rms}
     if out_gpu.dtype == torch.bfloat16:
         # rounding the exact result to bf16 alone costs up to half a bf16 ulp
         half_ulp = 0.5 * np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
         err["max_excess_over_half_bf16_ulp_over_rms"] = float(np.maximum(diff - half_ulp, 0).max()) / rms
+    if out32_gpu is not None:
+        got32 = out32_gpu[sel].double().cpu().numpy()
+        err["fp32_out_max_abs_err_over_rms"] = float(np.abs(got32 - ref).max()) / rms
     cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
     return {"value": n / secs, "unit": "tokens/s", "cores": cores, "cpu": _cpu_model(),
             "kind": "oracle",
@@ -216,37 +222,31 @@ def _cpu_baseline(cfg, inp, out_gpu, target_s):
                       f"token, {secs:.1f} s", "seconds": secs}, err
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    # 50 warm-up steps: the shader clock ramps up over the first ~50 ms of
-    # load (prefill_bf16 GEMMs at ~2.08 GHz after 5 steps, ~2.23 GHz after 50)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="prefill_bf16")
-    ap.add_argument("--cpu-seconds", type=float, default=16.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--block-m", type=int, default=0, help="expert tile height (0 = auto)")
-    ap.add_argument("--ring", action="store_true",
-                    help="time moe_forward_ring (both GEMMs in one launch, h in a bounded ring)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
-              f"(--gpus {args.gpus} requested)", file=sys.stderr)
-        sys.exit(2)
+def _free(torch):
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
+
+def _say(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
+    """Time `steps` whole-layer forwards of cfg after `warmup` untimed ones;
+    returns the per-workload record (tokens/s, roofline of the dominant GEMM
+    launch, stage breakdown, CPU-oracle baseline and parity sample)."""
     import numpy as np
     import torch
 
     from mixture_experts_layer_softmax_amd import binding as B
-    from mixture_experts_layer_softmax_amd.configs import CONFIGS
     from mixture_experts_layer_softmax_amd.inputs import make_inputs
 
-    cfg = CONFIGS[args.workload]
-    torch.cuda.set_device(0)
-    B.load()
+    _say(f"{cfg.name}: drawing inputs")
     inp = make_inputs(cfg, device="cuda")
+    t_pack = time.perf_counter()
     packed = B.pack_weights(inp)
+    torch.cuda.synchronize()
+    pack_s = time.perf_counter() - t_pack
     p = B.problem_of(cfg, block_m=args.block_m)
     if args.ring:
         ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
@@ -255,20 +255,19 @@ def main():
     out = B.out_tensor(cfg)
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    hip = _hip()
     nev = B.NUM_STAGE_EVENTS
-    evs = [_events(hip, nev) for _ in range(args.steps)]
+    evs = [_events(hip, nev) for _ in range(steps)]
 
-    def step(dbg=None):
+    def step(dbg=None, o=out, pp=p):
         if args.ring:
-            B.moe_forward_ring(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"],
-                               packed["W3t"], packed["W2t"], out, ws, dbg=dbg, stream=stream)
+            B.moe_forward_ring(pp, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"],
+                               packed["W3t"], packed["W2t"], o, ws, dbg=dbg, stream=stream)
             return
-        B.moe_forward(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"],
+        B.moe_forward(pp, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"],
                       packed["W3t"], packed["W2t"], packed.get("W1s"), packed.get("W3s"),
-                      packed.get("W2s"), out, ws, dbg=dbg, stream=stream)
+                      packed.get("W2s"), o, ws, dbg=dbg, stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step({"counts": counts})
     torch.cuda.synchronize()
 
@@ -276,10 +275,11 @@ def main():
     # boundaries 3, 4, 5), on the stream moe_forward launches on -- every
     # event record costs the GPU a few microseconds, so the full per-stage
     # breakdown comes from a separate, untimed pass below.
+    _say(f"{cfg.name}: {warmup} warm-up steps done, timing {steps}")
     t0 = time.perf_counter()
     clock = torch.zeros(4, dtype=torch.int64, device="cuda")
     gemm_only = (3, 4, 5)
-    for i in range(args.steps):
+    for i in range(steps):
         sel = [evs[i][j] if j in gemm_only else None for j in range(nev)]
         step({"stage_events": sel, "gemm_clock": clock})
     torch.cuda.synchronize()
@@ -295,13 +295,13 @@ def main():
         sustained = None
 
     # per-stage breakdown (untimed): every stage boundary recorded
-    nbreak = min(args.steps, 10)
+    nbreak = min(steps, 10)
     for i in range(nbreak):
         step({"stage_events": evs[i]})
     torch.cuda.synchronize()
     stage_ms = {}
-    for s, name in enumerate(STAGES, start=1):
-        stage_ms[name] = float(np.mean([_elapsed(hip, e[s - 1], e[s]) for e in evs[:nbreak]]))
+    for s_, name in enumerate(STAGES, start=1):
+        stage_ms[name] = float(np.mean([_elapsed(hip, e[s_ - 1], e[s_]) for e in evs[:nbreak]]))
     gpu_ms = _elapsed(hip, evs[0][0], evs[nbreak - 1][-1]) / nbreak
     per_step = np.array([_elapsed(hip, e[0], e[-1]) for e in evs[:nbreak]])
     step_stats = {"median": float(np.median(per_step)), "min": float(per_step.min()),
@@ -310,8 +310,8 @@ def main():
         for v in e:
             hip.hipEventDestroy(v)
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = cfg.T * args.steps / elapsed
+    ms_per_step = elapsed * 1e3 / steps
+    value = cfg.T * steps / elapsed
     work = _stage_work(cfg, counts.cpu().numpy())
     if args.ring:
         # one launch runs both GEMMs: its time is stage 4, stage 5 is empty
@@ -325,7 +325,6 @@ def main():
         dom = max(("gemm_w13_swiglu", "gemm_w2"), key=lambda k: timed_gemm_ms[k])
     dom_s = timed_gemm_ms[dom] * 1e-3
     decode = cfg.T * cfg.k / cfg.E < 16  # expected rows per routed expert
-    copy_gbps = _copy_gbps(torch)
     if decode:
         achieved = work[dom]["bytes"] / dom_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -348,39 +347,112 @@ def main():
         "gpu_event_ms_per_step": gpu_ms,
         "gpu_event_ms_per_step_stats": step_stats,
     }
-    device = _device_info()
-    device["sustained_clock_mhz"] = sustained
-    device["measured_copy_GBps"] = copy_gbps
 
-    cpu = None
-    parity = None
+    # the same layer with an fp32 output (the primary parity bar of bf16
+    # layers), for the parity sample below
+    out32 = None
+    if not args.no_cpu_baseline and cfg.out_dtype != 0 and not args.ring:
+        p32 = B.problem_of(cfg, block_m=args.block_m, out_dtype=0)
+        out32 = B.out_tensor(cfg, out_dtype=0)
+        step(None, out32, p32)
+        torch.cuda.synchronize()
+
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu, parity = _cpu_baseline(cfg, inp, out, args.cpu_seconds)
+        _say(f"{cfg.name}: CPU oracle baseline (~{cpu_seconds:.0f} s)")
+        cpu, parity = _cpu_baseline(cfg, inp, out, out32, cpu_seconds)
 
     dtype = {0: "f32", 1: "bf16", 2: "fp8e4m3", 3: "mxfp4xmxfp8"}[cfg.w_dtype]
+    rec = {
+        "value": value, "unit": "tokens/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "dtype": dtype,
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
+                   "top_k": cfg.k, "n_shared": cfg.n_shared, "parallelism": "single GPU",
+                   "gemms": "one launch, h ring" if args.ring else "two launches"},
+        "roofline": roof, "cpu_baseline": cpu, "stages_ms": stage_ms, "layer": layer,
+        "sustained_clock_mhz": sustained, "parity_sample": parity,
+        "weight_pack_ms": pack_s * 1e3,
+    }
+    del inp, packed, ws, out, out32
+    _free(torch)
+    return rec
+
+
+# the other stated workloads, measured after the headline one in a default run
+OTHER_CONFIGS = ["tiny_fp32", "decode_bf16", "skewed_bf16", "prefill_fp8"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    # 50 warm-up steps: the shader clock ramps up over the first ~50 ms of
+    # load (prefill_bf16 GEMMs at ~2.08 GHz after 5 steps, ~2.23 GHz after 50)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
+    ap.add_argument("--other-cpu-seconds", type=float, default=8.0,
+                    help="CPU-oracle seconds for each of the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="measure only --workload (by default the other stated workloads "
+                         "follow the headline one, each in a block of its own)")
+    ap.add_argument("--block-m", type=int, default=0, help="expert tile height (0 = auto)")
+    ap.add_argument("--ring", action="store_true",
+                    help="time moe_forward_ring (both GEMMs in one launch, h in a bounded ring)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_layer_softmax_amd import binding as B
+    from mixture_experts_layer_softmax_amd.configs import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    B.load()
+    hip = _hip()
+    copy_gbps = _copy_gbps(torch)
+    head = measure(cfg, args, args.steps, args.warmup, args.cpu_seconds, hip, copy_gbps)
+
+    others = {}
+    if not args.no_other_configs and not args.ring and args.workload == "prefill_bf16":
+        for name in OTHER_CONFIGS:
+            rec = measure(CONFIGS[name], args, args.steps, args.warmup, args.other_cpu_seconds,
+                          hip, copy_gbps)
+            rec.pop("layer", None)
+            others[name] = rec
+
+    device = _device_info()
+    device["sustained_clock_mhz"] = head.pop("sustained_clock_mhz")
+    device["measured_copy_GBps"] = copy_gbps
     line = {
         "metric": "MoE-layer tokens/s on 1 MI355X; MFMA % peak (prefill), HBM GB/s (decode)",
-        "value": value,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": head["dtype"],
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
-                   "top_k": cfg.k, "n_shared": cfg.n_shared, "parallelism": "single GPU",
-                   "gemms": "one launch, h ring" if args.ring else "two launches"},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "stages_ms": stage_ms,
-        "layer": layer,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "stages_ms": head["stages_ms"],
+        "layer": head["layer"],
         "device": device,
-        "parity_sample": parity,
+        "parity_sample": head["parity_sample"],
+        "weight_pack_ms": head["weight_pack_ms"],
     }
+    if others:
+        line["configs"] = others
     print(json.dumps(line), flush=True)
 
 

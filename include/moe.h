@@ -62,7 +62,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = 1,          /* null pointer, bad size, bad dtype   */
     MOE_ERR_UNSUPPORTED = 2,          /* valid but not implemented shape     */
     MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes < moe_workspace_size()     */
-    MOE_ERR_HIP = 4                   /* a HIP launch/runtime call failed    */
+    MOE_ERR_HIP = 4,                  /* a HIP launch/runtime call failed    */
+    MOE_ERR_DEVICE = 5                /* a bounded wait inside a launch gave
+                                         up (reported by moe_ring_status)   */
 } moe_status;
 
 typedef enum {
@@ -71,6 +73,19 @@ typedef enum {
     MOE_FP8_E4M3 = 2,
     MOE_MXFP4 = 3   /* OCP MX FP4: E2M1 codes, E8M0 scale per 32 along K */
 } moe_dtype;
+
+/* Storage order of each expert's weight matrix (K = contraction length, N =
+ * output columns: W1 and W3 are K = d by N = f, W2 is K = f by N = d).
+ *   MOE_W_KN: row-major [K][N] per expert, the layout the workloads state
+ *             (W1, W3 [E+S][d][f]; W2 [E+S][f][d]); FP8 codes the same, with
+ *             [E+S][K/128][N/128] fp32 block scales.  Not defined for MXFP4.
+ *   MOE_W_NK: [N][K] per expert (contraction axis contiguous), the layout
+ *             moe_pack_weight writes; MXFP4 codes [N][K/2] with their E8M0
+ *             scales packed by moe_pack_weight. */
+typedef enum {
+    MOE_W_KN = 0,
+    MOE_W_NK = 1
+} moe_weight_layout;
 
 /* Problem description.  Sizes: T tokens, hidden d, expert intermediate f,
  * E experts, top_k experts per token (1 <= top_k <= E <= 1024).
@@ -95,6 +110,8 @@ typedef enum {
  *            output is added with weight 1 after the gate-weighted routed
  *            sum; its weights follow the E routed experts' in W1/W3/W2 (and
  *            their FP8 scales), which then hold E + n_shared experts.
+ * w_layout: a moe_weight_layout, the storage order of W1, W3 and W2 (a
+ *            zero-initialised problem means the stated [K][N] layout).
  * d and f must be multiples of 32 (fp32 weights), 64 (bf16) or 128 (FP8, MXFP4), and
  * x, h and one expert's weight matrix must each span less than 2^31 bytes
  * (MOE_ERR_UNSUPPORTED otherwise). */
@@ -106,6 +123,7 @@ typedef struct {
     int32_t out_dtype;
     int32_t block_m;
     int32_t n_shared;
+    int32_t w_layout;
 } moe_problem;
 
 /* Optional device outputs filled from inside moe_forward, so that the routing
@@ -219,15 +237,23 @@ moe_status moe_weight_bytes(const moe_problem *p, size_t *bytes);
 moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
                            const void *src, void *dst, hipStream_t stream);
 
-/* Whole layer forward.
+/* Whole layer forward: the operator the FlashMoE Kernel page describes in
+ * its opening paragraph (gate -> dispatch -> expert FFN -> combine), for one
+ * GPU and every token.  Routing is the renormalised top-k softmax gate of the
+ * stated workloads; dispatch is dropless, each expert-ordered slot keeping
+ * the (token, k-slot) it came from (MegaMoE-vs-MoE-systems page, sections 2.4
+ * and 2.6); the expert FFN is SwiGLU; the combine is the gate-weighted sum
+ * over each token's k slots (FlashMoE Kernel page, Architecture section).
  *   x       [T][d]       act_dtype
  *   gate_w  [d][E]       act_dtype
  *   bias    [E]          fp32 or NULL
- *   W1t,W3t [E+S][f][d]  w_dtype, packed by moe_pack_weight (gate, up)
- *   W2t     [E+S][d][f]  w_dtype, packed by moe_pack_weight (down)
- *           (MXFP4: the same [N][K] shapes with two E2M1 codes per byte,
- *           element 2i in the low nibble of byte i -- K-major as given)
- *   W1s,W3s FP8: [E+S][d/128][f/128] fp32 block scales;
+ *   W1, W3  (gate, up) and W2 (down), E+S expert matrices each, in the order
+ *           p->w_layout names:
+ *             MOE_W_KN: W1, W3 [E+S][d][f], W2 [E+S][f][d] as stated;
+ *             MOE_W_NK: W1, W3 [E+S][f][d], W2 [E+S][d][f], as written by
+ *             moe_pack_weight (MXFP4: the same [N][K] shapes with two E2M1
+ *             codes per byte, element 2i in the low nibble of byte i)
+ *   W1s,W3s FP8: [E+S][d/128][f/128] fp32 block scales (either layout);
  *           MXFP4: E8M0 bytes, one per 32 elements along K, given as
  *           [E+S][f][d/32] and packed by moe_pack_weight (elem_bytes 4, the
  *           rows' dwords of 4 blocks transposed) to [E+S][d/128][f] dwords;
@@ -241,10 +267,16 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
  * Kernels enqueued: route (logits, top-k), FP8 / MX FP8 quantisation of x
  * (FP8 and MXFP4 layers),
  * histogram, scan + tile map, scatter, grouped W1/W3 GEMM + SwiGLU, grouped
- * W2 GEMM, combine. */
+ * W2 GEMM, combine.
+ * Errors: MOE_ERR_INVALID_ARG (bad problem, NULL operand), MOE_ERR_UNSUPPORTED
+ * (shape or layout the kernels do not cover, e.g. MOE_W_KN with MXFP4
+ * weights), MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP (a launch failed; the
+ * HIP code is kept for moe_last_hip_error).  All are returned before
+ * anything is enqueued except MOE_ERR_HIP, after which the stream may hold
+ * the kernels launched before the failing one. */
 moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
-                       const float *bias, const void *W1t, const void *W3t,
-                       const void *W2t, const void *W1s, const void *W3s,
+                       const float *bias, const void *W1, const void *W3,
+                       const void *W2, const void *W1s, const void *W3s,
                        const void *W2s, void *out, void *ws, size_t ws_bytes,
                        const moe_debug *dbg, hipStream_t stream);
 
@@ -260,8 +292,9 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
  * storing h.  h therefore needs 24 chunk-sized slots instead of T*k rows
  * (moe_ring_workspace_size); Y and everything else are as in moe_forward,
  * and the outputs are bit-identical to moe_forward's.
- * Supported: act_dtype = w_dtype = MOE_BF16 with 256-row tiles (block_m 256,
- * or block_m 0 when T*top_k/E picks 256); otherwise MOE_ERR_UNSUPPORTED.
+ * Supported: act_dtype = w_dtype = MOE_BF16, w_layout = MOE_W_NK, with
+ * 256-row tiles (block_m 256, or block_m 0 when T*top_k/E picks 256);
+ * otherwise MOE_ERR_UNSUPPORTED.
  * Arguments as in moe_forward (no weight scales); ws must hold
  * moe_ring_workspace_size() bytes.  The waits inside the launch are bounded:
  * a wait that exceeds its poll limit (seconds of polling by default; see
@@ -284,6 +317,15 @@ moe_status moe_forward_ring(const moe_problem *p, const void *x, const void *gat
  * moe_ring_workspace_size(). */
 moe_status moe_ring_error_flag(const moe_problem *p, void *ws, size_t ws_bytes,
                                int32_t **flag);
+
+/* Outcome of the last moe_forward_ring call on ws: waits for `stream` (a host
+ * synchronisation, unlike every other entry point), reads the error flag and
+ * returns MOE_OK, or MOE_ERR_DEVICE when a bounded wait inside that launch
+ * gave up (its output is then wrong).  Argument errors as
+ * moe_ring_error_flag; MOE_ERR_HIP if the synchronisation or the read
+ * fails. */
+moe_status moe_ring_status(const moe_problem *p, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -16,13 +16,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
+MOE_W_KN, MOE_W_NK = 0, 1  # weight storage order: as stated [K][N], or packed [N][K]
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
-          3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+          3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP", 5: "MOE_ERR_DEVICE"}
 
 EXPORTS = ["moe_status_string", "moe_last_hip_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_quantize_fp8", "moe_quantize_mx", "moe_weight_bytes",
            "moe_pack_weight", "moe_forward", "moe_ring_workspace_size", "moe_forward_ring",
-           "moe_ring_error_flag"]
+           "moe_ring_error_flag", "moe_ring_status"]
 
 
 class MoEProblem(ctypes.Structure):
@@ -30,7 +31,7 @@ class MoEProblem(ctypes.Structure):
                 ("E", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("block_m", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32)]
+                ("n_shared", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
 
 NUM_STAGE_EVENTS = 7
@@ -83,6 +84,7 @@ def load(path: str = LIB_PATH):
     lib.moe_ring_workspace_size.argtypes = [PP, ctypes.POINTER(S)]
     lib.moe_forward_ring.argtypes = [PP, P, P, P, P, P, P, P, P, S, ctypes.POINTER(MoEDebug), P]
     lib.moe_ring_error_flag.argtypes = [PP, P, S, ctypes.POINTER(P)]
+    lib.moe_ring_status.argtypes = [PP, P, S, P]
     for fn in EXPORTS:
         if fn not in ("moe_status_string", "moe_last_hip_error"):
             getattr(lib, fn).restype = ctypes.c_int
@@ -111,14 +113,17 @@ def _check(fn, rc):
 
 
 def problem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m=0,
-            n_shared=0) -> MoEProblem:
-    return MoEProblem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m, n_shared)
+            n_shared=0, w_layout=MOE_W_NK) -> MoEProblem:
+    """moe_problem; w_layout defaults to the packed [N][K] weights that
+    pack_weights() produces."""
+    return MoEProblem(T, d, f, E, top_k, act_dtype, w_dtype, out_dtype, block_m, n_shared,
+                      w_layout)
 
 
-def problem_of(cfg, T=None, block_m=0, out_dtype=None) -> MoEProblem:
+def problem_of(cfg, T=None, block_m=0, out_dtype=None, w_layout=MOE_W_NK) -> MoEProblem:
     return problem(cfg.T if T is None else T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.act_dtype,
                    cfg.w_dtype, cfg.out_dtype if out_dtype is None else out_dtype, block_m,
-                   cfg.n_shared)
+                   cfg.n_shared, w_layout)
 
 
 def workspace_size(p: MoEProblem) -> int:
@@ -179,11 +184,11 @@ def moe_pack_weight(src, dst, stream=None):
     _check("moe_pack_weight", rc)
 
 
-def moe_forward(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, dbg=None,
+def moe_forward(p, x, gate_w, bias, W1, W3, W2, W1s, W3s, W2s, out, ws, dbg=None,
                 stream=None):
     dbg_s = _debug_struct(dbg)
-    rc = load().moe_forward(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(W1t), _p(W3t),
-                            _p(W2t), _p(W1s), _p(W3s), _p(W2s), _p(out), _p(ws), ws.numel(),
+    rc = load().moe_forward(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(W1), _p(W3),
+                            _p(W2), _p(W1s), _p(W3s), _p(W2s), _p(out), _p(ws), ws.numel(),
                             None if dbg_s is None else ctypes.byref(dbg_s), _stream(stream))
     _check("moe_forward", rc)
 
@@ -217,15 +222,19 @@ def moe_ring_error_flag(p, ws):
     return addr.value
 
 
+def moe_ring_status(p, ws, stream=None) -> int:
+    """Status of the last moe_forward_ring call on ws (waits for the stream):
+    0 (MOE_OK) or 5 (MOE_ERR_DEVICE, a wait inside the launch gave up)."""
+    rc = load().moe_ring_status(ctypes.byref(p), _p(ws), ws.numel(), _stream(stream))
+    if rc not in (0, 5):
+        _check("moe_ring_status", rc)
+    return rc
+
+
 def ring_failed(p, ws, stream=None):
-    """The error flag of the last moe_forward_ring call on ws (waits for the
-    stream): True when one of its waits gave up."""
-    off = moe_ring_error_flag(p, ws) - ws.data_ptr()
-    if stream is not None:
-        stream.synchronize()
-    else:
-        torch.cuda.current_stream(ws.device).synchronize()
-    return bool(ws[off:off + 4].view(torch.int32).item())
+    """True when a wait of the last moe_forward_ring call on ws gave up
+    (moe_ring_status returned MOE_ERR_DEVICE)."""
+    return moe_ring_status(p, ws, stream) == 5
 
 
 # ---------------------------------------------------------------------------
@@ -264,22 +273,30 @@ def out_tensor(cfg, T=None, device="cuda", out_dtype=None):
                        dtype=torch.float32 if od == MOE_F32 else torch.bfloat16, device=device)
 
 
-def forward(cfg, inp: dict, packed: dict, out=None, ws=None, dbg=None, out_dtype=None,
+def forward(cfg, inp: dict, packed: dict | None, out=None, ws=None, dbg=None, out_dtype=None,
             block_m=0, stream=None, ring=False):
     """Whole-layer forward of cfg on resident inputs; returns the output tensor.
+    packed: weights from pack_weights() (layout MOE_W_NK), or None to pass
+    inp's weights in the stated [K][N] layout (MOE_W_KN).
     ring=True runs moe_forward_ring (both GEMMs in one launch, h in a ring)."""
     T = inp["x"].shape[0]
-    p = problem_of(cfg, T=T, block_m=block_m, out_dtype=out_dtype)
+    layout = MOE_W_KN if packed is None else MOE_W_NK
+    p = problem_of(cfg, T=T, block_m=block_m, out_dtype=out_dtype, w_layout=layout)
+    if packed is None:
+        W1, W3, W2 = inp["W1"], inp["W3"], inp["W2"]
+        W1s, W3s, W2s = inp.get("W1s"), inp.get("W3s"), inp.get("W2s")
+    else:
+        W1, W3, W2 = packed["W1t"], packed["W3t"], packed["W2t"]
+        W1s, W3s, W2s = packed.get("W1s"), packed.get("W3s"), packed.get("W2s")
     if out is None:
         out = out_tensor(cfg, T=T, device=inp["x"].device, out_dtype=out_dtype)
     if ws is None:
         size = ring_workspace_size(p) if ring else workspace_size(p)
         ws = torch.empty(size, dtype=torch.uint8, device=inp["x"].device)
     if ring:
-        moe_forward_ring(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"],
-                         packed["W3t"], packed["W2t"], out, ws, dbg=dbg, stream=stream)
+        moe_forward_ring(p, inp["x"], inp["gate_w"], inp.get("bias"), W1, W3, W2, out, ws,
+                         dbg=dbg, stream=stream)
     else:
-        moe_forward(p, inp["x"], inp["gate_w"], inp.get("bias"), packed["W1t"], packed["W3t"],
-                    packed["W2t"], packed.get("W1s"), packed.get("W3s"), packed.get("W2s"), out,
-                    ws, dbg=dbg, stream=stream)
+        moe_forward(p, inp["x"], inp["gate_w"], inp.get("bias"), W1, W3, W2, W1s, W3s, W2s,
+                    out, ws, dbg=dbg, stream=stream)
     return out

@@ -73,8 +73,12 @@ bool valid_problem(const moe_problem* p) {
   if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
       p->block_m != 128 && p->block_m != 256)
     return false;
+  if (p->w_layout != MOE_W_KN && p->w_layout != MOE_W_NK) return false;
   return true;
 }
+
+// Weight layouts the GEMM kernels read: [N][K] (packed) for every dtype.
+bool supported_layout(const moe_problem& p) { return p.w_layout == MOE_W_NK; }
 
 // Expert rows of the grouped GEMMs: the T*k routed slots, then T per shared
 // expert.
@@ -197,6 +201,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or type combination";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_DEVICE: return "a bounded wait inside a launch gave up";
   }
   return "unknown status";
 }
@@ -230,9 +235,9 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* gate_w, co
     lg = at<float>(ws, L.logits);
   }
   (void)hipGetLastError();
-  moe::launch_gate(x, gate_w, bias, lg, topk_ids, topk_w, static_cast<int>(p->T),
-                   static_cast<int>(p->d), p->E, p->top_k, p->act_dtype == MOE_BF16, stream);
-  return hip_status();
+  return from_code(moe::launch_gate(x, gate_w, bias, lg, topk_ids, topk_w,
+                                    static_cast<int>(p->T), static_cast<int>(p->d), p->E,
+                                    p->top_k, p->act_dtype == MOE_BF16, stream));
 }
 
 moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* counts,
@@ -294,6 +299,7 @@ namespace {
 // codes below 2^24: queue << 24 | pull index).
 bool ring_supported(const moe_problem& p) {
   if (p.act_dtype != MOE_BF16 || p.w_dtype != MOE_BF16 || pick_bm(p) != 256) return false;
+  if (p.w_layout != MOE_W_NK) return false;
   const int64_t gm = group_m(p, 256);
   const int64_t tiles = (gemm_rows(p) + static_cast<int64_t>(p.E + p.n_shared) * 255) / 256 + 1;
   const int64_t per_step = gm * (ceil_div(2 * p.f, 256) + ceil_div(p.d, 256));
@@ -305,7 +311,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
                         const void* W1s, const void* W3s, const void* W2s, void* out, void* ws,
                         size_t ws_bytes, const moe_debug* dbg, hipStream_t stream, bool ring) {
   if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
-  if (!supported_shape(p)) return MOE_ERR_UNSUPPORTED;
+  if (!supported_shape(p) || !supported_layout(*p)) return MOE_ERR_UNSUPPORTED;
   if (ring && !ring_supported(*p)) return MOE_ERR_UNSUPPORTED;
   if (ring && dbg) {
     if (dbg->ring_poll_limit < 0) return MOE_ERR_INVALID_ARG;
@@ -343,8 +349,9 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   (void)hipGetLastError();
   mark(0);
   // 1. gate
-  moe::launch_gate(x, gate_w, bias, logits, ids, w, T, d, E, k, p->act_dtype == MOE_BF16,
-                   stream);
+  moe_status st = from_code(moe::launch_gate(x, gate_w, bias, logits, ids, w, T, d, E, k,
+                                             p->act_dtype == MOE_BF16, stream));
+  if (st != MOE_OK) return st;
   mark(1);
   // 2. FP8 (or MX FP8) activations
   if (fp8)
@@ -358,7 +365,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   moe::launch_permute(ids, T, k, E, p->n_shared, L.bm, at<int32_t>(ws, L.table), counts,
                       offsets, slot_token, slot_k, token_slot, tm, stream);
   mark(3);
-  moe_status st = hip_status();
+  st = hip_status();
   if (st != MOE_OK) return st;
 
   // 4. W1/W3 + SwiGLU
@@ -460,10 +467,10 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
 extern "C" {
 
 moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, const float* bias,
-                       const void* W1t, const void* W3t, const void* W2t, const void* W1s,
+                       const void* W1, const void* W3, const void* W2, const void* W1s,
                        const void* W3s, const void* W2s, void* out, void* ws, size_t ws_bytes,
                        const moe_debug* dbg, hipStream_t stream) {
-  return forward_impl(p, x, gate_w, bias, W1t, W3t, W2t, W1s, W3s, W2s, out, ws, ws_bytes, dbg,
+  return forward_impl(p, x, gate_w, bias, W1, W3, W2, W1s, W3s, W2s, out, ws, ws_bytes, dbg,
                       stream, false);
 }
 
@@ -481,6 +488,18 @@ moe_status moe_ring_error_flag(const moe_problem* p, void* ws, size_t ws_bytes, 
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   *flag = at<int32_t>(ws, L.ring_ctrl) + 8 + 2 * L.max_mtiles;
   return MOE_OK;
+}
+
+moe_status moe_ring_status(const moe_problem* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int32_t* flag = nullptr;
+  const moe_status st = moe_ring_error_flag(p, ws, ws_bytes, &flag);
+  if (st != MOE_OK) return st;
+  int32_t v = 0;
+  (void)hipGetLastError();
+  hipError_t e = hipMemcpyAsync(&v, flag, sizeof v, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return from_code(static_cast<int>(e));
+  return v ? MOE_ERR_DEVICE : MOE_OK;
 }
 
 moe_status moe_forward_ring(const moe_problem* p, const void* x, const void* gate_w,

@@ -372,8 +372,12 @@ do {                                                                            
   const cfloat* sbp1 = nullptr;
   float sb_cur0 = 0.f, sb_cur1 = 0.f, sb_nxt0 = 0.f, sb_nxt1 = 0.f;
   if constexpr (DT == kFP8) {
-    const int nb = (PHASE == 1) ? static_cast<int>(n0 / 256)  // 128 f columns per tile
-                                : static_cast<int>((n0 + wn * WTN) / 128);
+    // the scale block of this wave's columns; waves whose columns all lie
+    // past N (the last n-tile of a ragged N) are clamped to the last block,
+    // so the scalar loads stay inside the expert's scale rows (their
+    // results feed only columns that are never stored)
+    const int nb = min(nblocks - 1, (PHASE == 1) ? static_cast<int>(n0 / 256)  // 128 f per tile
+                                                 : static_cast<int>((n0 + wn * WTN) / 128));
     const int64_t base = static_cast<int64_t>(e) * kblocks * nblocks + nb;
     sbp0 = (const cfloat*)(g.sb0) + base;
     sbp1 = (PHASE == 1) ? (const cfloat*)(g.sb1) + base : sbp0;

@@ -87,7 +87,8 @@ constexpr int kRingPollLimit = 1 << 22;
 constexpr int kRingForcedPollMax = 4096;
 
 // Gate: logits [T][E] (+ bias), top-k ids and renormalised weights [T][k].
-void launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
+// Returns a hipError_t.
+int launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
                  int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s);
 // S shared experts add T slots each after the T*k routed ones (slot
 // T*k + s*T + t holds token t, k-slot k + s) and their m-tiles after the

@@ -8,8 +8,9 @@
 // slot and padding exists only in the tile map, never in memory (the local
 // "in-place padding" idea of the FlashMoE Kernel page, Communication section).
 //
-// No global atomics: each chunk of consecutive pairs is counted by one
-// wavefront into a [chunks x E] table; one workgroup scans it in (expert,
+// No atomics of any kind: each chunk of consecutive pairs is counted by one
+// wavefront (ballot-matched lanes, one writer per expert) into a [chunks x E]
+// table; one workgroup scans it in (expert,
 // chunk) order; the scatter wavefront of each chunk re-ranks its pairs with
 // ballots so equal experts keep increasing q = t*k + j order.  When all the
 // pairs fit one chunk (decode), one workgroup does the three steps in a
@@ -33,15 +34,35 @@ __device__ __forceinline__ uint64_t match_lanes(int e, int nbits, bool active) {
   return m;
 }
 
+// Count the experts of pairs [q0, q1) into cnt[] (LDS) with one wavefront and
+// no atomics: in each group of 64 pairs, the lanes holding the same expert are
+// found with ballots over the expert bits, and the last of them adds the
+// group's count for that expert.  Distinct experts have distinct writers, and
+// the groups run one after another, so every count is a plain add.
+__device__ void count_run(const int32_t* __restrict__ ids, int q0, int q1, int nbits,
+                          int32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int qb = q0; qb < q1; qb += 64) {
+    const int q = qb + lane;
+    const bool active = q < q1;
+    const int e = active ? ids[q] : 0;
+    const uint64_t peers = match_lanes(e, nbits, active);
+    if (active && __popcll(peers & ~below) == 1) cnt[e] += __popcll(peers);  // last peer
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+}
+
 __global__ __launch_bounds__(64) void hist_kernel(const int32_t* __restrict__ ids, int n,
-                                                  int E, int chunk, int32_t* __restrict__ table) {
+                                                  int E, int nbits, int chunk,
+                                                  int32_t* __restrict__ table) {
   extern __shared__ int32_t cnt[];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   __syncthreads();
   const int q0 = blockIdx.x * chunk;
-  const int q1 = min(n, q0 + chunk);
-  for (int q = q0 + lane; q < q1; q += 64) atomicAdd(&cnt[ids[q]], 1);  // LDS integer add
+  count_run(ids, q0, min(n, q0 + chunk), nbits, cnt);
   __syncthreads();
   for (int e = lane; e < E; e += 64) table[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
 }
@@ -208,7 +229,7 @@ __global__ __launch_bounds__(1024) void permute_one_kernel(
   const int tid = threadIdx.x;
   if (tid < E) s_tab[tid] = 0;
   __syncthreads();
-  for (int q = tid; q < n; q += 1024) atomicAdd(&s_tab[ids[q]], 1);  // LDS integer add
+  if (tid < 64) count_run(ids, 0, n, nbits, s_tab);  // n <= one chunk of pairs
   __syncthreads();
   scan_core(s_tab, 1, E, bm, counts, offsets, tm, T, k, S, slot_token, slot_k, s_cnt);
   if (tid < E) s_tab[tid] += s_cnt[tid];
@@ -242,7 +263,7 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int S, int bm, int3
                                           slot_token, slot_k, token_slot);
     return;
   }
-  if (nchunk > 0) hist_kernel<<<nchunk, 64, lds, s>>>(ids, n, E, chunk, table);
+  if (nchunk > 0) hist_kernel<<<nchunk, 64, lds, s>>>(ids, n, E, nbits, chunk, table);
   // the table in LDS when it fits next to the kernel's 8 KB of static LDS
   constexpr size_t kMaxTab = 144 * 1024;
   static const bool big_lds = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel<true>),

@@ -450,6 +450,30 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
   }
 }
 
+// Raise the dynamic LDS limit of one gate_kernel instantiation to the 160 KB
+// of a CU, once per instantiation (a function-local static of a template is
+// per instantiation); the result of that first call is returned every time.
+template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE>
+hipError_t gate_lds_attr() {
+  static const hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(gate_kernel<TEF, WS, KB, TG, BF16, FUSE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  return e;
+}
+
+template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE>
+int launch_gate_variant(const void* x, const void* gate_w, const float* bias, float* logits,
+                        int32_t* ids, float* w, int T, int d, int E, int k, hipStream_t s) {
+  const hipError_t attr = gate_lds_attr<TEF, WS, KB, TG, BF16, FUSE>();
+  if (attr != hipSuccess) return static_cast<int>(attr);
+  const dim3 grid((T + 16 * TG - 1) / (16 * TG), FUSE ? 1 : (E + 16 * TEF - 1) / (16 * TEF));
+  size_t lds = sizeof(float) * 2 * static_cast<size_t>(GateLds<TEF, KB, TG>::BUF);
+  if (FUSE) lds = std::max(lds, sizeof(float) * 16 * TG * static_cast<size_t>(E + 1));
+  gate_kernel<TEF, WS, KB, TG, BF16, FUSE>
+      <<<grid, 64 * TG * WS, lds, s>>>(x, gate_w, bias, logits, ids, w, T, d, E, k);
+  return static_cast<int>(hipGetLastError());
+}
+
 }  // namespace
 
 void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int k,
@@ -467,10 +491,11 @@ void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int 
 // the chip >= 1024 waves; otherwise experts are split across workgroups (as many
 // fragments per wave as still give >= 1024 waves) and a top-k kernel follows.
 // Two waves share each token group where the fragments allow, so that one
-// wave's staging overlaps the other's MFMAs.  d % 32 == 0.
-void launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
-                 int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s) {
-  if (T <= 0) return;
+// wave's staging overlaps the other's MFMAs.  d % 32 == 0.  Returns a
+// hipError_t (hipSuccess when everything was enqueued).
+int launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
+                int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s) {
+  if (T <= 0) return 0;
   const long long tw = (T + 15) / 16;  // token waves
   const int ef = (E + 15) / 16;        // expert fragments
   int tef = 1;
@@ -488,29 +513,21 @@ void launch_gate(const void* x, const void* gate_w, const float* bias, float* lo
       }
     }
   }
-  auto go = [&](auto kern, int TEF, int WS, int KB, int TG, bool fused) {
-    dim3 grid((T + 16 * TG - 1) / (16 * TG), fused ? 1 : (E + 16 * TEF - 1) / (16 * TEF));
-    size_t lds = sizeof(float) * 2 *
-                 static_cast<size_t>(16 * TG * (4 * (KB / 4 + kGateGroupPad) + 4) +
-                                     KB * (16 * TEF + 16));
-    if (fused) lds = std::max(lds, sizeof(float) * 16 * TG * static_cast<size_t>(E + 1));
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-        160 * 1024);  // once per kernel: every configuration fits in 160 KB
-    (void)attr;
-    kern<<<grid, 64 * TG * WS, lds, s>>>(x, gate_w, bias, logits, ids, w, T, d, E, k);
-  };
+  int rc = -1;
   // (TEF, WS, KB, TG): the widest expert tiles stage 128 tokens per
   // workgroup, which halves the gate_w traffic per token
-#define MOE_G(TEF_, WS_, KB_, TG_)                                                        \
-  if (tef == TEF_) {                                                                      \
-    if (fuse) {                                                                           \
-      if (bf16) go(gate_kernel<TEF_, WS_, KB_, TG_, true, true>, TEF_, WS_, KB_, TG_, true); \
-      else go(gate_kernel<TEF_, WS_, KB_, TG_, false, true>, TEF_, WS_, KB_, TG_, true);  \
-    } else {                                                                              \
-      if (bf16) go(gate_kernel<TEF_, WS_, KB_, TG_, true, false>, TEF_, WS_, KB_, TG_, false); \
-      else go(gate_kernel<TEF_, WS_, KB_, TG_, false, false>, TEF_, WS_, KB_, TG_, false); \
-    }                                                                                     \
+#define MOE_G(TEF_, WS_, KB_, TG_)                                                          \
+  if (tef == TEF_) {                                                                        \
+    if (fuse)                                                                               \
+      rc = bf16 ? launch_gate_variant<TEF_, WS_, KB_, TG_, true, true>(                     \
+                      x, gate_w, bias, logits, ids, w, T, d, E, k, s)                       \
+                : launch_gate_variant<TEF_, WS_, KB_, TG_, false, true>(                    \
+                      x, gate_w, bias, logits, ids, w, T, d, E, k, s);                      \
+    else                                                                                    \
+      rc = bf16 ? launch_gate_variant<TEF_, WS_, KB_, TG_, true, false>(                    \
+                      x, gate_w, bias, logits, ids, w, T, d, E, k, s)                       \
+                : launch_gate_variant<TEF_, WS_, KB_, TG_, false, false>(                   \
+                      x, gate_w, bias, logits, ids, w, T, d, E, k, s);                      \
   }
   MOE_G(1, 1, 128, 4)
   MOE_G(2, 2, 128, 4)
@@ -518,7 +535,9 @@ void launch_gate(const void* x, const void* gate_w, const float* bias, float* lo
   MOE_G(8, 2, 64, 4)
   MOE_G(16, 2, 32, 8)
 #undef MOE_G
+  if (rc != 0) return rc;
   if (!fuse) launch_topk(logits, ids, w, T, E, k, s);
+  return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace moe

@@ -17,6 +17,22 @@ def say(*a):
     print(*a, flush=True)
 
 
+def poison_(t: torch.Tensor) -> torch.Tensor:
+    """Fill every byte of t with 0xFF: NaN in fp32 and bf16, -1 in int32.  A
+    kernel that skips an element it should write leaves NaN or -1 behind
+    instead of a stale value from an earlier call in the same memory."""
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+def poisoned(shape, dtype, device="cuda") -> torch.Tensor:
+    return poison_(torch.empty(shape, dtype=dtype, device=device))
+
+
+def poisoned_workspace(p, device="cuda") -> torch.Tensor:
+    return poison_(B.alloc_workspace(p, device))
+
+
 def gpu_inputs(cfg, seed=None):
     inp = make_inputs(cfg, device="cuda", seed=seed)
     torch.cuda.synchronize()
@@ -58,9 +74,9 @@ def gpu_route(cfg, inp, T=None):
     T = inp["x"].shape[0] if T is None else T
     p = B.problem_of(cfg, T=T)
     dev = inp["x"].device
-    logits = torch.empty((T, cfg.E), dtype=torch.float32, device=dev)
-    ids = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+    logits = poisoned((T, cfg.E), torch.float32, dev)
+    ids = poisoned((T, cfg.k), torch.int32, dev)
+    w = poisoned((T, cfg.k), torch.float32, dev)
     B.moe_route(p, inp["x"], inp["gate_w"], inp.get("bias"), logits, ids, w)
     torch.cuda.synchronize()
     return logits, ids, w
@@ -71,16 +87,54 @@ def gpu_permute(cfg, ids, T=None, block_m=0):
     p = B.problem_of(cfg, T=T, block_m=block_m)
     dev = ids.device
     n = T * cfg.k
-    out = {"counts": torch.empty(cfg.E, dtype=torch.int32, device=dev),
-           "offsets": torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
-           "slot_token": torch.empty(n, dtype=torch.int32, device=dev),
-           "slot_k": torch.empty(n, dtype=torch.int32, device=dev),
-           "token_slot": torch.empty(n, dtype=torch.int32, device=dev)}
-    ws = B.alloc_workspace(p, dev)
+    out = {"counts": poisoned(cfg.E, torch.int32, dev),
+           "offsets": poisoned(cfg.E + 1, torch.int32, dev),
+           "slot_token": poisoned(n, torch.int32, dev),
+           "slot_k": poisoned(n, torch.int32, dev),
+           "token_slot": poisoned(n, torch.int32, dev)}
+    ws = poisoned_workspace(p, dev)
     B.moe_permute(p, ids, out["counts"], out["offsets"], out["slot_token"], out["slot_k"],
                   out["token_slot"], ws)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def forward(cfg, inp, packed, out_dtype=None, block_m=0, dbg=None, stream=None):
+    """One moe_forward of cfg through the C ABI with a freshly allocated
+    workspace and output whose every byte is 0xFF (NaN) beforehand.  packed
+    None passes the weights in their stated layout (MOE_W_KN)."""
+    T = inp["x"].shape[0]
+    p = B.problem_of(cfg, T=T, block_m=block_m, out_dtype=out_dtype,
+                     w_layout=B.MOE_W_KN if packed is None else B.MOE_W_NK)
+    ws = poisoned_workspace(p, inp["x"].device)
+    out = poison_(B.out_tensor(cfg, T=T, device=inp["x"].device, out_dtype=out_dtype))
+    return B.forward(cfg, inp, packed, out=out, ws=ws, dbg=dbg, out_dtype=out_dtype,
+                     block_m=block_m, stream=stream)
+
+
+def forward_ring(cfg, inp, packed, ws=None, out=None, out_dtype=None, block_m=0, dbg=None,
+                 stream=None):
+    """moe_forward_ring through the C ABI; a workspace or output not passed in
+    is allocated with every byte 0xFF (NaN) beforehand."""
+    T = inp["x"].shape[0]
+    p = B.problem_of(cfg, T=T, block_m=block_m, out_dtype=out_dtype)
+    if ws is None:
+        ws = poisoned(B.ring_workspace_size(p), torch.uint8, inp["x"].device)
+    if out is None:
+        out = poison_(B.out_tensor(cfg, T=T, device=inp["x"].device, out_dtype=out_dtype))
+    return B.forward(cfg, inp, packed, out=out, ws=ws, dbg=dbg, out_dtype=out_dtype,
+                     block_m=block_m, stream=stream, ring=True)
+
+
+def debug_buffers(cfg, T=None, keys=None):
+    """Poisoned device buffers for moe_debug's routing outputs."""
+    T = cfg.T if T is None else T
+    n = T * cfg.k
+    sizes = {"topk_ids": n, "topk_w": n, "counts": cfg.E, "offsets": cfg.E + 1,
+             "slot_token": n, "slot_k": n, "token_slot": n}
+    keys = keys or list(sizes)
+    return {k: poisoned(sizes[k], torch.float32 if k == "topk_w" else torch.int32)
+            for k in keys}
 
 
 def free():

@@ -35,8 +35,44 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     lib = _lib()
-    for code in range(5):
-        assert lib.moe_status_string(code)
+    names = set()
+    for code in range(6):
+        names.add(lib.moe_status_string(code))
+    assert len(names) == 6 and b"unknown status" not in names
+    assert lib.moe_status_string(6) == b"unknown status"
+
+
+def test_weight_layout_is_part_of_the_problem():
+    # a zero-initialised moe_problem means the stated [K][N] weight layout;
+    # an unknown layout is an invalid problem, and MXFP4 weights have no
+    # stated [K][N] form: both are refused before anything is looked at
+    lib = _lib()
+    assert ctypes.sizeof(B.MoEProblem) == 3 * 8 + 8 * 4
+    assert B.MoEProblem().w_layout == B.MOE_W_KN == 0
+    bad = B.problem(16, 128, 128, 8, 2, 1, 1, 1, w_layout=7)
+    with pytest.raises(B.MoEError) as e:
+        B.workspace_size(bad)
+    assert e.value.code == 1
+    mx = B.problem(16, 128, 128, 8, 2, 1, B.MOE_MXFP4, 1, w_layout=B.MOE_W_KN)
+    rc = lib.moe_forward(ctypes.byref(mx), None, None, None, None, None, None, None, None,
+                         None, None, None, 0, None, None)
+    assert rc == 2
+    for layout in (B.MOE_W_KN, B.MOE_W_NK):  # both lay out the same workspace
+        p = B.problem(4096, 1024, 512, 16, 2, 1, 1, 1, w_layout=layout)
+        assert B.workspace_size(p) == B.workspace_size(B.problem(4096, 1024, 512, 16, 2, 1, 1, 1))
+
+
+def test_ring_status_checks_arguments():
+    # moe_ring_status validates like moe_ring_error_flag before it touches
+    # the device: bad problem, NULL workspace, too small a workspace
+    lib = _lib()
+    p = B.problem(16384, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_BF16, B.MOE_BF16)
+    n = B.ring_workspace_size(p)
+    fake = 1 << 40
+    assert lib.moe_ring_status(ctypes.byref(p), None, n, None) == 1
+    assert lib.moe_ring_status(ctypes.byref(p), fake, n - 1, None) == 3
+    fp8 = B.problem(16384, 2048, 2048, 32, 2, B.MOE_BF16, B.MOE_FP8_E4M3, B.MOE_BF16)
+    assert lib.moe_ring_status(ctypes.byref(fp8), fake, n, None) == 2
 
 
 def test_workspace_size_is_pure_and_checks_args():

@@ -4,6 +4,9 @@ Routing (logits, ids), histogram, offsets, permutation and FP8 activation
 codes must be bit-exact; gate weights within 4 fp32 ulp; layer outputs
 within the tolerance of the layer's precision (fp32 output: max error <=
 bar x RMS; bf16 output: every element within bar x RMS + 1/2 bf16 ulp).
+Every workspace, output and debug buffer is filled with 0xFF bytes (NaN,
+or -1 for integers) before the call that writes it, so an element a kernel
+fails to write cannot pass on a value left by an earlier call.
 """
 import numpy as np
 import pytest
@@ -12,8 +15,9 @@ import torch
 import oracle
 from mixture_experts_layer_softmax_amd import binding as B
 from mixture_experts_layer_softmax_amd.configs import BF16, CONFIGS, F32, FP8, MXFP4, MoEConfig
-from tests.gpu_common import (free, gpu_inputs, gpu_permute, gpu_route, oracle_forward_rows,
-                              oracle_route_rows, say)
+from tests.gpu_common import (debug_buffers, forward, forward_ring, free, gpu_inputs, gpu_permute, gpu_route,
+                              oracle_forward_rows, oracle_route_rows, poison_, poisoned,
+                              poisoned_workspace, say)
 from tests.helpers import TOL, check_output, f32_ulps
 
 pytestmark = pytest.mark.gpu
@@ -32,9 +36,9 @@ REDUCED = {
 }
 
 
-def _forward(cfg, inp, out_dtype=None, block_m=0, dbg=None):
-    packed = B.pack_weights(inp)
-    out = B.forward(cfg, inp, packed, out_dtype=out_dtype, block_m=block_m, dbg=dbg)
+def _forward(cfg, inp, out_dtype=None, block_m=0, dbg=None, packed=None):
+    packed = B.pack_weights(inp) if packed is None else packed
+    out = forward(cfg, inp, packed, out_dtype=out_dtype, block_m=block_m, dbg=dbg)
     torch.cuda.synchronize()
     return out
 
@@ -176,7 +180,7 @@ def test_route_logits_in_the_workspace():
     p = B.problem_of(cfg)
     ids2 = torch.full_like(ids, -1)
     w2 = torch.full_like(w, -1.0)
-    ws = B.alloc_workspace(p)
+    ws = poisoned_workspace(p)
     B.moe_route(p, inp["x"], inp["gate_w"], inp.get("bias"), None, ids2, w2, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(ids2, ids) and torch.equal(w2, w)
@@ -191,8 +195,8 @@ def test_quantize_fp8_bit_exact():
     x = (torch.randn((333, 1024), generator=g, device="cuda") *
          torch.logspace(-3, 3, 1024, device="cuda")).to(torch.bfloat16)
     x[7, 128:256] = 0  # an all-zero group
-    q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
-    s = torch.empty((333, 8), dtype=torch.float32, device="cuda")
+    q = poisoned(x.shape, torch.uint8)
+    s = poisoned((333, 8), torch.float32)
     B.moe_quantize_fp8(x, q, s)
     torch.cuda.synchronize()
     rq, rs = oracle.fp8_quant_rows(x.float().cpu().numpy())
@@ -208,8 +212,8 @@ def test_quantize_mx_bit_exact():
          torch.logspace(-3, 3, 1024, device="cuda")).to(torch.bfloat16)
     x[7, 128:160] = 0  # an all-zero block
     x[9, 0:32] = 3.0   # a constant block
-    q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
-    s = torch.empty((333, 32), dtype=torch.uint8, device="cuda")
+    q = poisoned(x.shape, torch.uint8)
+    s = poisoned((333, 32), torch.uint8)
     B.moe_quantize_mx(x, q, s)
     torch.cuda.synchronize()
     rq, rs = oracle.mx_quant_rows(x.float().cpu().numpy(), oracle.MX_E4M3)
@@ -253,8 +257,7 @@ def test_largest_supported_operands(name):
     say("max offsets", name)
     assert max(cfg.T * cfg.k * cfg.f, cfg.T * cfg.d) * 2 >= (1 << 31) - 2 * max(cfg.f, cfg.d)
     inp = gpu_inputs(cfg)
-    n = cfg.T * cfg.k
-    dbg = {"topk_ids": torch.empty(n, dtype=torch.int32, device="cuda")}
+    dbg = debug_buffers(cfg, keys=["topk_ids"])
     out = _forward(cfg, inp, dbg=dbg)
     rng = np.random.default_rng(1)
     rows = np.sort(rng.choice(cfg.T, size=12, replace=False))
@@ -296,15 +299,7 @@ def test_forward_routing_equals_route_and_permute():
     cfg = REDUCED["skewed_bf16_r"]
     say("routing consistency")
     inp = gpu_inputs(cfg)
-    n = cfg.T * cfg.k
-    dev = "cuda"
-    dbg = {"topk_ids": torch.empty(n, dtype=torch.int32, device=dev),
-           "topk_w": torch.empty(n, dtype=torch.float32, device=dev),
-           "counts": torch.empty(cfg.E, dtype=torch.int32, device=dev),
-           "offsets": torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
-           "slot_token": torch.empty(n, dtype=torch.int32, device=dev),
-           "slot_k": torch.empty(n, dtype=torch.int32, device=dev),
-           "token_slot": torch.empty(n, dtype=torch.int32, device=dev)}
+    dbg = debug_buffers(cfg)
     _forward(cfg, inp, dbg=dbg)
     _, ids, w = gpu_route(cfg, inp)
     assert torch.equal(dbg["topk_ids"].view(cfg.T, cfg.k), ids)
@@ -319,7 +314,7 @@ def test_forward_is_deterministic():
     say("determinism")
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
-    outs = [B.forward(cfg, inp, packed, out_dtype=F32) for _ in range(4)]
+    outs = [forward(cfg, inp, packed, out_dtype=F32) for _ in range(4)]
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
@@ -333,15 +328,15 @@ def test_concurrent_calls_on_two_streams():
     say("two streams", [c.name for c in cfgs])
     inps = [gpu_inputs(c) for c in cfgs]
     packs = [B.pack_weights(i) for i in inps]
-    ref = [B.forward(c, i, p, out_dtype=F32) for c, i, p in zip(cfgs, inps, packs)]
+    ref = [forward(c, i, p, out_dtype=F32) for c, i, p in zip(cfgs, inps, packs)]
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [[], []]
     for rep in range(3):
         for j in (0, 1):
             with torch.cuda.stream(streams[j]):
-                outs[j].append(B.forward(cfgs[j], inps[j], packs[j], out_dtype=F32,
-                                         stream=streams[j]))
+                outs[j].append(forward(cfgs[j], inps[j], packs[j], out_dtype=F32,
+                                       stream=streams[j]))
     torch.cuda.synchronize()
     for j in (0, 1):
         for o in outs[j]:
@@ -356,9 +351,9 @@ def test_gemm_clock_record():
     say("gemm clock")
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
-    ref = B.forward(cfg, inp, packed, out_dtype=F32)
+    ref = forward(cfg, inp, packed, out_dtype=F32)
     clock = torch.zeros(4, dtype=torch.int64, device="cuda")
-    got = B.forward(cfg, inp, packed, out_dtype=F32, dbg={"gemm_clock": clock})
+    got = forward(cfg, inp, packed, out_dtype=F32, dbg={"gemm_clock": clock})
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
     c = clock.cpu().tolist()
@@ -410,13 +405,10 @@ def test_shared_expert_leaves_routing_alone():
     plain = cfg.replace(n_shared=0)
     say("shared routing")
     inp = gpu_inputs(cfg)
-    n = cfg.T * cfg.k
     keys = ("topk_ids", "counts", "offsets", "slot_token", "slot_k", "token_slot")
-    sizes = {"counts": cfg.E, "offsets": cfg.E + 1}
     dbgs = []
     for c in (cfg, plain):
-        dbg = {key: torch.empty(sizes.get(key, n), dtype=torch.int32, device="cuda")
-               for key in keys}
+        dbg = debug_buffers(c, keys=keys)
         _forward(c, inp, dbg=dbg)
         dbgs.append(dbg)
     for key in keys:
@@ -424,12 +416,15 @@ def test_shared_expert_leaves_routing_alone():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads in the launch configuration the benchmark times;
-# outputs compared on a sample of tokens the oracle computes one by one
+# full-size workloads in the launch configuration the benchmark times:
+# routing (logits, ids, weights) of every token through moe_route, the fused
+# call's routing and permutation of every token, and the outputs of a token
+# sample the oracle computes one by one -- both with the fp32 output (the
+# primary bar) and with the workload's own output type
 # ---------------------------------------------------------------------------
 
-FULL_SAMPLE = {"prefill_bf16": 48, "decode_bf16": 12, "skewed_bf16": 24, "prefill_fp8": 6,
-               "prefill_bf16_shared": 24, "prefill_mxfp4": 6, "decode_mxfp4": 12}
+FULL_SAMPLE = {"prefill_bf16": 256, "decode_bf16": 64, "skewed_bf16": 256, "prefill_fp8": 64,
+               "prefill_bf16_shared": 256, "prefill_mxfp4": 64, "decode_mxfp4": 64}
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16", "decode_bf16", "skewed_bf16",
@@ -439,29 +434,69 @@ def test_full_size_parity(name):
     cfg = CONFIGS[name]
     say("full", name)
     inp = gpu_inputs(cfg)
-    n = cfg.T * cfg.k
-    dbg = {"topk_ids": torch.empty(n, dtype=torch.int32, device="cuda"),
-           "counts": torch.empty(cfg.E, dtype=torch.int32, device="cuda")}
-    out = _forward(cfg, inp, dbg=dbg)
-    counts = dbg["counts"].cpu().numpy()
-    assert counts.sum() == n
-    rng = np.random.default_rng(0)
-    if name == "tiny_fp32":
+    # the gate of every token: logits and ids bit for bit, weights within 4 ulp
+    logits, ids, w = gpu_route(cfg, inp)
+    say("  oracle gate of", cfg.T, "tokens")
+    ref_l, ref_ids, ref_w = oracle_route_rows(cfg, inp, np.arange(cfg.T))
+    assert np.array_equal(logits.cpu().numpy(), ref_l)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert f32_ulps(w.cpu().numpy(), ref_w) <= 4
+    del logits
+    # the whole layer: its routing and permutation on every token
+    packed = B.pack_weights(inp)
+    dbg = debug_buffers(cfg)
+    out = _forward(cfg, inp, dbg=dbg, packed=packed)
+    assert torch.equal(dbg["topk_ids"].view(cfg.T, cfg.k), ids)
+    assert torch.equal(dbg["topk_w"].view(cfg.T, cfg.k), w)
+    perm = oracle.permute(ref_ids, cfg.E)
+    for key, v in perm.items():
+        assert np.array_equal(dbg[key].cpu().numpy(), v), key
+    del dbg
+    # outputs of a token sample (first and last token always)
+    if cfg.T <= FULL_SAMPLE.get(name, cfg.T):
         rows = np.arange(cfg.T)
     else:
+        rng = np.random.default_rng(0)
         rows = np.sort(rng.choice(cfg.T, size=FULL_SAMPLE[name], replace=False))
-        rows[0], rows[-1] = 0, cfg.T - 1  # first and last token always
-    ref, ref_ids, _ = oracle_forward_rows(cfg, inp, rows)
-    got_ids = dbg["topk_ids"].view(cfg.T, cfg.k).cpu().numpy()[rows]
-    assert np.array_equal(got_ids, ref_ids)
-    _outputs_ok(cfg, out[torch.as_tensor(rows, device="cuda")], ref, "sampled")
-    # full-size routing of every token against the oracle gate, in blocks
-    step = 4096 if cfg.E * cfg.d < 2 ** 20 else 512
-    sel = np.arange(0, cfg.T, max(1, cfg.T // step)) if cfg.T > step else np.arange(cfg.T)
-    _, r_ids, _ = oracle_route_rows(cfg, inp, sel)
-    assert np.array_equal(dbg["topk_ids"].view(cfg.T, cfg.k).cpu().numpy()[sel], r_ids)
-    del inp, out
+        rows[0], rows[-1] = 0, cfg.T - 1
+    say("  oracle forward of", len(rows), "tokens")
+    ref, ref_rows_ids, _ = oracle_forward_rows(cfg, inp, rows)
+    assert np.array_equal(ref_rows_ids, ref_ids[rows])
+    sel = torch.as_tensor(rows, device="cuda")
+    _outputs_ok(cfg, out[sel], ref, "native out")
+    del out
     free()
+    if cfg.out_dtype != F32:
+        out32 = _forward(cfg, inp, out_dtype=F32, packed=packed)
+        _outputs_ok(cfg, out32[sel], ref, "fp32 out")
+        del out32
+    del inp, packed
+    free()
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16_r", "decode_bf16_r",
+                                  "prefill_fp8_r"])
+def test_stated_layout_weights_match_or_are_refused(name):
+    # weights passed as the workloads state them ([E][d][f], [E][f][d]) with
+    # w_layout MOE_W_KN: the call either computes the layer (checked against
+    # the oracle) or refuses with MOE_ERR_UNSUPPORTED before writing anything;
+    # it never reads them as the packed layout
+    cfg = REDUCED[name]
+    say("stated layout", name)
+    inp = gpu_inputs(cfg)
+    p = B.problem_of(cfg, w_layout=B.MOE_W_KN)
+    ws = poisoned_workspace(p)
+    out = torch.full((cfg.T, cfg.d), 7.0, device="cuda").to(B.out_tensor(cfg).dtype)
+    try:
+        B.forward(cfg, inp, None, out=out, ws=ws)
+    except B.MoEError as e:
+        assert e.code == 2, e
+        torch.cuda.synchronize()
+        assert (out.float() == 7.0).all()
+        return
+    torch.cuda.synchronize()
+    ref, _, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
+    _outputs_ok(cfg, out, ref, "stated layout")
 
 
 def test_abi_errors_launch_nothing():
@@ -513,9 +548,9 @@ def test_forward_graph_replay(name):
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
     p = B.problem_of(cfg)
-    ws = B.alloc_workspace(p)
-    out = B.out_tensor(cfg)
-    ref = B.forward(cfg, inp, packed, out=torch.empty_like(out), ws=torch.empty_like(ws))
+    ws = poisoned_workspace(p)
+    out = poison_(B.out_tensor(cfg))
+    ref = forward(cfg, inp, packed)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
@@ -560,8 +595,7 @@ def _random_configs(n=40, seed=1234):
 def test_random_config_parity(cfg, block_m):
     say("random", cfg, block_m)
     inp = gpu_inputs(cfg)
-    n = cfg.T * cfg.k
-    dbg = {"topk_ids": torch.empty(n, dtype=torch.int32, device="cuda")}
+    dbg = debug_buffers(cfg, keys=["topk_ids"])
     ref, ref_ids, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
     out = _forward(cfg, inp, out_dtype=F32, block_m=block_m, dbg=dbg)
     assert np.array_equal(dbg["topk_ids"].view(cfg.T, cfg.k).cpu().numpy(), ref_ids)
@@ -591,13 +625,13 @@ def test_ring_forward_equals_forward(name):
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
     for out_dtype in (F32, BF16):
-        ref = B.forward(cfg, inp, packed, out_dtype=out_dtype, block_m=256)
+        ref = forward(cfg, inp, packed, out_dtype=out_dtype, block_m=256)
         for rep in range(2):
-            got = B.forward(cfg, inp, packed, out_dtype=out_dtype, block_m=256, ring=True)
+            got = forward_ring(cfg, inp, packed, out_dtype=out_dtype, block_m=256)
             torch.cuda.synchronize()
             assert torch.equal(got, ref), (name, out_dtype, rep)
     ref64, _, _ = oracle_forward_rows(cfg, inp, np.arange(min(cfg.T, 64)))
-    out = B.forward(cfg, inp, packed, out_dtype=F32, block_m=256, ring=True)
+    out = forward_ring(cfg, inp, packed, out_dtype=F32, block_m=256)
     torch.cuda.synchronize()
     _outputs_ok(cfg, out[: ref64.shape[0]], ref64, "ring vs oracle")
 
@@ -608,8 +642,8 @@ def test_ring_full_size_equals_forward(name):
     say("ring full", name)
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
-    ref = B.forward(cfg, inp, packed)
-    got = B.forward(cfg, inp, packed, ring=True)
+    ref = forward(cfg, inp, packed)
+    got = forward_ring(cfg, inp, packed)
     torch.cuda.synchronize()
     assert torch.equal(got, ref), name
     del inp, packed, ref, got
@@ -630,17 +664,17 @@ def test_ring_graph_replay():
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
     p = B.problem_of(cfg, block_m=256)
-    ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ws = poisoned(B.ring_workspace_size(p), torch.uint8)
     out = B.out_tensor(cfg)
-    ref = B.forward(cfg, inp, packed, block_m=256)
+    ref = forward(cfg, inp, packed, block_m=256)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
-        B.forward(cfg, inp, packed, out=out, ws=ws, block_m=256, stream=s, ring=True)
+        forward_ring(cfg, inp, packed, out=out, ws=ws, block_m=256, stream=s)
         s.synchronize()
         with torch.cuda.graph(g, stream=s):
-            B.forward(cfg, inp, packed, out=out, ws=ws, block_m=256, stream=s, ring=True)
+            forward_ring(cfg, inp, packed, out=out, ws=ws, block_m=256, stream=s)
     torch.cuda.synchronize()
     for rep in range(3):
         out.fill_(0)
@@ -660,10 +694,10 @@ def test_ring_repeated_runs_identical():
     say("ring repeated", cfg.name)
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
-    ref = B.forward(cfg, inp, packed)
+    ref = forward(cfg, inp, packed)
     p = B.problem_of(cfg)
-    ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
-    outs = [B.forward(cfg, inp, packed, ws=ws, ring=True) for _ in range(30)]
+    ws = poisoned(B.ring_workspace_size(p), torch.uint8)
+    outs = [forward_ring(cfg, inp, packed, ws=ws) for _ in range(30)]
     torch.cuda.synchronize()
     assert not B.ring_failed(p, ws)
     for i, o in enumerate(outs):
@@ -682,19 +716,19 @@ def test_ring_error_flag_reports_a_wait_that_gave_up():
     inp = gpu_inputs(cfg)
     packed = B.pack_weights(inp)
     p = B.problem_of(cfg, block_m=256)
-    ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
-    ref = B.forward(cfg, inp, packed, block_m=256)
-    out = B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True)
+    ws = poisoned(B.ring_workspace_size(p), torch.uint8)
+    ref = forward(cfg, inp, packed, block_m=256)
+    out = forward_ring(cfg, inp, packed, ws=ws, block_m=256)
     assert not B.ring_failed(p, ws)
     assert torch.equal(out, ref)
-    B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True,
+    forward_ring(cfg, inp, packed, ws=ws, block_m=256,
               dbg={"ring_poll_limit": 4, "ring_force_timeout": 1})
     assert B.ring_failed(p, ws)
-    out = B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True)
+    out = forward_ring(cfg, inp, packed, ws=ws, block_m=256)
     assert not B.ring_failed(p, ws)
     assert torch.equal(out, ref)
     # a poll limit alone only bounds the waits: a generous one changes nothing
-    out = B.forward(cfg, inp, packed, ws=ws, block_m=256, ring=True,
+    out = forward_ring(cfg, inp, packed, ws=ws, block_m=256,
                     dbg={"ring_poll_limit": 1 << 20})
     assert not B.ring_failed(p, ws)
     assert torch.equal(out, ref)
@@ -708,17 +742,17 @@ def test_ring_concurrent_on_two_streams():
     say("ring two streams", [c.name for c in cfgs])
     inps = [gpu_inputs(c) for c in cfgs]
     packs = [B.pack_weights(i) for i in inps]
-    ref = [B.forward(c, i, p, block_m=256) for c, i, p in zip(cfgs, inps, packs)]
+    ref = [forward(c, i, p, block_m=256) for c, i, p in zip(cfgs, inps, packs)]
     probs = [B.problem_of(c, block_m=256) for c in cfgs]
-    wss = [torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda") for p in probs]
+    wss = [poisoned(B.ring_workspace_size(p), torch.uint8) for p in probs]
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [[], []]
     for rep in range(3):
         for j in (0, 1):
             with torch.cuda.stream(streams[j]):
-                outs[j].append(B.forward(cfgs[j], inps[j], packs[j], ws=wss[j], block_m=256,
-                                         stream=streams[j], ring=True))
+                outs[j].append(forward_ring(cfgs[j], inps[j], packs[j], ws=wss[j], block_m=256,
+                                         stream=streams[j]))
     torch.cuda.synchronize()
     for j in (0, 1):
         assert not B.ring_failed(probs[j], wss[j])
