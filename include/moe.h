@@ -280,6 +280,28 @@ moe_status moe_forward(const moe_problem *p, const void *x, const void *gate_w,
                        const void *W2s, void *out, void *ws, size_t ws_bytes,
                        const moe_debug *dbg, hipStream_t stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc: moe_forward
+ * with its workspace in a device array of the library itself
+ * (MOE_NOALLOC_WORKSPACE_BYTES on each GPU it runs on, held until the process
+ * ends).  Nothing is allocated inside the call, by the library or any routine
+ * it calls; the caller still owns and passes every input and output, as in
+ * moe_forward (same arguments, less ws/ws_bytes; same results bit for bit).
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give wrong results; the
+ * array keeps the last call's contents, and every value a call reads from it
+ * is written by the same call first.
+ * MOE_ERR_WORKSPACE_TOO_SMALL (before anything is enqueued) when
+ * moe_workspace_size(p) exceeds MOE_NOALLOC_WORKSPACE_BYTES -- a decode-sized
+ * layer such as T = 64, d = 7168, f = 2048, E = 256, top_k = 8 needs 16 MB;
+ * other errors as moe_forward. */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_problem *p, const void *x, const void *gate_w,
+                               const float *bias, const void *W1, const void *W3,
+                               const void *W2, const void *W1s, const void *W3s,
+                               const void *W2s, void *out, const moe_debug *dbg,
+                               hipStream_t stream);
+
 /* The same layer forward with both expert GEMMs in ONE persistent launch
  * that hands h from the W1/W3 tasks to the W2 tasks through a bounded ring:
  * the ring of in-flight blocks (sized by blocks in flight, not by routed

@@ -23,7 +23,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ["moe_status_string", "moe_last_hip_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_quantize_fp8", "moe_quantize_mx", "moe_weight_bytes",
            "moe_pack_weight", "moe_forward", "moe_ring_workspace_size", "moe_forward_ring",
-           "moe_ring_error_flag", "moe_ring_status"]
+           "moe_ring_error_flag", "moe_ring_status", "moe_forward_noalloc"]
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # MOE_NOALLOC_WORKSPACE_BYTES
 
 
 class MoEProblem(ctypes.Structure):
@@ -85,6 +86,8 @@ def load(path: str = LIB_PATH):
     lib.moe_forward_ring.argtypes = [PP, P, P, P, P, P, P, P, P, S, ctypes.POINTER(MoEDebug), P]
     lib.moe_ring_error_flag.argtypes = [PP, P, S, ctypes.POINTER(P)]
     lib.moe_ring_status.argtypes = [PP, P, S, P]
+    lib.moe_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P,
+                                        ctypes.POINTER(MoEDebug), P]
     for fn in EXPORTS:
         if fn not in ("moe_status_string", "moe_last_hip_error"):
             getattr(lib, fn).restype = ctypes.c_int
@@ -191,6 +194,17 @@ def moe_forward(p, x, gate_w, bias, W1, W3, W2, W1s, W3s, W2s, out, ws, dbg=None
                             _p(W2), _p(W1s), _p(W3s), _p(W2s), _p(out), _p(ws), ws.numel(),
                             None if dbg_s is None else ctypes.byref(dbg_s), _stream(stream))
     _check("moe_forward", rc)
+
+
+def moe_forward_noalloc(p, x, gate_w, bias, W1, W3, W2, W1s, W3s, W2s, out, dbg=None,
+                        stream=None):
+    """moe_forward with the library's own static workspace (no allocation)."""
+    dbg_s = _debug_struct(dbg)
+    rc = load().moe_forward_noalloc(ctypes.byref(p), _p(x), _p(gate_w), _p(bias), _p(W1),
+                                    _p(W3), _p(W2), _p(W1s), _p(W3s), _p(W2s), _p(out),
+                                    None if dbg_s is None else ctypes.byref(dbg_s),
+                                    _stream(stream))
+    _check("moe_forward_noalloc", rc)
 
 
 def _debug_struct(dbg):

@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -187,6 +188,33 @@ moe_status from_code(int code) {
     g_last_hip = code;
     return MOE_ERR_HIP;
   }
+  return MOE_OK;
+}
+
+// Workspace of moe_forward_noalloc: a device array of the library, one copy
+// per GPU (each device's copy has its own address), held until the process
+// ends.  Host code never passes `scratch` itself to a kernel or a copy -- on
+// the host it only names the symbol; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = MOE_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the calling thread's current device's scratch array.
+moe_status scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_code(static_cast<int>(e));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) return from_code(static_cast<int>(g_scratch_err[dev]));
+  *ptr = g_scratch_ptr[dev];
   return MOE_OK;
 }
 
@@ -471,6 +499,19 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* gate_w, 
                        const void* W3s, const void* W2s, void* out, void* ws, size_t ws_bytes,
                        const moe_debug* dbg, hipStream_t stream) {
   return forward_impl(p, x, gate_w, bias, W1, W3, W2, W1s, W3s, W2s, out, ws, ws_bytes, dbg,
+                      stream, false);
+}
+
+moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* gate_w,
+                               const float* bias, const void* W1, const void* W3, const void* W2,
+                               const void* W1s, const void* W3s, const void* W2s, void* out,
+                               const moe_debug* dbg, hipStream_t stream) {
+  if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
+  if (make_layout(*p).total > kScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  const moe_status st = scratch_of_current_device(&ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(p, x, gate_w, bias, W1, W3, W2, W1s, W3s, W2s, out, ws, kScratchBytes, dbg,
                       stream, false);
 }
 

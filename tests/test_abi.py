@@ -62,6 +62,23 @@ def test_weight_layout_is_part_of_the_problem():
         assert B.workspace_size(p) == B.workspace_size(B.problem(4096, 1024, 512, 16, 2, 1, 1, 1))
 
 
+def test_noalloc_size_limit_is_checked_before_launch():
+    # moe_forward_noalloc refuses, before touching any pointer or the device,
+    # a problem whose workspace exceeds its static array
+    lib = _lib()
+    big = B.problem(16384, 2048, 2048, 32, 2, 1, 1, 1)
+    assert B.workspace_size(big) > B.NOALLOC_WORKSPACE_BYTES
+    rc = lib.moe_forward_noalloc(ctypes.byref(big), None, None, None, None, None, None, None,
+                                 None, None, None, None, None)
+    assert rc == 3
+    bad = B.problem(16, 64, 64, 4, 5, 1, 1, 1)  # top_k > E
+    rc = lib.moe_forward_noalloc(ctypes.byref(bad), None, None, None, None, None, None, None,
+                                 None, None, None, None, None)
+    assert rc == 1
+    decode = B.problem(64, 7168, 2048, 256, 8, 1, 1, 1)  # the decode layer fits
+    assert B.workspace_size(decode) <= B.NOALLOC_WORKSPACE_BYTES
+
+
 def test_ring_status_checks_arguments():
     # moe_ring_status validates like moe_ring_error_flag before it touches
     # the device: bad problem, NULL workspace, too small a workspace
