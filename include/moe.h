@@ -160,6 +160,21 @@ typedef struct {
      * MOE_ERR_INVALID_ARG) and the error flag is set; the output is then
      * meaningless. */
     int32_t ring_force_timeout;
+    /* moe_forward only: order in which each XCD's task queue hands out its
+     * tasks -- 0 as laid out, 1 reversed, 2 a fixed shuffle (other values:
+     * MOE_ERR_INVALID_ARG).  Every output element is written by one task, so
+     * the output does not depend on it (the work-conserving queue of the
+     * MegaMoE-vs-MoE-systems page, section 2.7, only decides who runs what). */
+    int32_t queue_order;
+    /* moe_forward only: NULL, or a device buffer of [2][task_log_capacity][4]
+     * uint32 receiving one record per task of the W1/W3 (row 0) and W2 (row 1)
+     * GEMM launches, at the task's index m_tile * n_tiles + n_tile: start time
+     * and duration on the 100 MHz chip-wide reference clock (low 32 bits),
+     * the workgroup that ran it, and 0x100 | the XCD it ran on.  Tasks with an
+     * index >= task_log_capacity are not recorded; entries of tasks that do
+     * not exist are left as they were. */
+    uint32_t *task_log;
+    int32_t task_log_capacity;
 } moe_debug;
 
 /* Human-readable name of a status code (static storage). */

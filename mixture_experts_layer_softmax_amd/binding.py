@@ -44,7 +44,9 @@ class MoEDebug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in DEBUG_BUFFERS] + [
         ("stage_events", ctypes.c_void_p * NUM_STAGE_EVENTS),
         ("gemm_clock", ctypes.c_void_p),
-        ("ring_poll_limit", ctypes.c_int32), ("ring_force_timeout", ctypes.c_int32)]
+        ("ring_poll_limit", ctypes.c_int32), ("ring_force_timeout", ctypes.c_int32),
+        ("queue_order", ctypes.c_int32), ("task_log", ctypes.c_void_p),
+        ("task_log_capacity", ctypes.c_int32)]
 
 
 class MoEError(RuntimeError):
@@ -217,6 +219,10 @@ def _debug_struct(dbg):
         dbg_s.gemm_clock = dbg["gemm_clock"].data_ptr()
     dbg_s.ring_poll_limit = int(dbg.get("ring_poll_limit", 0))
     dbg_s.ring_force_timeout = int(dbg.get("ring_force_timeout", 0))
+    dbg_s.queue_order = int(dbg.get("queue_order", 0))
+    if dbg.get("task_log") is not None:  # uint32 tensor [2][capacity][4]
+        dbg_s.task_log = dbg["task_log"].data_ptr()
+        dbg_s.task_log_capacity = int(dbg["task_log"].shape[1])
     return dbg_s
 
 

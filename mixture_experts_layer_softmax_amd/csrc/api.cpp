@@ -81,6 +81,11 @@ bool valid_problem(const moe_problem* p) {
 // Weight layouts the GEMM kernels read: [N][K] (packed) for every dtype.
 bool supported_layout(const moe_problem& p) { return p.w_layout == MOE_W_NK; }
 
+// Bytes per element of Y, the expert outputs per slot: fp32, except bf16 for
+// FP8 and MXFP4 weights (their 5e-2 tolerance leaves room for the rounding,
+// and Y is the largest buffer of those layers).
+int y_bytes(const moe_problem& p) { return quantised_weights(p.w_dtype) ? 2 : 4; }
+
 // Expert rows of the grouped GEMMs: the T*k routed slots, then T per shared
 // expert.
 int64_t gemm_rows(const moe_problem& p) { return p.T * (p.top_k + p.n_shared); }
@@ -153,7 +158,7 @@ Layout make_layout(const moe_problem& p, bool ring = false) {
                esize(p.act_dtype));
   else
     L.h = take(static_cast<size_t>(rows) * p.f * (fp8 || mx ? 1 : esize(p.act_dtype)));
-  L.y = take(sizeof(float) * rows * p.d);
+  L.y = take(static_cast<size_t>(y_bytes(p)) * rows * p.d);
   L.ring_ctrl = take(ring ? sizeof(int32_t) * ring_ctrl_words(L.max_mtiles) : 0);
   L.total = off;
   return L;
@@ -341,6 +346,9 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   if (!valid_problem(p)) return MOE_ERR_INVALID_ARG;
   if (!supported_shape(p) || !supported_layout(*p)) return MOE_ERR_UNSUPPORTED;
   if (ring && !ring_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  if (dbg && (dbg->queue_order < 0 || dbg->queue_order > 2 || dbg->task_log_capacity < 0 ||
+              (dbg->task_log && dbg->task_log_capacity == 0)))
+    return MOE_ERR_INVALID_ARG;
   if (ring && dbg) {
     if (dbg->ring_poll_limit < 0) return MOE_ERR_INVALID_ARG;
     if (dbg->ring_force_timeout &&
@@ -415,6 +423,9 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g1.queue_idx = 0;
   g1.group_m = group_m(*p, L.bm);
   g1.clock = dbg ? dbg->gemm_clock : nullptr;
+  g1.queue_order = dbg ? dbg->queue_order : 0;
+  g1.task_log = dbg ? dbg->task_log : nullptr;
+  g1.task_log_capacity = dbg ? dbg->task_log_capacity : 0;
   if (!ring) {
     st = from_code(moe::launch_gemm(1, gdt, L.bm, g1, stream));
     if (st != MOE_OK) return st;
@@ -443,8 +454,11 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   // anyway: non-temporal stores keep it from displacing the operands cached
   // for the GEMMs (measured 1-3 % on W2 and the combine for Y of 0.8-7.5 GB;
   // for a 268 MB Y the combine lost what W2 gained)
-  g2.stream_c = static_cast<double>(gemm_rows(*p)) * p->d * 4 >= 512.0 * (1 << 20);
+  g2.stream_c = static_cast<double>(gemm_rows(*p)) * p->d * y_bytes(*p) >= 512.0 * (1 << 20);
   g2.clock = (dbg && dbg->gemm_clock) ? dbg->gemm_clock + 2 : nullptr;
+  g2.queue_order = g1.queue_order;
+  g2.task_log = g1.task_log ? g1.task_log + 4ll * g1.task_log_capacity : nullptr;
+  g2.task_log_capacity = g1.task_log_capacity;
   if (!ring) {
     st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));
     if (st != MOE_OK) return st;
@@ -463,6 +477,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
     g1.C = r.h;
     g2.A = r.h;
     g1.clock = g2.clock = nullptr;
+    g1.task_log = g2.task_log = nullptr;  // (the ring kernel keeps no task log)
+    g1.queue_order = g2.queue_order = 0;
     moe::launch_zero(ctrl, ring_ctrl_words(L.max_mtiles), stream);
     st = from_code(moe::launch_gemm_ring(g1, g2, r, stream));
     if (st != MOE_OK) return st;
@@ -471,8 +487,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   mark(5);
 
   // 6. combine
-  moe::launch_combine(at<float>(ws, L.y), w, token_slot, out, T, d, k, p->n_shared,
-                      p->out_dtype == MOE_BF16, stream);
+  moe::launch_combine(at<uint8_t>(ws, L.y), y_bytes(*p) == 2, w, token_slot, out, T, d, k,
+                      p->n_shared, p->out_dtype == MOE_BF16, stream);
   mark(6);
 
   if (dbg) {

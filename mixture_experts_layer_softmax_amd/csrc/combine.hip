@@ -27,8 +27,10 @@ namespace {
 // CU; the accumulation itself stays j ascending, then the shared experts.
 constexpr int kCombineGroup = 8;
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ Y,
+// Y rows are fp32, or bf16 (Y_BF16: FP8 and MXFP4 layers); either way every
+// term is widened to fp32 before its fma.
+template <bool OUT_BF16, bool Y_BF16>
+__global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ Yv,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ token_slot,
                                                       void* __restrict__ out, int T, int d, int k,
@@ -55,9 +57,21 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
 #pragma unroll
       for (int u = 0; u < kCombineGroup; ++u) {
         if (j0 + u < n) {
-          const float* row = Y + static_cast<size_t>(s_slot[j0 + u]) * d + c;
-          y0[u] = *reinterpret_cast<const f32x4*>(row);
-          y1[u] = *reinterpret_cast<const f32x4*>(row + 4);
+          const size_t o = static_cast<size_t>(s_slot[j0 + u]) * d + c;
+          if constexpr (Y_BF16) {
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Yv) + o);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              y0[u][2 * q] = __uint_as_float(raw[q] << 16);
+              y0[u][2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
+              y1[u][2 * q] = __uint_as_float(raw[2 + q] << 16);
+              y1[u][2 * q + 1] = __uint_as_float(raw[2 + q] & 0xffff0000u);
+            }
+          } else {
+            const float* row = static_cast<const float*>(Yv) + o;
+            y0[u] = *reinterpret_cast<const f32x4*>(row);
+            y1[u] = *reinterpret_cast<const f32x4*>(row + 4);
+          }
         }
       }
 #pragma unroll
@@ -99,14 +113,18 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
 
 }  // namespace
 
-void launch_combine(const float* Y, const float* w, const int32_t* token_slot, void* out,
-                    int T, int d, int k, int S, bool out_bf16, hipStream_t s) {
+void launch_combine(const void* Y, bool y_bf16, const float* w, const int32_t* token_slot,
+                    void* out, int T, int d, int k, int S, bool out_bf16, hipStream_t s) {
   if (T <= 0) return;
   const int threads = std::min(1024, std::max(64, (d / 8 + 63) / 64 * 64));
-  if (out_bf16)
-    combine_kernel<true><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
+  if (out_bf16 && y_bf16)
+    combine_kernel<true, true><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
+  else if (out_bf16)
+    combine_kernel<true, false><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
+  else if (y_bf16)
+    combine_kernel<false, true><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
   else
-    combine_kernel<false><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
+    combine_kernel<false, false><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
 }
 
 }  // namespace moe

@@ -89,8 +89,11 @@ struct Geo {
   // streams better than one of 8 (one refills while the other starts a task)
   static constexpr int NS_CAP = BM <= 32 ? ((MX && BM == 16) ? 4 : 8) : 6;
   static constexpr int NS = NS0 > NS_CAP ? NS_CAP : NS0;
+  // phase-2 output element: Y is fp32 for fp32 and bf16 weights, bf16 (RNE)
+  // for FP8 and MXFP4 weights, whose 5e-2 tolerance absorbs the rounding
+  static constexpr int YES = (DT == kFP8 || DT == kMX4) ? 2 : 4;
   static constexpr int EPI =  // output staging, one pass per wave row
-      (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : 4);
+      (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : YES);
   static constexpr int RING = NS * STAGE;
   static constexpr int LDS = (RING > EPI ? RING : EPI) + RED;
   static_assert(NS >= 2, "at least two LDS stages");
@@ -135,6 +138,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef MOE_W
 }
 
+// s_waitcnt lgkmcnt(0): every LDS read of this wave has returned (vmcnt
+// and expcnt fields at their maxima, so they do not wait).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Direct global -> LDS loads; the LDS pointer must be wave-uniform.
 __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
@@ -161,6 +170,14 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// ring_barrier that the instruction scheduler also may not move any
+// instruction across (the ping-pong phases must stay whole).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  ring_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 constexpr int kXcd = 8;  // XCDs (L2 domains) of the chip
 
 // Per-XCD task queues of one grouped GEMM (see the kernel).  Task ids are
@@ -169,14 +186,22 @@ constexpr int kXcd = 8;  // XCDs (L2 domains) of the chip
 struct TaskQueue {
   int* counters;  // [kXcd] integer pull counters, zeroed by the scan kernel
   int M, NT, GM, nchunks, xcd;
+  int order;      // 0 as laid out; 1 each queue reversed; 2 each queue shuffled
 
   __device__ int limit(int y) const {
     const int owned = nchunks > y ? (nchunks - y + kXcd - 1) / kXcd : 0;
     return owned * GM * NT;
   }
   // task of pull number v of queue y, or -1 (the last chunk may hold fewer
-  // than GM m-tiles)
+  // than GM m-tiles).  A debug order first maps v through a bijection of
+  // [0, limit(y)): reversal, or v -> (v * P + 12345) mod limit with P a prime
+  // above any limit (so coprime to it).
   __device__ int decode(int v, int y) const {
+    if (order != 0) {
+      const int lim = limit(y);
+      v = order == 1 ? lim - 1 - v
+                     : static_cast<int>((static_cast<int64_t>(v) * 2147483629ll + 12345) % lim);
+    }
     const int per_chunk = GM * NT;
     const int p = v % per_chunk;
     const int mt = (y + kXcd * (v / per_chunk)) * GM + p % GM;
@@ -205,7 +230,7 @@ struct TaskQueue {
 // map) times column tile nt -- the K loop through the LDS ring, then the
 // epilogue.  kpull() runs a few k-steps before the end (the next task's
 // queue request); pre_epi() runs between the main loop and the epilogue.
-template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, class KPull,
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, int SCHED, class KPull,
           class PreEpi>
 __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const int nt,
                                           const int64_t arow_base, const int64_t crow_base,
@@ -395,6 +420,139 @@ do {                                                                            
   for (int p = 0; p < NS - 1; ++p)
     if (p < ksteps) MOE_ISSUE(p);
 
+  if constexpr (SCHED == 2) {
+    // Interleaved DMA: each k-step of a stage reads its fragments, then runs
+    // its MFMAs with one DMA instruction of the next stage between every
+    // few of them (the activation rows' DMAs with the first k-step, the
+    // weight rows' with the second).  Issued as one block, a wave's DMA
+    // instructions stall its in-order issue until the memory pipeline
+    // accepts them, which delays its MFMAs; spread out, they drain behind
+    // the MFMAs.  Measured in isolation on a 256 x 256 stage fed from L2:
+    // 3022 instead of 3437 clocks per stage (the MFMAs alone: 2075).
+    static_assert(DT == kBF16 && KRB == 128, "interleaved DMA: bf16, two k-steps per stage");
+    constexpr int MA = (TM * TN + G::AW - 1) / G::AW;  // MFMAs after each activation DMA
+    constexpr int MB = (TM * TN + G::BW - 1) / G::BW;  // and after each weight DMA
+    const bool compute = wm * WTM < rows;
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const int ahead = min(NS - 2, ksteps - 1 - ks);
+      wait_vmcnt(ahead * my_loads);
+      ring_barrier();
+      if (ks == k_pull) kpull();
+      const bool refill = ks + NS - 1 < ksteps;
+      const int kn = ks + NS - 1;
+      uint8_t* st_n = lds + (kn % NS) * G::STAGE;
+      const uint32_t ko_n = static_cast<uint32_t>(kn) * KRB;
+      const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
+      const uint8_t* Bb = Ab + BM * KRB;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 wf[TN], xf[TM];
+        if (compute) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            wf[j] = *reinterpret_cast<const bf16x8*>(
+                Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            xf[i] = *reinterpret_cast<const bf16x8*>(
+                Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));
+        }
+        constexpr int ND = 4;  // DMA slots of this k-step (A: AW, B: BW, at most 4 each)
+        static_assert(G::AW <= ND && G::BW <= ND, "DMA slots per k-step");
+        const int MPD = (kk == 0) ? MA : MB;  // (kk is unrolled: a constant)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < ND; ++u) {
+          if (kk == 0) {
+            const int q = wave + NW * u;
+            if (refill && u < G::AW && (G::ABLK % NW == 0 || q < G::ABLK))
+              dma16(g.A + (oa[u] + ko_n), st_n + q * 1024);
+          } else {
+            const int q = wave + NW * u;
+            if (refill && u < G::BW && (G::BBLK % NW == 0 || q < G::BBLK))
+              dma16(((up_mask >> u) & 1u ? b1 : b0) + (ob[u] + static_cast<uint32_t>(kn) * KRBW),
+                    st_n + BM * KRB + q * 1024);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (compute) {
+#pragma unroll
+            for (int m = u * MPD; m < (u + 1) * MPD && m < TM * TN; ++m) {
+              const int i = m / TN, j = m % TN;
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  } else if constexpr (SCHED == 1) {
+    // Ping-pong schedule: the two waves of each SIMD (wave row wm = 0 and
+    // wm = 1) run half a stage apart.  While one runs the stage's 64 MFMAs
+    // from registers at raised priority, the other reads its fragments of
+    // the next stage from LDS and issues its share of the DMA, so the matrix
+    // core of every SIMD always has one wave with a dense MFMA cluster; the
+    // barrier between two phases is where the waves trade roles.  Group 1
+    // starts one barrier late and group 0 finishes one barrier late, so
+    // both pass the same number of barriers.
+    //   barrier 2s:   stage s is in LDS (both groups waited for their own
+    //                 loads of it); group 0 reads it, group 1 runs stage s-1
+    //   barrier 2s+1: group 0 runs stage s, group 1 reads it
+    // Stage s+1 goes into the slot of stage s-1, which both groups finished
+    // reading by barrier 2s; each group issues its share of it in the phase
+    // after barrier 2s (group 0 before its reads, group 1 before its
+    // MFMAs) and waits for it before barrier 2s+2.
+    static_assert(DT == kBF16 && NS == 2 && WM == 2 && KRB == 128,
+                  "ping-pong: bf16, two stages, two wave rows");
+    const bool late = wm == 1;
+    const bool compute = wm * WTM < rows;
+    wait_vmcnt(0);
+    phase_barrier();  // stage 0 is in LDS
+    if (late) {
+      if (1 < ksteps) MOE_ISSUE(1);
+      phase_barrier();
+    }
+    bf16x8 xf[2][TM], wf[2][TN];
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const uint8_t* Ab = lds + (ks & 1) * G::STAGE;
+      const uint8_t* Bb = Ab + BM * KRB;
+      // ---- load phase: this wave's fragments of stage ks ----
+      if (!late && ks + 1 < ksteps) MOE_ISSUE(ks + 1);
+      if (ks == k_pull) kpull();
+      if (compute) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            wf[kk][j] = *reinterpret_cast<const bf16x8*>(
+                Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            xf[kk][i] = *reinterpret_cast<const bf16x8*>(
+                Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));
+        }
+      }
+      if (late) wait_vmcnt(0);  // own share of stage ks + 1 has landed
+      wait_lgkmcnt0();          // fragments in registers before the slot is refilled
+      phase_barrier();
+      // ---- compute phase: the 64 MFMAs of stage ks ----
+      if (late && ks + 2 < ksteps) MOE_ISSUE(ks + 2);
+      if (compute) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[kk][j], xf[kk][i], acc[i][j],
+                                                                   0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if (!late) wait_vmcnt(0);  // own share of stage ks + 1 has landed
+      phase_barrier();
+    }
+    if (!late) phase_barrier();
+  } else
   for (int ks = 0; ks < ksteps; ++ks) {
     // my loads of stage ks have landed once at most `ahead` later stages
     // are still in flight; the barrier then publishes everyone's loads and
@@ -589,7 +747,7 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
   // keep the fragment writes off a single bank group.
   {
     constexpr int OUT_COLS = (PHASE == 1) ? BN / 2 : BN;
-    constexpr int OUT_ES = (PHASE == 1) ? ES : 4;
+    constexpr int OUT_ES = (PHASE == 1) ? ES : G::YES;
     constexpr int ROWB = OUT_COLS * OUT_ES;
     constexpr int CPR = ROWB / 16;
     constexpr int XM = (CPR >= 16 ? 16 : CPR) - 1;
@@ -628,11 +786,21 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
         for (int i = 0; i < TM; ++i) {
           const int lr = wm * WTM + 16 * i + l16;  // row within the tile
           const int r = lr - pass * PROWS;          // row within this pass
-          if constexpr (PHASE == 2) {
+          if constexpr (PHASE == 2 && G::YES == 4) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
               *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
                   acc[i][j];
+          } else if constexpr (PHASE == 2) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              u32x2 v;
+              v.x = f32_to_bf16_rne(acc[i][j][0]) |
+                    (static_cast<uint32_t>(f32_to_bf16_rne(acc[i][j][1])) << 16);
+              v.y = f32_to_bf16_rne(acc[i][j][2]) |
+                    (static_cast<uint32_t>(f32_to_bf16_rne(acc[i][j][3])) << 16);
+              *reinterpret_cast<u32x2*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 2)) = v;
+            }
           } else if constexpr (MX) {
             // h = SiLU(gate) * up; each block of 32 h columns (two 16-column
             // fragments, held by the four lanes of this row) gets its MX FP8
@@ -724,7 +892,7 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
 
 }
 
-template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_>
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, int SCHED>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   using G = Geo<DT, PHASE, BM, BN, WM, WN, KRB_>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -749,7 +917,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
                     (*g.tm.n_mtiles + g.group_m - 1) / g.group_m,
                     // s_getreg_b32 hwreg(HW_REG_XCC_ID, 0, 4): id of this XCD
                     static_cast<int>(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) &
-                                     (kXcd - 1))};
+                                     (kXcd - 1)),
+                    g.queue_order};
   const int NT = q.NT;
   const int own_limit = q.limit(q.xcd);
   bool own_open = true;  // (thread 0) the own XCD queue may still hold tasks
@@ -767,7 +936,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     int next_v = -1;
     const int mt = task / NT;
     const int nt = task - mt * NT;
-    gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_>(
+    const uint64_t t_start = g.task_log ? __builtin_amdgcn_s_memrealtime() : 0;
+    gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_, SCHED>(
         g, mt, nt, -1, -1,
         [&] {
           if (tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
@@ -778,6 +948,16 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     // LDS reads from the hand-over slot write and from the next task's
     // first DMA writes
     __syncthreads();
+    if (tid == 0 && g.task_log && task < g.task_log_capacity) {
+      // debug record of this task: start and end on the 100 MHz chip-wide
+      // reference clock, the workgroup and the XCD that ran it
+      const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+      uint32_t* r = g.task_log + 4ll * task;
+      r[0] = static_cast<uint32_t>(t_start);
+      r[1] = static_cast<uint32_t>(t_end - t_start);
+      r[2] = blockIdx.x;
+      r[3] = static_cast<uint32_t>(q.xcd) | 0x100u;
+    }
     if (tid == 0) {
       int t = -1;
       if (next_v >= 0) {
@@ -905,7 +1085,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
           __syncthreads();
         }
       };
-      gemm_task<kBF16, 1, BM, BN, WM, WN, 128>(g1, mt, nt, -1, ring_row, kpull, slot_free);
+      gemm_task<kBF16, 1, BM, BN, WM, WN, 128, 0>(g1, mt, nt, -1, ring_row, kpull, slot_free);
       wait_vmcnt(0);  // this wave's h stores are done
       __syncthreads();
       if (tid == 0)
@@ -916,7 +1096,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
         ring_wait(&r.l1_done[c], min(GM, M - c * GM) * NT1 + r.unreachable, true, r.err,
                   r.poll_limit);
       __syncthreads();
-      gemm_task<kBF16, 2, BM, BN, WM, WN, 128>(g2, mt, nt, ring_row, -1, kpull, [] {});
+      gemm_task<kBF16, 2, BM, BN, WM, WN, 128, 0>(g2, mt, nt, ring_row, -1, kpull, [] {});
       __syncthreads();  // (the task's h loads all landed before its last stage)
       if (tid == 0) __hip_atomic_fetch_add(&r.l2_done[c], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -939,12 +1119,13 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
   }
 }
 
-template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB = (DT == kF32 ? 64 : 128)>
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB = (DT == kF32 ? 64 : 128),
+          int SCHED = 0>
 struct Variant {
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int lds_bytes() { return Geo<DT, PHASE, BM, BN, WM, WN, KRB>::LDS; }
   static int launch(const GemmArgs& a, hipStream_t s) {
-    auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN, KRB>;
+    auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN, KRB, SCHED>;
     static int grid = 0;
     static hipError_t attr_err = hipSuccess;
     static std::once_flag once;
@@ -982,6 +1163,13 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
     return f(Variant<DT, P, BM_, BN_, WM_, WN_ __VA_OPT__(, ) __VA_ARGS__>{});
   MOE_V(kBF16, 1, 256, 0, 256, 2, 4)
   MOE_V(kBF16, 2, 256, 0, 256, 2, 4)
+  // measured alternatives of the 256 x 256 schedule (both slower on the
+  // prefill and skewed layers): 3 = DMA interleaved with the MFMAs,
+  // 4 = ping-pong of the two waves of each SIMD
+  MOE_V(kBF16, 1, 256, 3, 256, 2, 4, 128, 2)
+  MOE_V(kBF16, 2, 256, 3, 256, 2, 4, 128, 2)
+  MOE_V(kBF16, 1, 256, 4, 256, 2, 4, 128, 1)
+  MOE_V(kBF16, 2, 256, 4, 256, 2, 4, 128, 1)
   MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 2, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 1, 128, 1, 256, 1, 4)

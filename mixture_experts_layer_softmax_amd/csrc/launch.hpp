@@ -49,7 +49,8 @@ struct GemmArgs {
   int64_t K;              // contraction length (elements)
   int64_t N;              // output columns: f (phase 1) or d (phase 2)
   // outputs
-  uint8_t* C;             // h [slots][f] (phase 1) or Y fp32 [slots][d] (phase 2)
+  uint8_t* C;             // h [slots][f] (phase 1) or Y [slots][d] (phase 2: fp32, or
+                          // bf16 for FP8 and MXFP4 weights)
   float* sc;              // phase 1 h scales: FP8 [slots][f/128]; MX E8M0 bytes [slots][f/32]
   TileMap tm;
   int n_tiles_n;          // column tiles per m-tile
@@ -57,6 +58,9 @@ struct GemmArgs {
   int group_m;            // m-tiles per XCD work chunk (1..8)
   int stream_c;           // phase 2: store Y with non-temporal hints (Y far beyond the MALL)
   uint64_t* clock;        // [2] or null: ticks of workgroup 0 (shader, 100 MHz reference)
+  int queue_order;        // debug: 0 as laid out, 1 reversed, 2 shuffled task order
+  uint32_t* task_log;     // debug: [task_log_capacity][4] per-task records, or null
+  int task_log_capacity;
 };
 
 // Single-launch W1/W3 -> W2 pipeline (bf16, 256 x 256 tiles) through a
@@ -110,8 +114,9 @@ int launch_gemm_ring(const GemmArgs& g1, const GemmArgs& g2, const RingArgs& r, 
 void launch_zero(int32_t* p, int64_t n, hipStream_t s);
 // Column tiles per m-tile for a phase (depends on the kernel variant).
 int gemm_tile_n(int phase, int dtype, int bm);
-void launch_combine(const float* Y, const float* w, const int32_t* token_slot, void* out,
-                    int T, int d, int k, int S, bool out_bf16, hipStream_t s);
+// Y [T*k + S*T][d], fp32 or (y_bf16) bf16.
+void launch_combine(const void* Y, bool y_bf16, const float* w, const int32_t* token_slot,
+                    void* out, int T, int d, int k, int S, bool out_bf16, hipStream_t s);
 void launch_pack(int E, int64_t K, int64_t N, int elem_bytes, const void* src, void* dst,
                  hipStream_t s);
 

@@ -79,6 +79,21 @@ def test_noalloc_size_limit_is_checked_before_launch():
     assert B.workspace_size(decode) <= B.NOALLOC_WORKSPACE_BYTES
 
 
+def test_debug_fields_are_checked_before_launch():
+    # an unknown queue order, a negative task-log capacity or a task log
+    # without a capacity: MOE_ERR_INVALID_ARG before any pointer is used
+    lib = _lib()
+    p = B.problem(64, 128, 128, 8, 2, 1, 1, 1)
+    n = B.workspace_size(p)
+    fake = 1 << 40  # never dereferenced
+    for order, log, cap in ((3, None, 0), (-1, None, 0), (0, fake, 0), (0, None, -2)):
+        dbg = B.MoEDebug()
+        dbg.queue_order, dbg.task_log, dbg.task_log_capacity = order, log, cap
+        rc = lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, fake, fake, None, None,
+                             None, fake, fake, n, ctypes.byref(dbg), None)
+        assert rc == 1, (order, log, cap)
+
+
 def test_ring_status_checks_arguments():
     # moe_ring_status validates like moe_ring_error_flag before it touches
     # the device: bad problem, NULL workspace, too small a workspace
