@@ -86,6 +86,11 @@ bool supported_layout(const moe_problem& p) { return p.w_layout == MOE_W_NK; }
 // and Y is the largest buffer of those layers).
 int y_bytes(const moe_problem& p) { return quantised_weights(p.w_dtype) ? 2 : 4; }
 
+// Floats per row of the FP8 activation scales inside the workspace (x and
+// h: one per 128 elements): padded to a multiple of 4, so that the GEMM
+// fetches four stages' scales of a row with one 16-byte load.
+int64_t fp8_scale_stride(int64_t k) { return (k / 128 + 3) / 4 * 4; }
+
 // Expert rows of the grouped GEMMs: the T*k routed slots, then T per shared
 // expert.
 int64_t gemm_rows(const moe_problem& p) { return p.T * (p.top_k + p.n_shared); }
@@ -151,8 +156,8 @@ Layout make_layout(const moe_problem& p, bool ring = false) {
   const bool fp8 = p.w_dtype == MOE_FP8_E4M3, mx = p.w_dtype == MOE_MXFP4;
   // FP8: fp32 scales per 128 elements; MX: one E8M0 byte per 32 elements
   L.xq = take(fp8 || mx ? static_cast<size_t>(p.T) * p.d : 0);
-  L.sx = take(fp8 ? sizeof(float) * p.T * (p.d / 128) : (mx ? p.T * (p.d / 32) : 0));
-  L.hs = take(fp8 ? sizeof(float) * rows * (p.f / 128) : (mx ? rows * (p.f / 32) : 0));
+  L.sx = take(fp8 ? sizeof(float) * p.T * fp8_scale_stride(p.d) : (mx ? p.T * (p.d / 32) : 0));
+  L.hs = take(fp8 ? sizeof(float) * rows * fp8_scale_stride(p.f) : (mx ? rows * (p.f / 32) : 0));
   if (ring)  // h only for the chunks in flight: 8 XCDs x kRingSlots x group_m tiles
     L.h = take(static_cast<size_t>(8 * kRingSlots) * group_m(p, L.bm) * L.bm * p.f *
                esize(p.act_dtype));
@@ -295,7 +300,8 @@ moe_status moe_quantize_fp8(int64_t rows, int64_t cols, const void* x_bf16, uint
   if (rows == 0) return MOE_OK;
   if (!x_bf16 || !q || !s) return MOE_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  moe::launch_quant_fp8(static_cast<const uint16_t*>(x_bf16), rows, cols, q, s, stream);
+  moe::launch_quant_fp8(static_cast<const uint16_t*>(x_bf16), rows, cols, q, s, cols / 128,
+                        stream);
   return hip_status();
 }
 
@@ -392,7 +398,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   // 2. FP8 (or MX FP8) activations
   if (fp8)
     moe::launch_quant_fp8(static_cast<const uint16_t*>(x), p->T, p->d, at<uint8_t>(ws, L.xq),
-                          at<float>(ws, L.sx), stream);
+                          at<float>(ws, L.sx), fp8_scale_stride(p->d), stream);
   if (mx)
     moe::launch_quant_mx(static_cast<const uint16_t*>(x), p->T, p->d, at<uint8_t>(ws, L.xq),
                          at<uint8_t>(ws, L.sx), stream);
@@ -410,6 +416,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g1.a_row_bytes = p->d * (q8 ? 1 : esize(p->act_dtype));
   g1.gather = slot_token;
   g1.sa = q8 ? at<float>(ws, L.sx) : nullptr;  // (MX: E8M0 bytes)
+  g1.sa_stride = static_cast<int>(fp8_scale_stride(p->d));
   g1.B0 = static_cast<const uint8_t*>(W1t);
   g1.B1 = static_cast<const uint8_t*>(W3t);
   g1.sb0 = static_cast<const float*>(W1s);
@@ -418,6 +425,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g1.N = p->f;
   g1.C = at<uint8_t>(ws, L.h);
   g1.sc = q8 ? at<float>(ws, L.hs) : nullptr;
+  g1.sc_stride = static_cast<int>(fp8_scale_stride(p->f));
   g1.tm = tm;
   g1.n_tiles_n = static_cast<int>(ceil_div(2 * p->f, moe::gemm_tile_n(1, gdt, L.bm)));
   g1.queue_idx = 0;
@@ -438,6 +446,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g2.a_row_bytes = p->f * (q8 ? 1 : esize(p->act_dtype));
   g2.gather = nullptr;
   g2.sa = q8 ? at<float>(ws, L.hs) : nullptr;
+  g2.sa_stride = static_cast<int>(fp8_scale_stride(p->f));
   g2.B0 = static_cast<const uint8_t*>(W2t);
   g2.B1 = nullptr;
   g2.sb0 = static_cast<const float*>(W2s);

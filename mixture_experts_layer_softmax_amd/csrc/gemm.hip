@@ -80,10 +80,16 @@ struct Geo {
   static constexpr int SA_DMA = (DT == kFP8 || MX) ? (BM + 63) / 64 : 0;
   static constexpr int SB_DMA = MX ? (BN + 63) / 64 : 0;
   static constexpr int SCW = (SA_DMA + SB_DMA + NW - 1) / NW;  // scale DMAs per wave (MX)
-  static constexpr int SCALE_BYTES = (SA_DMA + SB_DMA) * 256;  // per stage
+  static constexpr int SCALE_BYTES = MX ? (SA_DMA + SB_DMA) * 256 : 0;  // per stage (MX)
   static constexpr int STAGE = BM * KRB + BN * KRBW + SCALE_BYTES;
   static constexpr int RED = (DT == kFP8 && PHASE == 1) ? WN * BM * 4 : 0;
-  static constexpr int NS0 = (kLdsBytes - RED) / STAGE;
+  // FP8 activation-row scales: one 16-byte DMA per row fetches the scales
+  // of four stages (a scale group) into a ring of three group buffers of
+  // SA_DMA * 64 rows, after the operand ring and the row maxima
+  static constexpr int SGROUP = 4;
+  static constexpr int SRING_BUFS = 3;
+  static constexpr int SRING = (DT == kFP8) ? SRING_BUFS * SA_DMA * 1024 : 0;
+  static constexpr int NS0 = (kLdsBytes - RED - SRING) / STAGE;
   // small tiles (decode: HBM bound) keep more stages in flight; 16-row MX
   // tiles are small enough that two workgroups of 4 stages share a CU, which
   // streams better than one of 8 (one refills while the other starts a task)
@@ -95,8 +101,12 @@ struct Geo {
   static constexpr int EPI =  // output staging, one pass per wave row
       (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : YES);
   static constexpr int RING = NS * STAGE;
-  static constexpr int LDS = (RING > EPI ? RING : EPI) + RED;
+  static constexpr int LDS = (RING > EPI ? RING : EPI) + RED + SRING;
   static_assert(NS >= 2, "at least two LDS stages");
+  // a scale group's buffer is refilled with the DMA of stage SGROUP * g,
+  // issued NS - 1 stages ahead; the group that used it last (three groups
+  // back) must have finished reading it by then
+  static_assert(DT != kFP8 || NS - 1 < SGROUP * (SRING_BUFS - 1) + 1, "scale ring depth");
   static_assert(LDS <= kLdsBytes, "LDS budget");
   static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMAW == 0, "whole DMA blocks");
 };
@@ -317,12 +327,16 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
     ob[j] = static_cast<uint32_t>(col * w_row + logical * 16);
     if (q < G::BBLK) ++my_loads;
   }
-  const float* sa_src = g.sa;  // FP8: this lane's A-row scale row
+  // FP8: this lane's A-row scale row (padded to sa_stride floats, a multiple
+  // of 4, so that a scale group is one aligned 16-byte piece), and the scale
+  // ring: group buffer b holds [SA_DMA * 64 rows][4 stages] floats
+  const float* sa_src = g.sa;
+  float* sring = reinterpret_cast<float*>(lds + (G::RING > G::EPI ? G::RING : G::EPI) + G::RED);
+  const bool scale_dma = DT == kFP8 && wave < G::SA_DMA;
   if constexpr (DT == kFP8) {
     const int rr = min(wave * 64 + lane, rows - 1);
     const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
-    sa_src = g.sa + src * kblocks;
-    if (wave < G::SA_DMA) ++my_loads;
+    sa_src = g.sa + src * g.sa_stride;
   }
   // MX: E8M0 scale dwords of this lane (4 blocks of 32 = one stage).
   // Scale DMA number c < SA_DMA covers activation rows 64c.. ([rows][K/32]
@@ -367,8 +381,9 @@ do {                                                                            
       const int q = wave + NW * j;                                                     \
       if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024); \
     }                                                                                  \
-    if (DT == kFP8 && wave < G::SA_DMA)                                                \
-      dma4(sa_src + (KS), st_ + BM * KRB + BN * KRBW + wave * 256);                    \
+    if (DT == kFP8 && scale_dma && (KS) % G::SGROUP == 0)                              \
+      dma16(sa_src + (KS), sring + ((KS) / G::SGROUP) % G::SRING_BUFS * (G::SA_DMA * 256) \
+                               + wave * 256);                                          \
   }                                                                                    \
   if (DO_B) {                                                                          \
     const uint32_t kw_ = static_cast<uint32_t>(KS) * KRBW;                             \
@@ -558,7 +573,13 @@ do {                                                                            
     // are still in flight; the barrier then publishes everyone's loads and
     // guarantees every wave is done with the slot reloaded below
     const int ahead = min(NS - 2, ksteps - 1 - ks);
-    wait_vmcnt(ahead * my_loads);
+    // (FP8: a scale-group DMA rides with the stages whose index is a
+    // multiple of SGROUP; count those among the stages still in flight)
+    const int groups_ahead =
+        (DT == kFP8 && scale_dma && ahead > 0)
+            ? (ks + ahead) / G::SGROUP - ks / G::SGROUP
+            : 0;
+    wait_vmcnt(ahead * my_loads + groups_ahead);
     ring_barrier();
     if (ks == k_pull) kpull();
     // bf16 stages hold two MFMA k-steps: the weight rows of the next stage
@@ -670,67 +691,53 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
         const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
         wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      const float* sa_st = reinterpret_cast<const float*>(Sb);
+      // this stage's column of the scale group buffer: [row][4 stages]
+      const float* sa_st = sring + (ks / G::SGROUP) % G::SRING_BUFS * (G::SA_DMA * 256) +
+                           ks % G::SGROUP;
       const float s_b0 = sb_cur0, s_b1 = sb_cur1;
-      if constexpr (PHASE == 1) {
-        // Row by row: the TN block products of row i are issued before the
-        // scaled accumulation of row i-1, so the fp32 fmas overlap MFMAs.
-        f32x4 pp[TN];
-        float spg = 0.f, spu = 0.f;
+      // Software pipeline over the TM fragment rows: row i + 1's activation
+      // fragment and row scale are read from LDS while row i's TN block
+      // products run on the MFMA, and row i - 1's products are scaled
+      // (s_x * s_w, fp32) into the accumulators behind them, so neither the
+      // LDS latency nor the MFMA result latency stalls the wave.
+      i32x8 xf[2];
+      float sa[2];
+      auto load_row = [&](int i, i32x8& x, float& s_x) {
+        const int r = wm * WTM + 16 * i + l16;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
+        x = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        s_x = sa_st[4 * r];
+      };
+      load_row(0, xf[0], sa[0]);
+      f32x4 pp[TN];
+      float spg = 0.f, spu = 0.f;
 #pragma unroll
-        for (int i = 0; i <= TM; ++i) {
-          f32x4 pc[TN];
-          float scg = 0.f, scu = 0.f;
-          if (i < TM) {
-            const int r = wm * WTM + 16 * i + l16;
-            const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
-            const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
-            const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const float s_a = sa_st[r];
-            scg = s_a * s_b0;
-            scu = s_a * s_b1;
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-          }
-          if (i > 0) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const float sc = (PHASE == 1 && (j & 1)) ? spu : spg;
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                acc[i - 1][j][q] = __builtin_fmaf(pp[j][q], sc, acc[i - 1][j][q]);
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < TN; ++j) pp[j] = pc[j];
-          spg = scg;
-          spu = scu;
-        }
-      } else {  // (measured: the lagged form loses here, to register pressure)
-        // per row of fragments: the TN block products first (independent
-        // MFMAs in flight), then their scaled accumulation
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = wm * WTM + 16 * i + l16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + swz<KRB>(r, 2 * lg + 1));
-          const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const float s_a = sa_st[r];
-          const float sg = s_a * s_b0, su = s_a * s_b1;
-          f32x4 p[TN];
+      for (int i = 0; i <= TM; ++i) {
+        f32x4 pc[TN];
+        float scg = 0.f, scu = 0.f;
+        if (i + 1 < TM) load_row(i + 1, xf[(i + 1) & 1], sa[(i + 1) & 1]);
+        if (i < TM) {
+          scg = sa[i & 1] * s_b0;
+          scu = sa[i & 1] * s_b1;
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                wf[j], xf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wf[j], xf[i & 1], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        }
+        if (i > 0) {
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const float sc = (PHASE == 1 && (j & 1)) ? su : sg;
+            const float sc = (PHASE == 1 && (j & 1)) ? spu : spg;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(p[j][q], sc, acc[i][j][q]);
+            for (int q = 0; q < 4; ++q)
+              acc[i - 1][j][q] = __builtin_fmaf(pp[j][q], sc, acc[i - 1][j][q]);
           }
         }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) pp[j] = pc[j];
+        spg = scg;
+        spu = scu;
       }
     }
   }
@@ -850,7 +857,7 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
                   packed;
             }
             if (wn == 0 && lg == 0 && lr < rows)
-              g.sc[static_cast<int64_t>(row0 + lr) * (N / 128) + n0 / 256] = sc;
+              g.sc[static_cast<int64_t>(row0 + lr) * g.sc_stride + n0 / 256] = sc;
           } else {
 #pragma unroll
             for (int p = 0; p < TN / 2; ++p) {

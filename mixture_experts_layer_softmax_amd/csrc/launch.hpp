@@ -40,7 +40,9 @@ struct GemmArgs {
   const uint8_t* A;
   int64_t a_row_bytes;
   const int32_t* gather;  // row index table (slot -> token), or null (row = slot)
-  const float* sa;        // FP8: [rows][K/128] scales of A rows; MX: E8M0 bytes [rows][K/32]
+  const float* sa;        // FP8: [rows][sa_stride] scales of A rows (K/128 used); MX: E8M0
+                          // bytes [rows][K/32]
+  int sa_stride;          // FP8: floats per A-row scale row, a multiple of 4
   // weight operand(s): [E][N][K] (contraction axis contiguous)
   const uint8_t* B0;      // W1t (phase 1) or W2t (phase 2)
   const uint8_t* B1;      // W3t (phase 1)
@@ -51,7 +53,8 @@ struct GemmArgs {
   // outputs
   uint8_t* C;             // h [slots][f] (phase 1) or Y [slots][d] (phase 2: fp32, or
                           // bf16 for FP8 and MXFP4 weights)
-  float* sc;              // phase 1 h scales: FP8 [slots][f/128]; MX E8M0 bytes [slots][f/32]
+  float* sc;              // phase 1 h scales: FP8 [slots][sc_stride]; MX E8M0 bytes [slots][f/32]
+  int sc_stride;          // FP8: floats per h scale row, a multiple of 4
   TileMap tm;
   int n_tiles_n;          // column tiles per m-tile
   int queue_idx;
@@ -100,8 +103,9 @@ int launch_gate(const void* x, const void* gate_w, const float* bias, float* log
 void launch_permute(const int32_t* ids, int T, int k, int E, int S, int bm, int32_t* table,
                     int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_k,
                     int32_t* token_slot, TileMap tm, hipStream_t s);
+// s has s_stride floats per row (cols/128 of them written).
 void launch_quant_fp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
-                      hipStream_t st);
+                      int64_t s_stride, hipStream_t st);
 // MX FP8: blocks of 32 along the row, E4M3 codes + E8M0 scale bytes [rows][cols/32].
 void launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
                      hipStream_t st);

@@ -16,7 +16,8 @@ namespace {
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x,
                                                         int64_t rows, int64_t cols,
                                                         uint8_t* __restrict__ q,
-                                                        float* __restrict__ s) {
+                                                        float* __restrict__ s,
+                                                        int64_t s_stride) {
   const int64_t groups_per_row = cols / 128;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < 4; ++i) out.y |= f32_to_e4m3(__fdiv_rn(v[4 + i], sc)) << (8 * i);
   *reinterpret_cast<uint2*>(q + base) = out;
-  if (sub == 0) s[row * groups_per_row + grp] = sc;
+  if (sub == 0) s[row * s_stride + grp] = sc;
 }
 
 // OCP MX FP8 of the bf16 activations: blocks of 32 consecutive elements of a
@@ -105,11 +106,12 @@ void launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, 
 }
 
 void launch_quant_fp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
-                      hipStream_t st) {
+                      int64_t s_stride, hipStream_t st) {
   const int64_t groups = rows * (cols / 128);
   if (groups <= 0) return;
   const int64_t blocks = (groups + 15) / 16;
-  quant_fp8_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, st>>>(x, rows, cols, q, s);
+  quant_fp8_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, st>>>(x, rows, cols, q, s,
+                                                                        s_stride);
 }
 
 }  // namespace moe
