@@ -175,6 +175,12 @@ typedef struct {
      * not exist are left as they were. */
     uint32_t *task_log;
     int32_t task_log_capacity;
+    /* moe_forward on FP8 and MXFP4 layers: NULL, or device buffers receiving
+     * the activation codes and scales the expert GEMMs read, as the gate
+     * wrote them: x_codes [T][d] E4M3 codes; x_scales FP8: [T][d/128] fp32,
+     * MXFP4: [T][d/32] E8M0 bytes.  Ignored on other layers. */
+    uint8_t *x_codes;
+    void *x_scales;
 } moe_debug;
 
 /* Human-readable name of a status code (static storage). */

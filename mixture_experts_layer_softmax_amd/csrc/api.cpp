@@ -390,19 +390,15 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   };
   (void)hipGetLastError();
   mark(0);
-  // 1. gate
-  moe_status st = from_code(moe::launch_gate(x, gate_w, bias, logits, ids, w, T, d, E, k,
-                                             p->act_dtype == MOE_BF16, stream));
+  // 1. gate; on FP8 and MXFP4 layers it also quantises x (FP8 per 1x128
+  // group, or MX FP8 per 32) in the same pass over x
+  moe_status st = from_code(moe::launch_gate(
+      x, gate_w, bias, logits, ids, w, T, d, E, k, p->act_dtype == MOE_BF16, stream,
+      fp8 ? 1 : (mx ? 2 : 0), q8 ? at<uint8_t>(ws, L.xq) : nullptr,
+      q8 ? at<void>(ws, L.sx) : nullptr, fp8_scale_stride(p->d)));
   if (st != MOE_OK) return st;
   mark(1);
-  // 2. FP8 (or MX FP8) activations
-  if (fp8)
-    moe::launch_quant_fp8(static_cast<const uint16_t*>(x), p->T, p->d, at<uint8_t>(ws, L.xq),
-                          at<float>(ws, L.sx), fp8_scale_stride(p->d), stream);
-  if (mx)
-    moe::launch_quant_mx(static_cast<const uint16_t*>(x), p->T, p->d, at<uint8_t>(ws, L.xq),
-                         at<uint8_t>(ws, L.sx), stream);
-  mark(2);
+  mark(2);  // (stage 2, the activation quantisation, is inside the gate)
   // 3. histogram, scan + tile map, scatter
   moe::launch_permute(ids, T, k, E, p->n_shared, L.bm, at<int32_t>(ws, L.table), counts,
                       offsets, slot_token, slot_k, token_slot, tm, stream);
@@ -511,6 +507,15 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
     cp(dbg->slot_token, slot_token, sizeof(int32_t) * n);
     cp(dbg->slot_k, slot_k, sizeof(int32_t) * n);
     cp(dbg->token_slot, token_slot, sizeof(int32_t) * n);
+    if (q8) {
+      cp(dbg->x_codes, at<uint8_t>(ws, L.xq), static_cast<size_t>(p->T) * p->d);
+      if (dbg->x_scales && fp8)  // drop the row padding of the workspace copy
+        (void)hipMemcpy2DAsync(dbg->x_scales, sizeof(float) * (p->d / 128), at<float>(ws, L.sx),
+                               sizeof(float) * fp8_scale_stride(p->d),
+                               sizeof(float) * (p->d / 128), p->T, hipMemcpyDeviceToDevice,
+                               stream);
+      if (mx) cp(dbg->x_scales, at<uint8_t>(ws, L.sx), static_cast<size_t>(p->T) * (p->d / 32));
+    }
   }
   return hip_status();
 }

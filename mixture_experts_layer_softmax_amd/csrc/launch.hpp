@@ -94,9 +94,12 @@ constexpr int kRingPollLimit = 1 << 22;
 constexpr int kRingForcedPollMax = 4096;
 
 // Gate: logits [T][E] (+ bias), top-k ids and renormalised weights [T][k].
-// Returns a hipError_t.
+// quant 1 / 2 also writes x (bf16) quantised to FP8 1x128 groups (codes xq
+// [T][d], fp32 scales xs [T][xs_stride]) or to MX FP8 blocks of 32 (codes xq,
+// E8M0 bytes xs [T][d/32]) in the same pass.  Returns a hipError_t.
 int launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
-                 int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s);
+                int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s,
+                int quant = 0, uint8_t* xq = nullptr, void* xs = nullptr, int64_t xs_stride = 0);
 // S shared experts add T slots each after the T*k routed ones (slot
 // T*k + s*T + t holds token t, k-slot k + s) and their m-tiles after the
 // routed ones.

@@ -213,14 +213,25 @@ struct GateLds {
   static constexpr int BUF = 16 * TG * LDR + KB * WE;  // floats per buffer
 };
 
-template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE>
+// Activation quantisation fused into the gate's pass over x (QUANT 1: FP8
+// E4M3 per 1x128 group with an fp32 scale amax / 448; QUANT 2: OCP MX FP8,
+// E4M3 with an E8M0 scale per block of 32), the activation format of the FP8
+// and MXFP4 expert GEMMs: the SFA load role of the MegaMoE-vs-MoE-systems
+// page, section 2.1, fed without a second read of x.
+struct GateQuant {
+  uint8_t* q;         // [T][d] codes
+  void* s;            // FP8: fp32 [T][s_stride]; MX: E8M0 bytes [T][d / 32]
+  int64_t s_stride;   // FP8: floats per scale row
+};
+
+template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE, int QUANT>
 __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restrict__ xv,
                                                         const void* __restrict__ wv,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ logits,
                                                         int32_t* __restrict__ ids,
                                                         float* __restrict__ wts, int T, int d,
-                                                        int E, int k) {
+                                                        int E, int k, GateQuant gq) {
   using GL = GateLds<TEF, KB, TG>;
   constexpr int GS = GL::GS, LDR = GL::LDR, WE = GL::WE, BUF = GL::BUF;
   constexpr int NT = 64 * TG * WS;                   // threads
@@ -320,12 +331,96 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
             f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
     }
   };
+  // Fused quantisation of x piece r of chunk i0 (still raw in xr[r]).  The
+  // KB / EPC lanes that hold one token's part of a chunk are consecutive
+  // lanes of one wave, and a thread holds the same (token, column) piece in
+  // every chunk.  MX: a block of 32 is four of those lanes, so it is
+  // encoded at once.  FP8: the thread keeps its raw pieces of the current
+  // 128-column group and their running amax; when the chunk that ends the
+  // group is staged, the lanes of the token combine their maxima and each
+  // thread encodes its pieces.  Called in wave-uniform control flow (the
+  // shuffles).
+  static_assert(QUANT == 0 || (BF16 && 128 % KB == 0), "quantised activations are bf16");
+  constexpr int QPIECES = (QUANT == 1) ? 128 / KB : 1;  // a thread's pieces of one group
+  float qmax[XR];
+  u32x4 qraw[XR][QPIECES];  // FP8: the raw pieces of the current group
+#pragma unroll
+  for (int r = 0; r < XR; ++r) qmax[r] = 0.f;
+  auto quant_piece = [&](int i0, int r) {
+    const int idx = tid + NT * r;
+    const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
+    const int t = t0 + tl, i = i0 + il;
+    // (when the experts are split over several workgroup columns, the
+    // first column writes the codes: all of them read the same x rows)
+    const bool writer = blockIdx.y == 0;
+    const bool valid = idx < XCH && t < T && i < d;
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = valid ? __uint_as_float(xr[r][q] << 16) : 0.f;
+      v[2 * q + 1] = valid ? __uint_as_float(xr[r][q] & 0xffff0000u) : 0.f;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+    if constexpr (QUANT == 2) {
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      const int xe = mx_exponent_e4m3(m);
+      if (valid && writer) {
+        u32x2 c;
+        c.x = c.y = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c.x |= f32_to_e4m3(__builtin_ldexpf(v[q], -xe)) << (8 * q);
+          c.y |= f32_to_e4m3(__builtin_ldexpf(v[4 + q], -xe)) << (8 * q);
+        }
+        *reinterpret_cast<u32x2*>(gq.q + static_cast<size_t>(t) * d + i) = c;
+        if ((il & 31) == 0)
+          static_cast<uint8_t*>(gq.s)[static_cast<size_t>(t) * (d / 32) + i / 32] =
+              static_cast<uint8_t>(xe + 127);
+      }
+    } else if constexpr (QUANT == 1) {
+      qmax[r] = fmaxf(qmax[r], m);
+      qraw[r][(i0 % 128) / KB] = xr[r];
+      if ((i0 + KB) % 128 == 0) {  // this chunk ends a 128-column group
+        float a = qmax[r];
+#pragma unroll
+        for (int o = 1; o < KB / EPC; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+        qmax[r] = 0.f;
+        const float sc = (a == 0.f) ? 1.0f : __fdiv_rn(a, 448.0f);
+        const int g0 = i0 + KB - 128;
+        if (idx < XCH && t < T && writer) {
+#pragma unroll
+          for (int c = 0; c < 128 / KB; ++c) {
+            const int col = g0 + c * KB + il;
+            const u32x4 raw = qraw[r][c];
+            u32x2 cd;
+            cd.x = cd.y = 0u;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              cd.x |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[q] << 16), sc)) << (16 * q);
+              cd.x |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[q] & 0xffff0000u), sc))
+                      << (16 * q + 8);
+              cd.y |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[2 + q] << 16), sc)) << (16 * q);
+              cd.y |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[2 + q] & 0xffff0000u), sc))
+                      << (16 * q + 8);
+            }
+            *reinterpret_cast<u32x2*>(gq.q + static_cast<size_t>(t) * d + col) = cd;
+          }
+          if (il == 0) static_cast<float*>(gq.s)[static_cast<size_t>(t) * gq.s_stride + g0 / 128] = sc;
+        }
+      }
+    }
+  };
+
   // piece p of the staging (x pieces, then gate_w pieces): store the loaded
   // piece of chunk i0 into buffer b, then (if i2 < d) load the same piece of
   // chunk i2 into the registers it frees
   constexpr int NP = XR + WR;
   auto stage = [&](int p, int b, int i0, int i2) {
     if (p < XR) {
+      if constexpr (QUANT != 0) quant_piece(i0, p);
       store_x(b, p);
       if (i2 < d) load_x(i2, p);
     } else {
@@ -453,24 +548,25 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
 // Raise the dynamic LDS limit of one gate_kernel instantiation to the 160 KB
 // of a CU, once per instantiation (a function-local static of a template is
 // per instantiation); the result of that first call is returned every time.
-template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE>
+template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE, int QUANT>
 hipError_t gate_lds_attr() {
   static const hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(gate_kernel<TEF, WS, KB, TG, BF16, FUSE>),
+      reinterpret_cast<const void*>(gate_kernel<TEF, WS, KB, TG, BF16, FUSE, QUANT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   return e;
 }
 
-template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE>
+template <int TEF, int WS, int KB, int TG, bool BF16, bool FUSE, int QUANT>
 int launch_gate_variant(const void* x, const void* gate_w, const float* bias, float* logits,
-                        int32_t* ids, float* w, int T, int d, int E, int k, hipStream_t s) {
-  const hipError_t attr = gate_lds_attr<TEF, WS, KB, TG, BF16, FUSE>();
+                        int32_t* ids, float* w, int T, int d, int E, int k, GateQuant gq,
+                        hipStream_t s) {
+  const hipError_t attr = gate_lds_attr<TEF, WS, KB, TG, BF16, FUSE, QUANT>();
   if (attr != hipSuccess) return static_cast<int>(attr);
   const dim3 grid((T + 16 * TG - 1) / (16 * TG), FUSE ? 1 : (E + 16 * TEF - 1) / (16 * TEF));
   size_t lds = sizeof(float) * 2 * static_cast<size_t>(GateLds<TEF, KB, TG>::BUF);
   if (FUSE) lds = std::max(lds, sizeof(float) * 16 * TG * static_cast<size_t>(E + 1));
-  gate_kernel<TEF, WS, KB, TG, BF16, FUSE>
-      <<<grid, 64 * TG * WS, lds, s>>>(x, gate_w, bias, logits, ids, w, T, d, E, k);
+  gate_kernel<TEF, WS, KB, TG, BF16, FUSE, QUANT>
+      <<<grid, 64 * TG * WS, lds, s>>>(x, gate_w, bias, logits, ids, w, T, d, E, k, gq);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -494,7 +590,8 @@ void launch_topk(const float* logits, int32_t* ids, float* w, int T, int E, int 
 // wave's staging overlaps the other's MFMAs.  d % 32 == 0.  Returns a
 // hipError_t (hipSuccess when everything was enqueued).
 int launch_gate(const void* x, const void* gate_w, const float* bias, float* logits,
-                int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s) {
+                int32_t* ids, float* w, int T, int d, int E, int k, bool bf16, hipStream_t s,
+                int quant, uint8_t* xq, void* xs, int64_t xs_stride) {
   if (T <= 0) return 0;
   const long long tw = (T + 15) / 16;  // token waves
   const int ef = (E + 15) / 16;        // expert fragments
@@ -513,21 +610,33 @@ int launch_gate(const void* x, const void* gate_w, const float* bias, float* log
       }
     }
   }
+  // fused quantisation: bf16 activations only (FP8 and MXFP4 layers)
+  if (quant != 0 && !bf16) return static_cast<int>(hipErrorInvalidValue);
+  const GateQuant gq{xq, xs, xs_stride};
   int rc = -1;
   // (TEF, WS, KB, TG): the widest expert tiles stage 128 tokens per
   // workgroup, which halves the gate_w traffic per token
-#define MOE_G(TEF_, WS_, KB_, TG_)                                                          \
-  if (tef == TEF_) {                                                                        \
-    if (fuse)                                                                               \
-      rc = bf16 ? launch_gate_variant<TEF_, WS_, KB_, TG_, true, true>(                     \
-                      x, gate_w, bias, logits, ids, w, T, d, E, k, s)                       \
-                : launch_gate_variant<TEF_, WS_, KB_, TG_, false, true>(                    \
-                      x, gate_w, bias, logits, ids, w, T, d, E, k, s);                      \
-    else                                                                                    \
-      rc = bf16 ? launch_gate_variant<TEF_, WS_, KB_, TG_, true, false>(                    \
-                      x, gate_w, bias, logits, ids, w, T, d, E, k, s)                       \
-                : launch_gate_variant<TEF_, WS_, KB_, TG_, false, false>(                   \
-                      x, gate_w, bias, logits, ids, w, T, d, E, k, s);                      \
+#define MOE_GQ(TEF_, WS_, KB_, TG_, FU_, Q_)                                                  \
+  rc = launch_gate_variant<TEF_, WS_, KB_, TG_, true, FU_, Q_>(x, gate_w, bias, logits, ids, w, \
+                                                              T, d, E, k, gq, s)
+#define MOE_G(TEF_, WS_, KB_, TG_)                                                            \
+  if (tef == TEF_) {                                                                          \
+    if (!bf16) {                                                                              \
+      if (fuse)                                                                               \
+        rc = launch_gate_variant<TEF_, WS_, KB_, TG_, false, true, 0>(                        \
+            x, gate_w, bias, logits, ids, w, T, d, E, k, gq, s);                              \
+      else                                                                                    \
+        rc = launch_gate_variant<TEF_, WS_, KB_, TG_, false, false, 0>(                       \
+            x, gate_w, bias, logits, ids, w, T, d, E, k, gq, s);                              \
+    } else if (fuse) {                                                                        \
+      if (quant == 1) MOE_GQ(TEF_, WS_, KB_, TG_, true, 1);                                   \
+      else if (quant == 2) MOE_GQ(TEF_, WS_, KB_, TG_, true, 2);                              \
+      else MOE_GQ(TEF_, WS_, KB_, TG_, true, 0);                                              \
+    } else {                                                                                  \
+      if (quant == 1) MOE_GQ(TEF_, WS_, KB_, TG_, false, 1);                                  \
+      else if (quant == 2) MOE_GQ(TEF_, WS_, KB_, TG_, false, 2);                             \
+      else MOE_GQ(TEF_, WS_, KB_, TG_, false, 0);                                             \
+    }                                                                                         \
   }
   MOE_G(1, 1, 128, 4)
   MOE_G(2, 2, 128, 4)
@@ -535,6 +644,7 @@ int launch_gate(const void* x, const void* gate_w, const float* bias, float* log
   MOE_G(8, 2, 64, 4)
   MOE_G(16, 2, 32, 8)
 #undef MOE_G
+#undef MOE_GQ
   if (rc != 0) return rc;
   if (!fuse) launch_topk(logits, ids, w, T, E, k, s);
   return static_cast<int>(hipGetLastError());

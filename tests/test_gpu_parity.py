@@ -204,6 +204,31 @@ def test_quantize_fp8_bit_exact():
     assert np.array_equal(s.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("name", ["prefill_fp8_r", "prefill_mxfp4_r", "fp8_small", "mx_small",
+                                  "wide_fp8", "prefill_fp8", "prefill_mxfp4"])
+def test_forward_activation_codes_bit_exact(name):
+    # the gate quantises x for the FP8 / MXFP4 expert GEMMs in its own pass
+    # over x: the codes and scales the fused call used equal the oracle's
+    # quantisation of x, bit for bit, on every token
+    cfg = REDUCED.get(name) or EDGE.get(name) or CONFIGS[name]
+    say("fused x quantisation", name)
+    inp = gpu_inputs(cfg)
+    mx = cfg.w_dtype == MXFP4
+    dbg = {"x_codes": poisoned((cfg.T, cfg.d), torch.uint8),
+           "x_scales": poisoned((cfg.T, cfg.d // 32), torch.uint8) if mx
+           else poisoned((cfg.T, cfg.d // 128), torch.float32)}
+    _forward(cfg, inp, dbg=dbg)
+    xf = inp["x"].float().cpu().numpy()
+    if mx:
+        rq, rs = oracle.mx_quant_rows(xf, oracle.MX_E4M3)
+    else:
+        rq, rs = oracle.fp8_quant_rows(xf)
+    assert np.array_equal(dbg["x_codes"].cpu().numpy(), rq)
+    assert np.array_equal(dbg["x_scales"].cpu().numpy(), rs)
+    del inp, dbg
+    free()
+
+
 def test_quantize_mx_bit_exact():
     say("quant mx")
     g = torch.Generator(device="cuda")
