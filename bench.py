@@ -116,8 +116,10 @@ def _elapsed(hip, a, b):
 
 
 def _src_hash():
+    """Hash of the sources the grouped-GEMM kernels are built from: counter
+    figures taken on them stay valid until one of these files changes."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc"))):
+    for f in ("gemm.hip", "launch.hpp", "device_common.hpp"):
         with open(os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -221,6 +223,96 @@ def _cpu_baseline(cfg, inp, out_gpu, out32_gpu, target_s):
             "kind": "oracle",
             "sample": f"{n} of {cfg.T} tokens (seeded random rows), full layer forward per "
                       f"token, {secs:.1f} s", "seconds": secs}, err
+
+
+def _kernel_short_name(name):
+    """'void moe::(anonymous namespace)::gemm<1, 2>(moe::GemmArgs)' ->
+    'gemm<1, 2>': return type, namespaces and the parameter list dropped."""
+    import re
+    name = re.sub(r"^void ", "", name.strip())
+    name = re.sub(r"^moe::\(anonymous namespace\)::", "", name)
+    depth = 0
+    for i, ch in enumerate(name):  # cut at the '(' of the parameter list
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i].strip()
+    return name
+
+
+def trace_summary(csv_path, warmup, steps, workloads):
+    """Markdown summary of a rocprofv3 kernel trace (--kernel-trace, csv) of a
+    bench.py run: per workload, per library kernel, the dispatch count, the
+    average over every dispatch and the average over the timed steps alone.
+    Each moe_forward call starts with exactly one gate_kernel dispatch, so
+    the library's dispatches (in start order) split into forward calls; the
+    workloads ran one after another in the given order, each with `warmup`
+    untimed calls first and `steps` timed ones next (then untimed ones)."""
+    import csv
+    import re
+    lib = re.compile(r"^(gate_kernel|topk_kernel|hist_kernel|scan_kernel|scatter_kernel|"
+                     r"permute_one_kernel|quant_fp8_kernel|quant_mx_kernel|"
+                     r"grouped_gemm_kernel|ring_gemm_kernel|combine_kernel|zero_kernel)")
+    rows = []
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            short = _kernel_short_name(r["Kernel_Name"])
+            if lib.match(short):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short))
+    rows.sort()
+    calls = []  # forward calls: lists of (kernel, microseconds)
+    for t0, t1, name in rows:
+        if name.startswith("gate_kernel") or not calls:
+            calls.append([])
+        calls[-1].append((name, (t1 - t0) / 1e3))
+    # a workload's calls: consecutive calls whose gate kernel has the same name
+    groups = []
+    for c in calls:
+        if not groups or groups[-1][0] != c[0][0]:
+            groups.append((c[0][0], []))
+        groups[-1][1].append(c)
+    out = []
+    for (gate, cs), wl in zip(groups, workloads):
+        out.append(f"\n### {wl} ({len(cs)} forward calls; timed: calls {warmup + 1}.."
+                   f"{warmup + steps})\n")
+        out.append("| kernel | calls | avg us | timed steps avg us | % of timed layer |")
+        out.append("|---|---|---|---|---|")
+        per = {}
+        for i, c in enumerate(cs):
+            for name, us in c:
+                d = per.setdefault(name, [[], []])
+                d[0].append(us)
+                if warmup <= i < warmup + steps:
+                    d[1].append(us)
+        tot = sum(sum(v[1]) for v in per.values()) or 1.0
+        for name, (a, tm) in sorted(per.items(), key=lambda kv: -sum(kv[1][1])):
+            avg_t = f"{sum(tm) / len(tm):.1f}" if tm else "-"
+            out.append(f"| {name} | {len(a)} | {sum(a) / len(a):.1f} | {avg_t} | "
+                       f"{100.0 * sum(tm) / tot:.1f} |")
+    return "\n".join(out)
+
+
+def counter_summary(csv_path):
+    """Markdown table of a rocprofv3 --pmc run (csv): per kernel, grid size
+    and counter, the number of dispatches and the mean value per dispatch
+    (the grid size tells apart dispatches of one kernel on different sizes,
+    such as the runtime's copy kernel on the 1 GiB calibration copy)."""
+    import csv
+    acc = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            name = _kernel_short_name(r["Kernel_Name"])
+            if name.startswith("at::native"):
+                continue
+            key = (name, int(r.get("Grid_Size") or 0), r["Counter_Name"])
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    out = ["| kernel | grid | counter | dispatches | mean per dispatch |",
+           "|---|---|---|---|---|"]
+    for (name, grid, ctr), v in sorted(acc.items()):
+        out.append(f"| {name[:90]} | {grid} | {ctr} | {len(v)} | {sum(v) / len(v):.1f} |")
+    return "\n".join(out)
 
 
 def _free(torch):
@@ -401,7 +493,22 @@ def main():
     ap.add_argument("--block-m", type=int, default=0, help="expert tile height (0 = auto)")
     ap.add_argument("--ring", action="store_true",
                     help="time moe_forward_ring (both GEMMs in one launch, h in a bounded ring)")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="print per-kernel mean counter values of a rocprofv3 --pmc csv (no GPU "
+                         "use)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print a per-kernel summary of a rocprofv3 kernel trace of a bench run "
+                         "made with the same --steps/--warmup/--workload flags (no GPU use)")
     args = ap.parse_args()
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
+        return
+    if args.trace_summary:
+        wls = [args.workload]
+        if not args.no_other_configs and not args.ring and args.workload == "prefill_bf16":
+            wls += OTHER_CONFIGS
+        print(trace_summary(args.trace_summary, args.warmup, args.steps, wls))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)

@@ -350,9 +350,11 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
     const int idx = tid + NT * r;
     const int tl = idx / (KB / EPC), il = (idx % (KB / EPC)) * EPC;
     const int t = t0 + tl, i = i0 + il;
-    // (when the experts are split over several workgroup columns, the
-    // first column writes the codes: all of them read the same x rows)
-    const bool writer = blockIdx.y == 0;
+    // (when the experts are split over several workgroup columns, all of
+    // them read the same x rows: 128-column group g is written by column
+    // g mod gridDim.y, which spreads the encoding over the columns when
+    // there are few token rows)
+    const bool writer = blockIdx.y == static_cast<unsigned>(i0 / 128) % gridDim.y;
     const bool valid = idx < XCH && t < T && i < d;
     float v[8];
 #pragma unroll
