@@ -158,7 +158,7 @@ def _stage_work(cfg, counts):
     n = cfg.T * (cfg.k + cfg.n_shared)
     w13 = dict(flops=4.0 * n * cfg.d * cfg.f,
                bytes=hit * 2.0 * cfg.d * cfg.f * es + cfg.T * cfg.d * ae + n * cfg.f * he)
-    ye = 2.0 if cfg.w_dtype in (2, 3) else 4.0  # Y: bf16 on FP8 / MXFP4 layers, else fp32
+    ye = 2.0 if cfg.w_dtype == 3 else 4.0  # Y: bf16 on MXFP4 layers, else fp32
     w2 = dict(flops=2.0 * n * cfg.d * cfg.f,
               bytes=hit * 1.0 * cfg.d * cfg.f * es + n * cfg.f * he + n * cfg.d * ye)
     return {"gemm_w13_swiglu": w13, "gemm_w2": w2, "hit_experts": hit}

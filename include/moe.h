@@ -37,7 +37,8 @@
  *  - SwiGLU expert: h = SiLU(x W1) * (x W3), SiLU(a) = a / (1 + e^-a),
  *    y = h W2, fp32 accumulation; h is rounded to the activation format
  *    (fp32, bf16 RNE, FP8 1x128 groups, or MX FP8 blocks of 32 for
- *    MOE_MXFP4) before W2; y stays fp32.
+ *    MOE_MXFP4) before W2; y per slot stays fp32 (bf16 RNE on MXFP4 layers,
+ *    whose 5e-2 tolerance absorbs that rounding).
  *  - FP8 groups: activations per 1x128 group along the contraction axis with
  *    scale s = amax / 448 (1 when amax == 0) and code e4m3_rne_sat(v / s)
  *    (both quotients fp32 IEEE); weights per 128x128 (K, N) block.
@@ -181,6 +182,15 @@ typedef struct {
      * MXFP4: [T][d/32] E8M0 bytes.  Ignored on other layers. */
     uint8_t *x_codes;
     void *x_scales;
+    /* moe_forward only: NULL, or device buffers receiving the input rows of
+     * the W2 GEMM (the SwiGLU output, rounded as W2 reads it) in slot order:
+     * the T*k routed slots, then T rows per shared expert.
+     *   h        [T*(k+n_shared)][f]  fp32 / bf16 layers: act_dtype values;
+     *                                  FP8 and MXFP4 layers: E4M3 codes
+     *   h_scales FP8: [T*(k+n_shared)][f/128] fp32; MXFP4: [..][f/32] E8M0
+     *            bytes; ignored on other layers. */
+    void *h;
+    void *h_scales;
 } moe_debug;
 
 /* Human-readable name of a status code (static storage). */

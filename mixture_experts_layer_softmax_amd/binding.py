@@ -47,7 +47,7 @@ class MoEDebug(ctypes.Structure):
         ("ring_poll_limit", ctypes.c_int32), ("ring_force_timeout", ctypes.c_int32),
         ("queue_order", ctypes.c_int32), ("task_log", ctypes.c_void_p),
         ("task_log_capacity", ctypes.c_int32), ("x_codes", ctypes.c_void_p),
-        ("x_scales", ctypes.c_void_p)]
+        ("x_scales", ctypes.c_void_p), ("h", ctypes.c_void_p), ("h_scales", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -221,7 +221,7 @@ def _debug_struct(dbg):
     dbg_s.ring_poll_limit = int(dbg.get("ring_poll_limit", 0))
     dbg_s.ring_force_timeout = int(dbg.get("ring_force_timeout", 0))
     dbg_s.queue_order = int(dbg.get("queue_order", 0))
-    for name in ("x_codes", "x_scales"):
+    for name in ("x_codes", "x_scales", "h", "h_scales"):
         if dbg.get(name) is not None:
             setattr(dbg_s, name, dbg[name].data_ptr())
     if dbg.get("task_log") is not None:  # uint32 tensor [2][capacity][4]

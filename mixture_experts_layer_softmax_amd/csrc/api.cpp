@@ -82,9 +82,10 @@ bool valid_problem(const moe_problem* p) {
 bool supported_layout(const moe_problem& p) { return p.w_layout == MOE_W_NK; }
 
 // Bytes per element of Y, the expert outputs per slot: fp32, except bf16 for
-// FP8 and MXFP4 weights (their 5e-2 tolerance leaves room for the rounding,
-// and Y is the largest buffer of those layers).
-int y_bytes(const moe_problem& p) { return quantised_weights(p.w_dtype) ? 2 : 4; }
+// MXFP4 weights (their 5e-2 tolerance leaves room for the rounding, and Y is
+// the largest buffer of those layers; on FP8 layers the rounding would use up
+// most of the margin the quantisation of h leaves, so they keep fp32).
+int y_bytes(const moe_problem& p) { return p.w_dtype == MOE_MXFP4 ? 2 : 4; }
 
 // Floats per row of the FP8 activation scales inside the workspace (x and
 // h: one per 128 elements): padded to a multiple of 4, so that the GEMM
@@ -515,6 +516,17 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
                                sizeof(float) * (p->d / 128), p->T, hipMemcpyDeviceToDevice,
                                stream);
       if (mx) cp(dbg->x_scales, at<uint8_t>(ws, L.sx), static_cast<size_t>(p->T) * (p->d / 32));
+    }
+    if (!ring) {  // (the ring keeps only the chunks in flight)
+      const int64_t rows = gemm_rows(*p);
+      cp(dbg->h, at<uint8_t>(ws, L.h),
+         static_cast<size_t>(rows) * p->f * (q8 ? 1 : esize(p->act_dtype)));
+      if (dbg->h_scales && fp8)
+        (void)hipMemcpy2DAsync(dbg->h_scales, sizeof(float) * (p->f / 128), at<float>(ws, L.hs),
+                               sizeof(float) * fp8_scale_stride(p->f),
+                               sizeof(float) * (p->f / 128), rows, hipMemcpyDeviceToDevice,
+                               stream);
+      if (mx) cp(dbg->h_scales, at<uint8_t>(ws, L.hs), static_cast<size_t>(rows) * (p->f / 32));
     }
   }
   return hip_status();

@@ -52,7 +52,7 @@ struct GemmArgs {
   int64_t N;              // output columns: f (phase 1) or d (phase 2)
   // outputs
   uint8_t* C;             // h [slots][f] (phase 1) or Y [slots][d] (phase 2: fp32, or
-                          // bf16 for FP8 and MXFP4 weights)
+                          // bf16 for MXFP4 weights)
   float* sc;              // phase 1 h scales: FP8 [slots][sc_stride]; MX E8M0 bytes [slots][f/32]
   int sc_stride;          // FP8: floats per h scale row, a multiple of 4
   TileMap tm;

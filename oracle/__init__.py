@@ -16,6 +16,7 @@ from .oracle import (  # noqa: F401
     e2m1_encode,
     e4m3_decode,
     e4m3_encode,
+    expert_hidden,
     fp8_quant_rows,
     forward,
     mx_exponent,

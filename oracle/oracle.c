@@ -513,6 +513,33 @@ static void mirror_h(const orc_problem *p, double *h)
 #define ORC_BLOCK 8 /* slots of one expert evaluated together */
 #define SCALED(p) ((p)->w_dtype == ORC_FP8 || (p)->w_dtype == ORC_MXFP4)
 
+/* SwiGLU hidden rows h = SiLU(rows W1) * (rows W3) in fp64, before any
+ * rounding to the format W2 reads (FlashMoE Kernel page, the FFN stage).
+ * rows: [nr x d]; h: [nr x f].  Each product is an fp64 sum over the
+ * contraction index ascending. */
+static void swiglu_rows(const orc_problem *p, int nr, const double *rows,
+                        const void *W1, const void *W3, const void *W1s,
+                        const void *W3s, double *h)
+{
+    int64_t d = p->d, f = p->f, i, n;
+    int r;
+    double *b = (double *)calloc((size_t)(nr * f), sizeof(double));
+    memset(h, 0, sizeof(double) * (size_t)(nr * f));
+    for (i = 0; i < d; ++i)
+        for (n = 0; n < f; ++n) {
+            double w1 = load_w(p, W1, W1s, f, i, n);
+            double w3 = load_w(p, W3, W3s, f, i, n);
+            for (r = 0; r < nr; ++r) {
+                h[r * f + n] += rows[r * d + i] * w1;
+                b[r * f + n] += rows[r * d + i] * w3;
+            }
+        }
+    for (r = 0; r < nr; ++r)
+        for (n = 0; n < f; ++n) /* SiLU(a) * b */
+            h[r * f + n] = h[r * f + n] / (1.0 + exp(-h[r * f + n])) * b[r * f + n];
+    free(b);
+}
+
 /* Expert FFN for up to ORC_BLOCK activation rows of one expert.
  * rows: [nr x d]; y: [nr x d].  Each output element is an fp64 sum over the
  * contraction index ascending. */
@@ -521,25 +548,12 @@ static void expert_ffn(const orc_problem *p, int nr, const double *rows,
                        const void *W1s, const void *W3s, const void *W2s,
                        double *y)
 {
-    int64_t d = p->d, f = p->f, i, n, m;
+    int64_t d = p->d, f = p->f, n, m;
     int r;
-    double *a = (double *)calloc((size_t)(nr * f), sizeof(double));
-    double *b = (double *)calloc((size_t)(nr * f), sizeof(double));
-    for (i = 0; i < d; ++i)
-        for (n = 0; n < f; ++n) {
-            double w1 = load_w(p, W1, W1s, f, i, n);
-            double w3 = load_w(p, W3, W3s, f, i, n);
-            for (r = 0; r < nr; ++r) {
-                a[r * f + n] += rows[r * d + i] * w1;
-                b[r * f + n] += rows[r * d + i] * w3;
-            }
-        }
-    for (r = 0; r < nr; ++r) {
-        double *h = a + r * f;
-        for (n = 0; n < f; ++n) /* SiLU(a) * b */
-            h[n] = h[n] / (1.0 + exp(-h[n])) * b[r * f + n];
-        mirror_h(p, h);
-    }
+    double *a = (double *)malloc(sizeof(double) * (size_t)(nr * f));
+    swiglu_rows(p, nr, rows, W1, W3, W1s, W3s, a);
+    for (r = 0; r < nr; ++r)
+        mirror_h(p, a + r * f);
     memset(y, 0, sizeof(double) * (size_t)(nr * d));
     for (n = 0; n < f; ++n)
         for (m = 0; m < d; ++m) {
@@ -548,7 +562,25 @@ static void expert_ffn(const orc_problem *p, int nr, const double *rows,
                 y[r * d + m] += a[r * f + n] * w2;
         }
     free(a);
-    free(b);
+}
+
+/* The exact SwiGLU output (fp64, before rounding to W2's input format) of
+ * token t through one expert's W1, W3 (and their scales for FP8 and MXFP4
+ * weights, else NULL): h [f].  The activation row is the one the experts
+ * consume (quantised and dequantised on FP8 and MXFP4 layers).  Returns 0,
+ * or 1 for a token out of range. */
+int orc_expert_hidden(const orc_problem *p, const void *x, int64_t t,
+                      const void *W1, const void *W3, const void *W1s,
+                      const void *W3s, double *h)
+{
+    if (t < 0 || t >= p->T)
+        return 1;
+    init_e4m3_values();
+    double *row = (double *)malloc(sizeof(double) * (size_t)p->d);
+    expert_input_row(p, x, t, row);
+    swiglu_rows(p, 1, row, W1, W3, W1s, W3s, h);
+    free(row);
+    return 0;
 }
 
 /* Layer forward for a list of tokens.

@@ -61,6 +61,8 @@ def _load():
     lib.orc_forward.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P, P, P, P,
                                 P, i64, P, P, P]
     lib.orc_forward.restype = ctypes.c_int
+    lib.orc_expert_hidden.argtypes = [ctypes.POINTER(_Problem), P, i64, P, P, P, P, P]
+    lib.orc_expert_hidden.restype = ctypes.c_int
     lib.orc_fp8_quant_rows.argtypes = [i64, i64, P, P, P]
     lib.orc_e4m3_encode_array.argtypes = [i64, P, P]
     lib.orc_e4m3_decode_array.argtypes = [i64, P, P]
@@ -198,6 +200,32 @@ def forward(x, gate_w, bias, W1, W3, W2, k, act_dtype, w_dtype, tokens=None,
     if rc:
         raise ValueError("orc_forward rejected its arguments (bad token or missing expert)")
     return out, ids, w
+
+
+def expert_hidden(x, t, W1, W3, act_dtype, w_dtype, W1s=None, W3s=None):
+    """Exact SwiGLU output of token t through one expert, before it is
+    rounded to the format W2 reads: fp64 [f].  x is the full [T x d]
+    activation matrix (fp32, or bf16 bits as uint16); W1, W3 one expert's
+    [d x f] weights in the layout forward() takes, W1s/W3s their scales for
+    FP8 and MXFP4 weights."""
+    lib = _load()
+    x = _act(x, act_dtype)
+    T, d = x.shape
+    wdt = {ORC_F32: np.float32, ORC_BF16: np.uint16, ORC_FP8: np.uint8,
+           ORC_MXFP4: np.uint8}[w_dtype]
+    W1, W3 = _c(W1, wdt), _c(W3, wdt)
+    f = W1.shape[1]
+    sdt = {ORC_FP8: np.float32, ORC_MXFP4: np.uint8}.get(w_dtype)
+    if sdt is not None:
+        W1s, W3s = _c(W1s, sdt), _c(W3s, sdt)
+    else:
+        W1s = W3s = None
+    h = np.empty(f, np.float64)
+    p = _problem(T, d, f, 1, 1, act_dtype, w_dtype)
+    if lib.orc_expert_hidden(ctypes.byref(p), _ptr(x), int(t), _ptr(W1), _ptr(W3),
+                             _ptr(W1s), _ptr(W3s), _ptr(h)):
+        raise ValueError("orc_expert_hidden: token out of range")
+    return h
 
 
 def fp8_quant_rows(v):

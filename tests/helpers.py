@@ -52,3 +52,76 @@ def f32_ulps(a: np.ndarray, b: np.ndarray) -> int:
     ia = a.astype(np.float32).view(np.int32).astype(np.int64)
     ib = b.astype(np.float32).view(np.int32).astype(np.int64)
     return int(np.max(np.abs(ia - ib))) if ia.size else 0
+
+
+# Slack of the hidden-row check, relative to the largest |h| of the row (fp32
+# and bf16 layers) or of the scale group (FP8, MX): how far the GPU's fp32 h
+# may sit from the exact value before it is rounded to the format W2 reads.
+# fp32 / bf16 layers sum exact products in fp32 (error ~1e-7 of the row's
+# largest |h|).  The FP8 and MX FP8 MFMAs add each group of 8 consecutive
+# products after aligning them to the largest with 13 fractional bits
+# (measured: of 1 + 7 products of 2^-14 in one group only the 1 survives,
+# products of 2^-13 all do), so their block sums carry ~1e-5 relative error;
+# the largest deviation measured over 2400 hidden rows at d = 512 and 128 at
+# d = 7168 was 8.2e-5 of the group amax.
+HIDDEN_SLACK = {"f32": 1e-5, "bf16": 1e-5, "fp8": 2e-4, "mx": 2e-4}
+
+
+def _e4m3_spacing(a: np.ndarray) -> np.ndarray:
+    """Spacing of E4M3FN numbers at magnitude a (subnormal spacing 2^-9)."""
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.exp2(e - 3)
+
+
+def _e4m3_value(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(
+        torch.float8_e4m3fn).double().numpy()
+
+
+def check_hidden_row(exact: np.ndarray, got: np.ndarray, fmt: str, scales=None):
+    """One W2 input row from the GPU against the exact fp64 SwiGLU output.
+
+    Every element must be a correct rounding (to the layer's format, under
+    the GPU's own scale) of some value within HIDDEN_SLACK[fmt] x the row's
+    (or group's) largest |h| of the exact one, and each FP8 group scale / MX
+    block exponent must be the one of such values.  fmt: "f32", "bf16"
+    (got: values), "fp8" (got: E4M3 codes, scales: fp32 per 128),
+    "mx" (got: E4M3 codes, scales: E8M0 bytes per 32).  Returns
+    (elements whose rounding differs from that of the exact value, worst
+    excess over the allowance in units of the allowance)."""
+    exact = np.asarray(exact, np.float64)
+    if fmt in ("f32", "bf16"):
+        got = np.asarray(got, np.float64)
+        slack = HIDDEN_SLACK[fmt] * np.abs(exact).max()
+        if fmt == "bf16":
+            half = 0.5 * ulp_bf16(np.abs(exact) + slack)
+            nearest = torch.from_numpy(exact).to(torch.bfloat16).double().numpy()
+        else:
+            half = 0.5 * np.spacing(np.abs(exact + slack).astype(np.float32)).astype(np.float64)
+            nearest = exact.astype(np.float32).astype(np.float64)
+        allow = half + slack
+        dev = np.abs(got - exact)
+        return int((got != nearest).sum()), float((dev / allow).max())
+    group = 128 if fmt == "fp8" else 32
+    g = exact.reshape(-1, group)
+    amax = np.abs(g).max(axis=1)
+    slack = HIDDEN_SLACK[fmt] * amax
+    if fmt == "fp8":
+        s = np.asarray(scales, np.float64)
+        s_exact = np.where(amax == 0, 1.0, amax / 448.0)
+        assert np.all(np.abs(s - s_exact) <= HIDDEN_SLACK[fmt] * s_exact + 1e-45), \
+            f"FP8 group scale off: worst {np.max(np.abs(s - s_exact) / s_exact):.3e}"
+    else:
+        x = np.asarray(scales, np.int64) - 127
+        lo = np.floor(np.log2(np.maximum(amax - slack, 1e-300))) - 8
+        hi = np.floor(np.log2(np.maximum(amax + slack, 1e-300))) - 8
+        ok = (x == np.clip(lo, -127, 127)) | (x == np.clip(hi, -127, 127)) | (amax == 0)
+        assert ok.all(), f"MX block exponent off in {int((~ok).sum())} blocks"
+        s = np.exp2(x.astype(np.float64))
+    u = np.clip(g / s[:, None], -448.0, 448.0)
+    slack_c = (slack / s)[:, None]
+    dec = _e4m3_value(np.asarray(got).reshape(u.shape))
+    allow = 0.5 * _e4m3_spacing(np.abs(u) + slack_c) + slack_c
+    dev = np.abs(dec - u)
+    nearest = torch.from_numpy(u.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+    return int((dec != nearest).sum()), float((dev / allow).max())

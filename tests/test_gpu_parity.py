@@ -18,7 +18,7 @@ from mixture_experts_layer_softmax_amd.configs import BF16, CONFIGS, F32, FP8, M
 from tests.gpu_common import (debug_buffers, forward, forward_ring, free, gpu_inputs, gpu_permute, gpu_route,
                               oracle_forward_rows, oracle_route_rows, poison_, poisoned,
                               poisoned_workspace, say)
-from tests.helpers import TOL, check_output, f32_ulps
+from tests.helpers import TOL, check_hidden_row, check_output, f32_ulps
 
 pytestmark = pytest.mark.gpu
 
@@ -450,6 +450,74 @@ def test_shared_expert_leaves_routing_alone():
 
 FULL_SAMPLE = {"prefill_bf16": 256, "decode_bf16": 64, "skewed_bf16": 256, "prefill_fp8": 64,
                "prefill_bf16_shared": 256, "prefill_mxfp4": 64, "decode_mxfp4": 64}
+
+
+HIDDEN = {n: REDUCED[n] for n in ("tiny_fp32", "prefill_bf16_r", "decode_bf16_r",
+                                    "prefill_fp8_r", "prefill_mxfp4_r", "decode_mxfp4_r")}
+HIDDEN.update({n: SHARED[n] for n in ("sh_fp32", "sh_bf16", "sh_fp8", "sh_mx")})
+
+
+@pytest.mark.parametrize("name", list(HIDDEN) + ["prefill_bf16", "prefill_fp8", "prefill_mxfp4"])
+def test_hidden_rows_match_oracle(name):
+    """The W2 GEMM's input rows (SwiGLU output as stored: bf16 / fp32 values,
+    or E4M3 codes with their FP8 group scales / MX block exponents) against
+    the oracle's exact SwiGLU output of the same (token, expert): each element
+    a correct rounding of a value within a small slack of the exact one.
+    Reduced shapes: every slot; full sizes: sampled slots."""
+    full = name not in HIDDEN
+    cfg = CONFIGS[name] if full else HIDDEN[name]
+    say("hidden", name)
+    T, E, k, f = cfg.T, cfg.E, cfg.k, cfg.f
+    rows, n = T * (k + cfg.n_shared), T * k
+    q8 = cfg.w_dtype in (FP8, MXFP4)
+    hdt = torch.uint8 if q8 else (torch.float32 if cfg.act_dtype == F32 else torch.bfloat16)
+    dbg = debug_buffers(cfg, keys=["topk_ids", "slot_token", "slot_k"])
+    dbg["h"] = poisoned((rows, f), hdt)
+    if q8:
+        dbg["h_scales"] = poisoned((rows, f // 128), torch.float32) if cfg.w_dtype == FP8 else \
+            poisoned((rows, f // 32), torch.uint8)
+    inp = gpu_inputs(cfg)
+    _forward(cfg, inp, dbg=dbg)
+    ids = dbg["topk_ids"].cpu().numpy()
+    st, sk = dbg["slot_token"].cpu().numpy(), dbg["slot_k"].cpu().numpy()
+    rng = np.random.default_rng(5)
+    slots = np.sort(rng.choice(n, size=24, replace=False)) if full else np.arange(n)
+    shared = [n + j * T + t for j in range(cfg.n_shared)
+              for t in (rng.choice(T, size=4, replace=False) if full else range(T))]
+    slots = np.concatenate([slots, np.asarray(shared, np.int64)]).astype(np.int64)
+    pairs = []
+    for s_ in slots:
+        if s_ < n:
+            t = int(st[s_])
+            pairs.append((t, int(ids[t * k + int(sk[s_])])))
+        else:
+            pairs.append((int((s_ - n) % T), E + int((s_ - n) // T)))
+    toks = sorted(set(t for t, _ in pairs))
+    xi = {t: i for i, t in enumerate(toks)}
+    from mixture_experts_layer_softmax_amd.inputs import host_arrays, host_weight
+    xh = host_arrays(inp["x"][torch.as_tensor(toks, device="cuda")])
+    sel = torch.as_tensor(slots, device="cuda")
+    h = dbg["h"][sel]
+    h = (h.float() if not q8 else h).cpu().numpy()
+    hs = dbg["h_scales"][sel].cpu().numpy() if q8 else None
+    fmt = {FP8: "fp8", MXFP4: "mx"}.get(cfg.w_dtype, "f32" if cfg.act_dtype == F32 else "bf16")
+    orc = {F32: oracle.ORC_F32, BF16: oracle.ORC_BF16, FP8: oracle.ORC_FP8,
+           MXFP4: oracle.ORC_MXFP4}
+    wcache, flips, worst = {}, 0, 0.0
+    for i, (t, e) in enumerate(pairs):
+        if e not in wcache:
+            wcache = {e: (host_weight(cfg, inp, "W1", e), host_weight(cfg, inp, "W3", e))}
+        (w1, s1), (w3, s3) = wcache[e]
+        exact = oracle.expert_hidden(xh, xi[t], w1, w3, orc[cfg.act_dtype], orc[cfg.w_dtype],
+                                     W1s=s1, W3s=s3)
+        nf, ex = check_hidden_row(exact, h[i], fmt, None if hs is None else hs[i])
+        flips += nf
+        worst = max(worst, ex)
+        assert ex <= 1.0, (f"{name}: slot {int(slots[i])} (token {t}, expert {e}) off by "
+                           f"{ex:.2f} x the allowance")
+    say(f"  {len(pairs)} rows, {flips} elements rounded the other way at a boundary, "
+        f"worst {worst:.3f} x allowance")
+    free()
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16", "decode_bf16", "skewed_bf16",

@@ -201,3 +201,28 @@ def test_tolerance_budget_of_fp32_accumulation_pipeline():
     rms = math.sqrt(float(np.mean(out ** 2)))
     err = float(np.abs(gpu.double().numpy() - out).max()) / rms
     assert err < 5e-3
+
+
+@pytest.mark.parametrize("act,wdt,d,f", [(ORC_F32, ORC_F32, 32, 48),
+                                         (ORC_BF16, ORC_BF16, 64, 64),
+                                         (ORC_BF16, ORC_FP8, 256, 256)])
+def test_expert_hidden_is_dense_swiglu(act, wdt, d, f):
+    # the unrounded SwiGLU output of one (token, expert): SiLU(x W1) * (x W3)
+    # by numpy matmuls on independently decoded operands (FP8: x quantised
+    # per 1x128 group by torch's cast, weights decoded by torch)
+    T, E = 12, 3
+    inp = _make(T, d, f, E, 1, act, wdt, seed=40 + act + wdt)
+    x = inp["xv"]
+    if wdt == ORC_FP8:
+        x = _quant_rows_torch(x.astype(np.float32))
+    sc = inp["scales"]
+    for e in range(E):
+        ref = _silu(x @ inp["W1v"][e]) * (x @ inp["W3v"][e])
+        for t in range(T):
+            h = oracle.expert_hidden(inp["x"], t, inp["W1"][e], inp["W3"][e], act, wdt,
+                                     W1s=sc["W1"][e] if sc else None,
+                                     W3s=sc["W3"][e] if sc else None)
+            assert np.abs(h - ref[t]).max() <= 1e-12 * np.abs(ref[t]).max()
+    with pytest.raises(ValueError):
+        oracle.expert_hidden(inp["x"], T, inp["W1"][0], inp["W3"][0], act, wdt,
+                             W1s=sc["W1"][0] if sc else None, W3s=sc["W3"][0] if sc else None)

@@ -192,3 +192,21 @@ def test_mxfp4_down_projection_block_sign_flip():
     hq = _mx_fp8_dequant(h.astype(np.float32))
     part = hq[:, :32] @ W2[2][:32]
     assert np.abs(out - out2 - 2 * part).max() <= 1e-12 * np.abs(out).max()
+
+
+def test_mxfp4_expert_hidden_is_dense_swiglu():
+    # unrounded SwiGLU output of each token through one MXFP4 expert against
+    # numpy matmuls on the MX FP8 activations and MX FP4 weights decoded by
+    # independent code
+    T, d, f = 10, 128, 64
+    rng = np.random.default_rng(8)
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    W1 = _mxfp4_weights((rng.standard_normal((d, f)) * 0.02).astype(np.float32))
+    W3 = _mxfp4_weights((rng.standard_normal((d, f)) * 0.02).astype(np.float32))
+    xq = _mx_fp8_dequant(x.float().numpy())
+    a, b = xq @ W1[2], xq @ W3[2]
+    ref = a / (1.0 + np.exp(-a)) * b
+    for t in range(T):
+        h = oracle.expert_hidden(xb, t, W1[0], W3[0], ORC_BF16, ORC_MXFP4, W1s=W1[1], W3s=W3[1])
+        assert np.abs(h - ref[t]).max() <= 1e-12 * np.abs(ref[t]).max()
