@@ -105,6 +105,11 @@ bool supported_shape(const moe_problem* p) {
   // activation element bytes of the GEMM operands (FP8 and MX FP8: 1)
   const int64_t es = p->w_dtype == MOE_F32 ? 4 : (p->w_dtype == MOE_BF16 ? 2 : 1);
   const int64_t lim = 1ll << 31;
+  // FP8: the GEMMs stage a tile's weight block scales for the whole
+  // contraction in LDS (at most kWscMax blocks of 128)
+  if (p->w_dtype == MOE_FP8_E4M3 &&
+      (p->d / 128 > moe::kWscMax || p->f / 128 > moe::kWscMax))
+    return false;
   return p->T * p->d * es < lim && gemm_rows(*p) * p->f * es < lim &&
          weight_matrix_bytes(p->w_dtype, p->d, p->f) < lim;
 }
@@ -411,9 +416,11 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   moe::GemmArgs g1{};
   g1.A = q8 ? at<uint8_t>(ws, L.xq) : static_cast<const uint8_t*>(x);
   g1.a_row_bytes = p->d * (q8 ? 1 : esize(p->act_dtype));
+  g1.a_bytes = p->T * g1.a_row_bytes;
   g1.gather = slot_token;
   g1.sa = q8 ? at<float>(ws, L.sx) : nullptr;  // (MX: E8M0 bytes)
   g1.sa_stride = static_cast<int>(fp8_scale_stride(p->d));
+  g1.sa_bytes = fp8 ? static_cast<int64_t>(L.hs - L.sx) : 0;  // the x scale region
   g1.B0 = static_cast<const uint8_t*>(W1t);
   g1.B1 = static_cast<const uint8_t*>(W3t);
   g1.sb0 = static_cast<const float*>(W1s);
@@ -441,9 +448,11 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   moe::GemmArgs g2{};
   g2.A = at<uint8_t>(ws, L.h);
   g2.a_row_bytes = p->f * (q8 ? 1 : esize(p->act_dtype));
+  g2.a_bytes = static_cast<int64_t>(L.y - L.h);  // the h region
   g2.gather = nullptr;
   g2.sa = q8 ? at<float>(ws, L.hs) : nullptr;
   g2.sa_stride = static_cast<int>(fp8_scale_stride(p->f));
+  g2.sa_bytes = fp8 ? static_cast<int64_t>(L.h - L.hs) : 0;  // the h scale region
   g2.B0 = static_cast<const uint8_t*>(W2t);
   g2.B1 = nullptr;
   g2.sb0 = static_cast<const float*>(W2s);

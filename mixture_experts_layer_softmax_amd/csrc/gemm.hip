@@ -39,6 +39,7 @@
 
 #include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 namespace moe {
 
@@ -89,7 +90,11 @@ struct Geo {
   static constexpr int SGROUP = 4;
   static constexpr int SRING_BUFS = 3;
   static constexpr int SRING = (DT == kFP8) ? SRING_BUFS * SA_DMA * 1024 : 0;
-  static constexpr int NS0 = (kLdsBytes - RED - SRING) / STAGE;
+  // FP8: the tile's weight block scales for the whole contraction, two
+  // columns of kWscMax floats (W1 and W3 of the tile's 128 f, or the two
+  // 128-column blocks of a W2 tile), staged once per task
+  static constexpr int WSC = (DT == kFP8) ? 2 * kWscMax * 4 : 0;
+  static constexpr int NS0 = (kLdsBytes - RED - SRING - WSC) / STAGE;
   // small tiles (decode: HBM bound) keep more stages in flight; 16-row MX
   // tiles are small enough that two workgroups of 4 stages share a CU, which
   // streams better than one of 8 (one refills while the other starts a task)
@@ -102,7 +107,7 @@ struct Geo {
   static constexpr int EPI =  // output staging, one pass per wave row
       (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : YES);
   static constexpr int RING = NS * STAGE;
-  static constexpr int LDS = (RING > EPI ? RING : EPI) + RED + SRING;
+  static constexpr int LDS = (RING > EPI ? RING : EPI) + RED + SRING + WSC;
   static_assert(NS >= 2, "at least two LDS stages");
   // a scale group's buffer is refilled with the DMA of stage SGROUP * g,
   // issued NS - 1 stages ahead; the group that used it last (three groups
@@ -149,6 +154,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef MOE_W
 }
 
+// wait_vmcnt with a compile-time count
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // s_waitcnt lgkmcnt(0): every LDS read of this wave has returned (vmcnt
 // and expcnt fields at their maxima, so they do not wait).
 __device__ __forceinline__ void wait_lgkmcnt0() {
@@ -161,6 +173,22 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 }
 __device__ __forceinline__ void dma4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
+
+// The same 16-byte direct load through a buffer resource (base, extent):
+// lane L reads voff bytes past the base (zeros past the extent) and writes
+// the wave's LDS base + 16 L.  The buffer form keeps the compiler's LDS wait
+// counts exact: it treats the global form as a possible LDS access of its
+// own, and then makes every LDS wait behind one in flight a wait for all.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  // word 3: gfx9 raw-buffer flags (32-bit data format, no swizzle)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(min(bytes, int64_t{0x7fffffff})),
+                                           0x00020000);
+}
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
 }
 
 // SiLU with the hardware exponential and reciprocal (about 2 ulp in fp32;
@@ -331,13 +359,14 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
   // FP8: this lane's A-row scale row (padded to sa_stride floats, a multiple
   // of 4, so that a scale group is one aligned 16-byte piece), and the scale
   // ring: group buffer b holds [SA_DMA * 64 rows][4 stages] floats
-  const float* sa_src = g.sa;
+  uint32_t sa_off = 0;  // byte offset of that row in g.sa
   float* sring = reinterpret_cast<float*>(lds + (G::RING > G::EPI ? G::RING : G::EPI) + G::RED);
+  float* wsc = sring + G::SRING / 4;  // FP8 weight block scales [2][kWscMax]
   const bool scale_dma = DT == kFP8 && wave < G::SA_DMA;
   if constexpr (DT == kFP8) {
     const int rr = min(wave * 64 + lane, rows - 1);
     const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(row0 + rr);
-    sa_src = g.sa + src * g.sa_stride;
+    sa_off = static_cast<uint32_t>(src * g.sa_stride * 4);
   }
   // MX: E8M0 scale dwords of this lane (4 blocks of 32 = one stage).
   // Scale DMA number c < SA_DMA covers activation rows 64c.. ([rows][K/32]
@@ -371,6 +400,14 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
     }
   }
 
+  // buffer resources of the activation rows, this expert's weight rows and
+  // (FP8) the activation-row scales
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.A, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb0 = buffer_rsrc(b0, w_bytes), rb1 = buffer_rsrc(b1, w_bytes);
+  const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(g.sa, DT == kFP8 ? g.sa_bytes : 0);
+  auto dma_a = [&](uint32_t off, void* dst) { dma16b(ra, off, dst); };
+  auto dma_b = [&](bool up, uint32_t off, void* dst) { dma16b(up ? rb1 : rb0, off, dst); };
+
 // DMA of stage KS: the activation rows (and FP8 row scales) when DO_A, the
 // weight rows when DO_B
 #define MOE_ISSUE_PART(KS, DO_A, DO_B)                                                   \
@@ -380,18 +417,18 @@ do {                                                                            
   if (DO_A) {                                                                          \
     _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                \
       const int q = wave + NW * j;                                                     \
-      if (G::ABLK % NW == 0 || q < G::ABLK) dma16(g.A + (oa[j] + ko_), st_ + q * 1024); \
+      if (G::ABLK % NW == 0 || q < G::ABLK) dma_a(oa[j] + ko_, st_ + q * 1024);          \
     }                                                                                  \
     if (DT == kFP8 && scale_dma && (KS) % G::SGROUP == 0)                              \
-      dma16(sa_src + (KS), sring + ((KS) / G::SGROUP) % G::SRING_BUFS * (G::SA_DMA * 256) \
-                               + wave * 256);                                          \
+      dma16b(rsa, sa_off + (KS) * 4,                                                   \
+             sring + ((KS) / G::SGROUP) % G::SRING_BUFS * (G::SA_DMA * 256) + wave * 256);  \
   }                                                                                    \
   if (DO_B) {                                                                          \
     const uint32_t kw_ = static_cast<uint32_t>(KS) * KRBW;                             \
     _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                \
       const int q = wave + NW * j;                                                     \
       if (G::BBLK % NW == 0 || q < G::BBLK)                                            \
-        dma16(((up_mask >> j) & 1u ? b1 : b0) + (ob[j] + kw_), st_ + BM * KRB + q * 1024); \
+        dma_b((up_mask >> j) & 1u, ob[j] + kw_, st_ + BM * KRB + q * 1024);              \
     }                                                                                  \
     if (MX) {                                                                          \
       _Pragma("unroll") for (int u = 0; u < G::SCW; ++u) {                             \
@@ -404,26 +441,30 @@ do {                                                                            
 } while (0)
 #define MOE_ISSUE(KS) MOE_ISSUE_PART(KS, true, true)
 
-  // FP8: the weight block scales of this tile are wave-uniform and
-  // read-only; they are loaded through the scalar cache (constant address
-  // space) one k-step ahead, off the vector-memory counter that orders the
-  // DMA ring.
-  typedef __attribute__((address_space(4))) const float cfloat;
-  const cfloat* sbp0 = nullptr;
-  const cfloat* sbp1 = nullptr;
-  float sb_cur0 = 0.f, sb_cur1 = 0.f, sb_nxt0 = 0.f, sb_nxt1 = 0.f;
+  // FP8: the weight block scales of this tile are read once per task, by
+  // the whole workgroup, into two LDS columns: W1 and W3 of block n0 / 256
+  // (phase 1), or blocks n0 / 128 and n0 / 128 + 1 (phase 2; a block past
+  // the last is clamped to it, and feeds only columns that are never
+  // stored).  Each k-step then reads its scale from LDS: no scalar loads
+  // (which would make every LDS wait in the loop a wait for all) and no
+  // vector loads among the DMAs.  Wave wn reads column wsc_col.
+  constexpr int WSCU = (2 * kWscMax + kThreads - 1) / kThreads;  // entries per thread
+  float wsc_v[WSCU];
+  int wsc_col = 0;
   if constexpr (DT == kFP8) {
-    // the scale block of this wave's columns; waves whose columns all lie
-    // past N (the last n-tile of a ragged N) are clamped to the last block,
-    // so the scalar loads stay inside the expert's scale rows (their
-    // results feed only columns that are never stored)
-    const int nb = min(nblocks - 1, (PHASE == 1) ? static_cast<int>(n0 / 256)  // 128 f per tile
-                                                 : static_cast<int>((n0 + wn * WTN) / 128));
-    const int64_t base = static_cast<int64_t>(e) * kblocks * nblocks + nb;
-    sbp0 = (const cfloat*)(g.sb0) + base;
-    sbp1 = (PHASE == 1) ? (const cfloat*)(g.sb1) + base : sbp0;
-    sb_nxt0 = sbp0[0];
-    sb_nxt1 = (PHASE == 1) ? sbp1[0] : 0.f;
+    wsc_col = (PHASE == 1) ? 0 : (wn * WTN) / 128;
+#pragma unroll
+    for (int u = 0; u < WSCU; ++u) {
+      wsc_v[u] = 0.f;
+      const int idx = tid + kThreads * u;  // column idx / kWscMax, block idx % kWscMax
+      const int c = idx / kWscMax, kb = idx % kWscMax;
+      if (c < 2 && kb < kblocks) {
+        const int nb = (PHASE == 1) ? static_cast<int>(n0 / 256)
+                                    : min(nblocks - 1, static_cast<int>(n0 / 128) + c);
+        const float* src = (PHASE == 1 && c == 1) ? g.sb1 : g.sb0;
+        wsc_v[u] = src[(static_cast<int64_t>(e) * kblocks + kb) * nblocks + nb];
+      }
+    }
   }
 
   f32x4 acc[TM][TN];
@@ -435,8 +476,92 @@ do {                                                                            
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < ksteps) MOE_ISSUE(p);
+  if constexpr (DT == kFP8) {
+    // (the previous task's reads of these columns ended before its epilogue
+    // barrier; the first stage barrier below publishes the new ones)
+#pragma unroll
+    for (int u = 0; u < WSCU; ++u)
+      if (tid + kThreads * u < 2 * kWscMax) wsc[tid + kThreads * u] = wsc_v[u];
+    wait_lgkmcnt0();
+  }
 
-  if constexpr (SCHED == 2) {
+  if constexpr (SCHED == 4) {
+    // Two MFMA k-steps per stage (128-byte rows, two stages), the second
+    // k-step's fragments read while the first one's MFMAs run: row by row
+    // into a second weight-fragment set and into the activation fragment
+    // the row's MFMAs have just consumed.  Only the first k-step's reads
+    // after each stage barrier are exposed.  The next stage's DMA goes out
+    // one instruction per MFMA row of the first k-step.
+    static_assert(DT == kBF16 && KRB == 128 && NS == 2, "bf16, 128-byte rows, two stages");
+    static_assert(G::ABLK % NW == 0 && G::BBLK % NW == 0, "every wave issues AW + BW DMAs");
+    static_assert(G::AW + G::BW <= TM, "one DMA per MFMA row");
+    // fragment j / i of a k-step: base + 16 rows further (the swizzle key of
+    // row r + 16 equals that of row r)
+    const int rw0 = BM * KRB + swz<KRB>(wn * WTN + l16, lg);
+    const int rw1 = BM * KRB + swz<KRB>(wn * WTN + l16, 4 + lg);
+    const int rx0 = swz<KRB>(wm * WTM + l16, lg);
+    const int rx1 = swz<KRB>(wm * WTM + l16, 4 + lg);
+    auto main_loop = [&](auto compute_c) {
+      constexpr bool kCompute = decltype(compute_c)::value;
+      bf16x8 xf[TM], wa[TN], wb[TN];
+      for (int ks = 0; ks < ksteps; ++ks) {
+        wait_vmcnt_c<0>();  // own loads of stage ks (the only stage in flight)
+        ring_barrier();     // everyone's; and stage ks - 1's slot is free
+        if (ks == k_pull) kpull();
+        const bool refill = ks + 1 < ksteps;
+        const uint8_t* St = lds + (ks & 1) * G::STAGE;
+        uint8_t* st_n = lds + ((ks + 1) & 1) * G::STAGE;
+        const uint32_t ko_n = static_cast<uint32_t>(ks + 1) * KRB;
+        if constexpr (kCompute) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            wa[j] = *reinterpret_cast<const bf16x8*>(St + rw0 + 16 * j * KRB);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            xf[i] = *reinterpret_cast<const bf16x8*>(St + rx0 + 16 * i * KRB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (kCompute) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[j], xf[i], acc[i][j], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (refill) {
+            if (i < G::AW) {
+              dma16b(ra, oa[i] + ko_n, st_n + (wave + NW * i) * 1024);
+            } else if (i < G::AW + G::BW) {
+              const int u = i - G::AW;
+              dma16b((up_mask >> u) & 1u ? rb1 : rb0, ob[u] + ko_n,
+                     st_n + BM * KRB + (wave + NW * u) * 1024);
+            }
+          }
+          if constexpr (kCompute) {
+            if (i < TN) wb[i] = *reinterpret_cast<const bf16x8*>(St + rw1 + 16 * i * KRB);
+            xf[i] = *reinterpret_cast<const bf16x8*>(St + rx1 + 16 * i * KRB);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (kCompute) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[j], xf[i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    };
+    if (wm * WTM < rows)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+  } else if constexpr (SCHED == 2) {
     // Interleaved DMA: each k-step of a stage reads its fragments, then runs
     // its MFMAs with one DMA instruction of the next stage between every
     // few of them (the activation rows' DMAs with the first k-step, the
@@ -482,11 +607,11 @@ do {                                                                            
           if (kk == 0) {
             const int q = wave + NW * u;
             if (refill && u < G::AW && (G::ABLK % NW == 0 || q < G::ABLK))
-              dma16(g.A + (oa[u] + ko_n), st_n + q * 1024);
+              dma_a(oa[u] + ko_n, st_n + q * 1024);
           } else {
             const int q = wave + NW * u;
             if (refill && u < G::BW && (G::BBLK % NW == 0 || q < G::BBLK))
-              dma16(((up_mask >> u) & 1u ? b1 : b0) + (ob[u] + static_cast<uint32_t>(kn) * KRBW),
+              dma_b((up_mask >> u) & 1u, ob[u] + static_cast<uint32_t>(kn) * KRBW,
                     st_n + BM * KRB + q * 1024);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -589,13 +714,10 @@ do {                                                                            
     constexpr bool kSplitDma = (DT == kBF16) && (KRB / 64 == 2);
     const bool refill = ks + NS - 1 < ksteps;
     if (refill) MOE_ISSUE_PART(ks + NS - 1, true, !kSplitDma);
+    float sb_cur0 = 0.f, sb_cur1 = 0.f;  // FP8 weight block scales of this k-step
     if constexpr (DT == kFP8) {
-      sb_cur0 = sb_nxt0;
-      sb_cur1 = sb_nxt1;
-      if (ks + 1 < ksteps) {
-        sb_nxt0 = sbp0[static_cast<int64_t>(ks + 1) * nblocks];
-        if (PHASE == 1) sb_nxt1 = sbp1[static_cast<int64_t>(ks + 1) * nblocks];
-      }
+      sb_cur0 = wsc[wsc_col * kWscMax + ks];
+      if (PHASE == 1) sb_cur1 = wsc[kWscMax + ks];
     }
     const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
     const uint8_t* Bb = Ab + BM * KRB;
@@ -911,6 +1033,10 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
 
   const int tid = threadIdx.x;
   const uint64_t clk0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
+  // (the clock reads are scalar-memory ops: wait for them here, so that no
+  // scalar load stays in flight through the main loops, where it would force
+  // every LDS wait there to wait for all LDS reads)
+  wait_lgkmcnt0();
 
   // XCD-aware work queue.  Each workgroup reads the XCD it runs on from the
   // XCC_ID hardware register and shares that XCD's L2 with the workgroups
@@ -944,7 +1070,11 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
     int next_v = -1;
     const int mt = task / NT;
     const int nt = task - mt * NT;
-    const uint64_t t_start = g.task_log ? __builtin_amdgcn_s_memrealtime() : 0;
+    uint64_t t_start = 0;
+    if (g.task_log) {
+      t_start = __builtin_amdgcn_s_memrealtime();
+      wait_lgkmcnt0();
+    }
     gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_, SCHED>(
         g, mt, nt, -1, -1,
         [&] {
@@ -1171,13 +1301,16 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
     return f(Variant<DT, P, BM_, BN_, WM_, WN_ __VA_OPT__(, ) __VA_ARGS__>{});
   MOE_V(kBF16, 1, 256, 0, 256, 2, 4)
   MOE_V(kBF16, 2, 256, 0, 256, 2, 4)
-  // measured alternatives of the 256 x 256 schedule (both slower on the
-  // prefill and skewed layers): 3 = DMA interleaved with the MFMAs,
-  // 4 = ping-pong of the two waves of each SIMD
+  // measured alternatives of the 256 x 256 schedule (slower, or no faster,
+  // on the prefill and skewed layers): 3 = DMA interleaved with the MFMAs,
+  // 4 = ping-pong of the two waves of each SIMD, 5 = the second k-step's
+  // fragments read during the first one's MFMAs
   MOE_V(kBF16, 1, 256, 3, 256, 2, 4, 128, 2)
   MOE_V(kBF16, 2, 256, 3, 256, 2, 4, 128, 2)
   MOE_V(kBF16, 1, 256, 4, 256, 2, 4, 128, 1)
   MOE_V(kBF16, 2, 256, 4, 256, 2, 4, 128, 1)
+  MOE_V(kBF16, 1, 256, 5, 256, 2, 4, 128, 4)
+  MOE_V(kBF16, 2, 256, 5, 256, 2, 4, 128, 4)
   MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 2, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 1, 128, 1, 256, 1, 4)

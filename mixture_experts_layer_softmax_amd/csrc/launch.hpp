@@ -19,6 +19,10 @@ inline int permute_chunk(long long n) {
 
 constexpr int kQueueWords = 16;  // 8 per-XCD work-queue counters per GEMM
 
+// Largest number of 128-element contraction blocks of an FP8 GEMM (the
+// kernel stages a tile's weight block scales in LDS): d, f <= 32768.
+constexpr int kWscMax = 256;
+
 // Expert m-tile map written by the scan kernel: tile i covers slots
 // [row0[i], row0[i] + rows[i]) of expert e[i].  n_mtiles is the number of
 // valid entries; queue[kQueueWords] are the per-XCD work-queue counters of
@@ -39,10 +43,12 @@ struct GemmArgs {
   // activation operand: rows of K elements
   const uint8_t* A;
   int64_t a_row_bytes;
+  int64_t a_bytes;        // bytes of the buffer A points into (its rows' extent)
   const int32_t* gather;  // row index table (slot -> token), or null (row = slot)
   const float* sa;        // FP8: [rows][sa_stride] scales of A rows (K/128 used); MX: E8M0
                           // bytes [rows][K/32]
   int sa_stride;          // FP8: floats per A-row scale row, a multiple of 4
+  int64_t sa_bytes;       // FP8: bytes of the buffer sa points into
   // weight operand(s): [E][N][K] (contraction axis contiguous)
   const uint8_t* B0;      // W1t (phase 1) or W2t (phase 2)
   const uint8_t* B1;      // W3t (phase 1)
