@@ -337,10 +337,16 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
     _say(f"{cfg.name}: drawing inputs")
     inp = make_inputs(cfg, device="cuda")
     t_pack = time.perf_counter()
-    packed = B.pack_weights(inp)
+    if args.stated_weights:  # the layouts the workload states, read without a pack
+        packed = {"W1t": inp["W1"], "W3t": inp["W3"], "W2t": inp["W2"]}
+        packed.update({k: inp[k] for k in ("W1s", "W3s", "W2s") if k in inp})
+        layout = B.MOE_W_KN
+    else:
+        packed = B.pack_weights(inp)
+        layout = B.MOE_W_NK
     torch.cuda.synchronize()
     pack_s = time.perf_counter() - t_pack
-    p = B.problem_of(cfg, block_m=args.block_m)
+    p = B.problem_of(cfg, block_m=args.block_m, w_layout=layout)
     if args.ring:
         ws = torch.empty(B.ring_workspace_size(p), dtype=torch.uint8, device="cuda")
     else:
@@ -445,7 +451,7 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
     # layers), for the parity sample below
     out32 = None
     if not args.no_cpu_baseline and cfg.out_dtype != 0 and not args.ring:
-        p32 = B.problem_of(cfg, block_m=args.block_m, out_dtype=0)
+        p32 = B.problem_of(cfg, block_m=args.block_m, out_dtype=0, w_layout=layout)
         out32 = B.out_tensor(cfg, out_dtype=0)
         step(None, out32, p32)
         torch.cuda.synchronize()
@@ -464,7 +470,8 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
                    "gemms": "one launch, h ring" if args.ring else "two launches"},
         "roofline": roof, "cpu_baseline": cpu, "stages_ms": stage_ms, "layer": layer,
         "sustained_clock_mhz": sustained, "parity_sample": parity,
-        "weight_pack_ms": pack_s * 1e3,
+        "weight_pack_ms": None if args.stated_weights else pack_s * 1e3,
+        "weights": "stated [K][N] layout, no pack" if args.stated_weights else "packed [N][K]",
     }
     del inp, packed, ws, out, out32
     _free(torch)
@@ -491,6 +498,9 @@ def main():
                     help="measure only --workload (by default the other stated workloads "
                          "follow the headline one, each in a block of its own)")
     ap.add_argument("--block-m", type=int, default=0, help="expert tile height (0 = auto)")
+    ap.add_argument("--stated-weights", action="store_true",
+                    help="pass the weights in the layouts the workloads state ([E][d][f], "
+                         "[E][f][d]) instead of packing them once")
     ap.add_argument("--ring", action="store_true",
                     help="time moe_forward_ring (both GEMMs in one launch, h in a bounded ring)")
     ap.add_argument("--counter-summary", metavar="CSV",

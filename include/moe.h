@@ -79,10 +79,15 @@ typedef enum {
  * output columns: W1 and W3 are K = d by N = f, W2 is K = f by N = d).
  *   MOE_W_KN: row-major [K][N] per expert, the layout the workloads state
  *             (W1, W3 [E+S][d][f]; W2 [E+S][f][d]); FP8 codes the same, with
- *             [E+S][K/128][N/128] fp32 block scales.  Not defined for MXFP4.
+ *             [E+S][K/128][N/128] fp32 block scales.  moe_forward reads it as
+ *             is for F32, BF16 and FP8 weights (the GEMMs stage k-rows of the
+ *             weights in LDS and transpose them on the fragment read), with
+ *             the same results bit for bit as MOE_W_NK; measured about 30 %
+ *             slower per call than the packed layout on the bf16 prefill
+ *             layer.  Not defined for MXFP4.
  *   MOE_W_NK: [N][K] per expert (contraction axis contiguous), the layout
- *             moe_pack_weight writes; MXFP4 codes [N][K/2] with their E8M0
- *             scales packed by moe_pack_weight. */
+ *             moe_pack_weight writes once, the faster one to read; MXFP4 codes
+ *             [N][K/2] with their E8M0 scales packed by moe_pack_weight. */
 typedef enum {
     MOE_W_KN = 0,
     MOE_W_NK = 1
@@ -257,7 +262,7 @@ moe_status moe_quantize_mx(int64_t rows, int64_t cols, const void *x_bf16,
  * element, the E8M0 scales, (E + n_shared)*d*f/32 bytes, not included). */
 moe_status moe_weight_bytes(const moe_problem *p, size_t *bytes);
 
-/* One-time weight re-layout (untimed, done when weights are loaded): each
+/* Optional one-time weight re-layout (untimed, done when weights are loaded): each
  * expert matrix given as [K][N] (W1, W3: [d][f]; W2: [f][d], the stated
  * layouts) is written as its transpose [N][K], so that the contraction axis
  * is contiguous for the MFMA operand loads.  src and dst must not overlap.
@@ -295,13 +300,13 @@ moe_status moe_pack_weight(int32_t E, int64_t K, int64_t N, int32_t elem_bytes,
  *   out     [T][d]       out_dtype
  *   ws/ws_bytes          workspace of at least moe_workspace_size()
  *   dbg                  NULL, or device buffers receiving the routing used.
- * Kernels enqueued: route (logits, top-k), FP8 / MX FP8 quantisation of x
- * (FP8 and MXFP4 layers),
- * histogram, scan + tile map, scatter, grouped W1/W3 GEMM + SwiGLU, grouped
- * W2 GEMM, combine.
+ * Kernels enqueued: route (logits, top-k; on FP8 and MXFP4 layers the same
+ * pass over x writes its FP8 / MX FP8 codes and scales), histogram, scan +
+ * tile map, scatter, grouped W1/W3 GEMM + SwiGLU, grouped W2 GEMM, combine.
  * Errors: MOE_ERR_INVALID_ARG (bad problem, NULL operand), MOE_ERR_UNSUPPORTED
  * (shape or layout the kernels do not cover, e.g. MOE_W_KN with MXFP4
- * weights), MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP (a launch failed; the
+ * weights, or FP8 weights with d or f above 32768), MOE_ERR_WORKSPACE_TOO_SMALL,
+ * MOE_ERR_HIP (a launch failed; the
  * HIP code is kept for moe_last_hip_error).  All are returned before
  * anything is enqueued except MOE_ERR_HIP, after which the stream may hold
  * the kernels launched before the failing one. */

@@ -78,8 +78,12 @@ bool valid_problem(const moe_problem* p) {
   return true;
 }
 
-// Weight layouts the GEMM kernels read: [N][K] (packed) for every dtype.
-bool supported_layout(const moe_problem& p) { return p.w_layout == MOE_W_NK; }
+// Weight layouts the GEMM kernels read: [N][K] (packed) for every dtype, and
+// the stated [K][N] for F32, BF16 and FP8 weights (k-row weight tiles read
+// with transposing LDS loads); MXFP4 codes are packed K-major by definition.
+bool supported_layout(const moe_problem& p) {
+  return p.w_layout == MOE_W_NK || p.w_dtype != MOE_MXFP4;
+}
 
 // Bytes per element of Y, the expert outputs per slot: fp32, except bf16 for
 // MXFP4 weights (their 5e-2 tolerance leaves room for the rounding, and Y is
@@ -431,7 +435,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g1.sc = q8 ? at<float>(ws, L.hs) : nullptr;
   g1.sc_stride = static_cast<int>(fp8_scale_stride(p->f));
   g1.tm = tm;
-  g1.n_tiles_n = static_cast<int>(ceil_div(2 * p->f, moe::gemm_tile_n(1, gdt, L.bm)));
+  const bool wkn = p->w_layout == MOE_W_KN;
+  g1.n_tiles_n = static_cast<int>(ceil_div(2 * p->f, moe::gemm_tile_n(1, gdt, L.bm, wkn)));
   g1.queue_idx = 0;
   g1.group_m = group_m(*p, L.bm);
   g1.clock = dbg ? dbg->gemm_clock : nullptr;
@@ -439,7 +444,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g1.task_log = dbg ? dbg->task_log : nullptr;
   g1.task_log_capacity = dbg ? dbg->task_log_capacity : 0;
   if (!ring) {
-    st = from_code(moe::launch_gemm(1, gdt, L.bm, g1, stream));
+    st = from_code(moe::launch_gemm(1, gdt, L.bm, wkn, g1, stream));
     if (st != MOE_OK) return st;
     mark(4);
   }
@@ -462,7 +467,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g2.C = at<uint8_t>(ws, L.y);
   g2.sc = nullptr;
   g2.tm = tm;
-  g2.n_tiles_n = static_cast<int>(ceil_div(p->d, moe::gemm_tile_n(2, gdt, L.bm)));
+  g2.n_tiles_n = static_cast<int>(ceil_div(p->d, moe::gemm_tile_n(2, gdt, L.bm, wkn)));
   g2.queue_idx = 1;
   g2.group_m = g1.group_m;
   // Y far larger than the 256 MB MALL is read back from HBM by the combine
@@ -475,7 +480,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g2.task_log = g1.task_log ? g1.task_log + 4ll * g1.task_log_capacity : nullptr;
   g2.task_log_capacity = g1.task_log_capacity;
   if (!ring) {
-    st = from_code(moe::launch_gemm(2, gdt, L.bm, g2, stream));
+    st = from_code(moe::launch_gemm(2, gdt, L.bm, wkn, g2, stream));
     if (st != MOE_OK) return st;
   } else {
     // both GEMMs in one launch; h lives in the ring, Y in full

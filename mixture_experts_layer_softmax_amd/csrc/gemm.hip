@@ -131,6 +131,38 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * KRB + ((c ^ swz_key<KRB>(r)) << 4);
 }
 
+// Weight tiles of the stated [K][N] layout ("k-row" tiles): a stage holds
+// KS contraction rows of the tile's columns, HB bytes per row (per half:
+// phase 1 keeps the tile's W1 and W3 columns in two halves).  16-byte chunk
+// c of row k is stored at chunk c ^ kn_key(k), a key chosen (with a model of
+// the 64 banks) so that the transposing fragment reads below -- 16 or 32
+// rows at a time -- touch every bank equally often.
+template <int ES, int HB>
+__device__ __forceinline__ int kn_key(int k) {
+  if constexpr (ES == 2) return HB >= 256 ? ((k << 2) ^ (k >> 2)) : (k ^ (k >> 1));
+  else if constexpr (ES == 1) return k ^ (k >> 2) ^ (k >> 3);
+  else return k;
+}
+template <int ES, int HB>
+__device__ __forceinline__ int kn_off(int k, int byte) {
+  return k * HB + ((((byte >> 4) ^ kn_key<ES, HB>(k)) & (HB / 16 - 1)) << 4) + (byte & 15);
+}
+typedef __attribute__((ext_vector_type(4))) short v4i16;
+typedef __attribute__((ext_vector_type(2))) int v2i32;
+#define MOE_LDS3 __attribute__((address_space(3)))
+// gfx950 transposing LDS reads.  Measured lane layout (16-lane groups, each
+// lane addressing 8 bytes): the 16-bit form gives lane i element i % 4 of
+// lane 4j + i / 4's 4 elements as its element j; the 8-bit form gives lane i
+// byte i % 8 of lane 2j + i / 8's 8 bytes as its byte j.  So lanes that
+// address 4 (or 8) consecutive columns of rows k0 + m / 4 (or k0 + m / 2)
+// hand every lane 4 (or 8) consecutive rows of one column.
+__device__ __forceinline__ v4i16 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS3 v4i16*)(p));
+}
+__device__ __forceinline__ v2i32 lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MOE_LDS3 v2i32*)(p));
+}
+
 // s_waitcnt vmcnt(n) that leaves expcnt and lgkmcnt alone (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 __device__ __forceinline__ void wait_vmcnt(int n) {
@@ -269,8 +301,8 @@ struct TaskQueue {
 // map) times column tile nt -- the K loop through the LDS ring, then the
 // epilogue.  kpull() runs a few k-steps before the end (the next task's
 // queue request); pre_epi() runs between the main loop and the epilogue.
-template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, int SCHED, class KPull,
-          class PreEpi>
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, int SCHED, bool WKN,
+          class KPull, class PreEpi>
 __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const int nt,
                                           const int64_t arow_base, const int64_t crow_base,
                                           KPull&& kpull,
@@ -285,6 +317,14 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
   static_assert(PHASE == 2 || TN % 2 == 0, "gate/up pairs");
   static_assert(!(DT == kFP8 && PHASE == 1) || BN == 256, "FP8 h groups of 128 f");
   static_assert(!(MX && PHASE == 1) || WTN % 64 == 0, "MX h blocks of 32 f inside one wave");
+  // k-row weight tiles (WKN, the stated [K][N] layout): NH halves (phase 1:
+  // the tile's W1 columns, then its W3 columns) of KSW rows of HB bytes
+  static_assert(!WKN || (!MX && SCHED == 0), "k-row weight tiles: F32, BF16, FP8; default loop");
+  constexpr int NH = (PHASE == 1) ? 2 : 1;
+  constexpr int KSW = KRB / ES;           // contraction rows of a stage
+  constexpr int HB = (BN / NH) * ES;      // bytes of one row of one half
+  constexpr int HALF = KSW * HB;          // bytes of one half
+  static_assert(!WKN || (HB <= 1024 && HALF % 1024 == 0 && HB % 16 == 0), "k-row DMA blocks");
 
   // LDS: NS stages of [BM rows A | BN rows B | BM A-scales (FP8)], reused by
   // the epilogue staging; then (FP8 phase 1) the per-wave row maxima.
@@ -339,6 +379,22 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
 #pragma unroll
   for (int j = 0; j < G::BW; ++j) {
     const int q = wave + NW * j;
+    if constexpr (WKN) {
+      // k-row tile: block q fills 1 KB of half q / (HALF / 1024); lane L
+      // fills row k, physical chunk p of it, from logical chunk p ^ key
+      const int h = q / (HALF / 1024);
+      const int byte = (q % (HALF / 1024)) * 1024 + 16 * lane;
+      const int k = byte / HB, p = (byte % HB) / 16;
+      const int logical = (p ^ kn_key<ES, HB>(k)) & (HB / 16 - 1);
+      const int64_t col0 = (PHASE == 1) ? n0 / 2 : n0;
+      // columns past N (the last n-tile of a ragged N) re-read the last
+      // chunk of the row; they feed only columns that are never stored
+      const int64_t cb = min(col0 * ES + logical * 16, N * ES - 16);
+      ob[j] = static_cast<uint32_t>(k * N * ES + cb);
+      if (h == 1) up_mask |= 1u << j;
+      if (q < G::BBLK) ++my_loads;
+      continue;
+    }
     const int r = q * RPDW + lroww;
     const int logical = lphysw ^ swz_key<KRBW>(r);
     const int64_t n = n0 + r;
@@ -407,6 +463,18 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
   const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(g.sa, DT == kFP8 ? g.sa_bytes : 0);
   auto dma_a = [&](uint32_t off, void* dst) { dma16b(ra, off, dst); };
   auto dma_b = [&](bool up, uint32_t off, void* dst) { dma16b(up ? rb1 : rb0, off, dst); };
+  // weight bytes between consecutive stages: KRBW along a packed row, or KSW
+  // rows of the stated layout
+  const uint32_t w_kstride = WKN ? static_cast<uint32_t>(KSW * N * ES) : KRBW;
+  // k-row tiles: LDS byte offset of the 4 (16-bit) / 8 (8-bit) bytes this
+  // lane addresses for the transposing read of rows k0 + .. of tile column
+  // block cb (16 columns, in the phase-1 combined order)
+  auto kn_addr = [&](int cb_col, int k, int colbyte) {  // (from the stage base)
+    const int blk = cb_col / 16;
+    const int h = (PHASE == 1) ? (blk & 1) : 0;
+    const int c0 = (PHASE == 1) ? (blk >> 1) * 16 : cb_col;
+    return BM * KRB + h * HALF + kn_off<ES, HB>(k, c0 * ES + colbyte);
+  };
 
 // DMA of stage KS: the activation rows (and FP8 row scales) when DO_A, the
 // weight rows when DO_B
@@ -424,7 +492,7 @@ do {                                                                            
              sring + ((KS) / G::SGROUP) % G::SRING_BUFS * (G::SA_DMA * 256) + wave * 256);  \
   }                                                                                    \
   if (DO_B) {                                                                          \
-    const uint32_t kw_ = static_cast<uint32_t>(KS) * KRBW;                             \
+    const uint32_t kw_ = static_cast<uint32_t>(KS) * w_kstride;                        \
     _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                \
       const int q = wave + NW * j;                                                     \
       if (G::BBLK % NW == 0 || q < G::BBLK)                                            \
@@ -733,9 +801,20 @@ do {                                                                            
         if (!compute) continue;
         bf16x8 wf[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          wf[j] = *reinterpret_cast<const bf16x8*>(
-              Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (WKN) {
+            // rows 32 kk + 8 lg + 0..7 of column wn WTN + 16 j + l16
+            const int k0 = kk * 32 + 8 * lg + (l16 >> 2);
+            const v4i16 lo = lds_tr16(Ab + kn_addr(wn * WTN + 16 * j, k0, 8 * (l16 & 3)));
+            const v4i16 hi = lds_tr16(Ab + kn_addr(wn * WTN + 16 * j, k0 + 4, 8 * (l16 & 3)));
+            typedef __attribute__((ext_vector_type(8))) short v8i16;
+            wf[j] = __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1],
+                                                     hi[2], hi[3]});
+          } else {
+            wf[j] = *reinterpret_cast<const bf16x8*>(
+                Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
+          }
+        }
 #define MOE_BF16_ROWS(SKIP)                                                               \
 bf16x8 xf[TM];                                                                          \
 _Pragma("unroll") for (int i = 0; i < TM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>( \
@@ -756,8 +835,16 @@ __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       if (!compute) continue;
       f32x4 wf[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz<KRB>(wn * WTN + 16 * j + l16, lg));
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (WKN) {  // rows 4 lg + u of column wn WTN + 16 j + l16
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            wf[j][u] = *reinterpret_cast<const float*>(
+                Ab + kn_addr(wn * WTN + 16 * j, 4 * lg + u, 4 * l16));
+        } else {
+          wf[j] = *reinterpret_cast<const f32x4*>(Bb + swz<KRB>(wn * WTN + 16 * j + l16, lg));
+        }
+      }
 #define MOE_F32_ROWS(SKIP)                                                                \
 _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
   if (SKIP) break;                                                                      \
@@ -809,10 +896,20 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
       i32x8 wf[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int r = wn * WTN + 16 * j + l16;
-        const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
-        const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
-        wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (WKN) {
+          // rows 32 lg + 0..31 of column wn WTN + 16 j + l16, 8 per read
+          v2i32 t[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            t[rr] = lds_tr8(Ab + kn_addr(wn * WTN + 16 * j, 32 * lg + 8 * rr + (l16 >> 1),
+                                         8 * (l16 & 1)));
+          wf[j] = i32x8{t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
+        } else {
+          const int r = wn * WTN + 16 * j + l16;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(Bb + swz<KRB>(r, 2 * lg + 1));
+          wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
       // this stage's column of the scale group buffer: [row][4 stages]
       const float* sa_st = sring + (ks / G::SGROUP) % G::SRING_BUFS * (G::SA_DMA * 256) +
@@ -1022,7 +1119,7 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
 
 }
 
-template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, int SCHED>
+template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, int SCHED, bool WKN>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   using G = Geo<DT, PHASE, BM, BN, WM, WN, KRB_>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -1075,7 +1172,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
       t_start = __builtin_amdgcn_s_memrealtime();
       wait_lgkmcnt0();
     }
-    gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_, SCHED>(
+    gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_, SCHED, WKN>(
         g, mt, nt, -1, -1,
         [&] {
           if (tid == 0 && own_open) next_v = atomicAdd(&q.counters[q.xcd], 1);
@@ -1223,7 +1320,8 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
           __syncthreads();
         }
       };
-      gemm_task<kBF16, 1, BM, BN, WM, WN, 128, 0>(g1, mt, nt, -1, ring_row, kpull, slot_free);
+      gemm_task<kBF16, 1, BM, BN, WM, WN, 128, 0, false>(g1, mt, nt, -1, ring_row, kpull,
+                                                        slot_free);
       wait_vmcnt(0);  // this wave's h stores are done
       __syncthreads();
       if (tid == 0)
@@ -1234,7 +1332,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
         ring_wait(&r.l1_done[c], min(GM, M - c * GM) * NT1 + r.unreachable, true, r.err,
                   r.poll_limit);
       __syncthreads();
-      gemm_task<kBF16, 2, BM, BN, WM, WN, 128, 0>(g2, mt, nt, ring_row, -1, kpull, [] {});
+      gemm_task<kBF16, 2, BM, BN, WM, WN, 128, 0, false>(g2, mt, nt, ring_row, -1, kpull, [] {});
       __syncthreads();  // (the task's h loads all landed before its last stage)
       if (tid == 0) __hip_atomic_fetch_add(&r.l2_done[c], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1258,12 +1356,12 @@ __global__ __launch_bounds__(WM * WN * 64) void ring_gemm_kernel(GemmArgs g1, Ge
 }
 
 template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB = (DT == kF32 ? 64 : 128),
-          int SCHED = 0>
+          int SCHED = 0, bool WKN = false>
 struct Variant {
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int lds_bytes() { return Geo<DT, PHASE, BM, BN, WM, WN, KRB>::LDS; }
   static int launch(const GemmArgs& a, hipStream_t s) {
-    auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN, KRB, SCHED>;
+    auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN, KRB, SCHED, WKN>;
     static int grid = 0;
     static hipError_t attr_err = hipSuccess;
     static std::once_flag once;
@@ -1359,8 +1457,50 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   return -1;
 }
 
+// Kernel with k-row weight tiles (the stated [K][N] weight layout) per
+// (dtype, phase, tile height): the default shapes.
 template <typename F>
-int dispatch(int phase, int dtype, int bm, F&& f) {
+int dispatch_kn(int phase, int dtype, int bm, F&& f) {
+#define MOE_KN(DT, P, BM_, BN_, WM_, WN_)                                             \
+  if (dtype == DT && phase == P && bm == BM_)                                        \
+    return f(Variant<DT, P, BM_, BN_, WM_, WN_, (DT == kF32 ? 64 : 128), 0, true>{});
+  MOE_KN(kBF16, 1, 256, 256, 2, 4)
+  MOE_KN(kBF16, 2, 256, 256, 2, 4)
+  MOE_KN(kBF16, 1, 128, 128, 2, 2)
+  MOE_KN(kBF16, 2, 128, 128, 2, 2)
+  MOE_KN(kBF16, 1, 64, 128, 1, 4)
+  MOE_KN(kBF16, 2, 64, 128, 1, 4)
+  MOE_KN(kBF16, 1, 32, 128, 1, 4)
+  MOE_KN(kBF16, 2, 32, 128, 1, 4)
+  MOE_KN(kBF16, 1, 16, 256, 1, 4)
+  MOE_KN(kBF16, 2, 16, 256, 1, 4)
+  MOE_KN(kFP8, 1, 256, 256, 2, 4)
+  MOE_KN(kFP8, 2, 256, 256, 2, 4)
+  MOE_KN(kFP8, 1, 128, 256, 2, 4)
+  MOE_KN(kFP8, 2, 128, 256, 2, 4)
+  MOE_KN(kFP8, 1, 64, 256, 1, 4)
+  MOE_KN(kFP8, 2, 64, 128, 1, 4)
+  MOE_KN(kFP8, 1, 32, 256, 2, 2)
+  MOE_KN(kFP8, 2, 32, 128, 1, 4)
+  MOE_KN(kFP8, 1, 16, 256, 1, 4)
+  MOE_KN(kFP8, 2, 16, 128, 1, 4)
+  MOE_KN(kF32, 1, 256, 128, 2, 2)
+  MOE_KN(kF32, 2, 256, 128, 2, 2)
+  MOE_KN(kF32, 1, 128, 128, 2, 2)
+  MOE_KN(kF32, 2, 128, 128, 2, 2)
+  MOE_KN(kF32, 1, 64, 128, 1, 4)
+  MOE_KN(kF32, 2, 64, 128, 1, 4)
+  MOE_KN(kF32, 1, 32, 128, 1, 4)
+  MOE_KN(kF32, 2, 32, 128, 1, 4)
+  MOE_KN(kF32, 1, 16, 128, 1, 4)
+  MOE_KN(kF32, 2, 16, 128, 1, 4)
+#undef MOE_KN
+  return -1;
+}
+
+template <typename F>
+int dispatch(int phase, int dtype, int bm, bool wkn, F&& f) {
+  if (wkn) return dispatch_kn(phase, dtype, bm, f);
   int r = dispatch_var(phase, dtype, bm, variant_choice(), f);
   if (r == -1 && variant_choice() != 0) r = dispatch_var(phase, dtype, bm, 0, f);
   return r;
@@ -1368,12 +1508,12 @@ int dispatch(int phase, int dtype, int bm, F&& f) {
 
 }  // namespace
 
-int launch_gemm(int phase, int dtype, int bm, const GemmArgs& a, hipStream_t s) {
-  return dispatch(phase, dtype, bm, [&](auto v) { return decltype(v)::launch(a, s); });
+int launch_gemm(int phase, int dtype, int bm, bool wkn, const GemmArgs& a, hipStream_t s) {
+  return dispatch(phase, dtype, bm, wkn, [&](auto v) { return decltype(v)::launch(a, s); });
 }
 
-int gemm_tile_n(int phase, int dtype, int bm) {
-  return dispatch(phase, dtype, bm, [&](auto v) { return decltype(v)::tile_n(); });
+int gemm_tile_n(int phase, int dtype, int bm, bool wkn) {
+  return dispatch(phase, dtype, bm, wkn, [&](auto v) { return decltype(v)::tile_n(); });
 }
 
 int launch_gemm_ring(const GemmArgs& g1, const GemmArgs& g2, const RingArgs& r, hipStream_t s) {

@@ -118,15 +118,17 @@ void launch_quant_fp8(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q,
 // MX FP8: blocks of 32 along the row, E4M3 codes + E8M0 scale bytes [rows][cols/32].
 void launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
                      hipStream_t st);
-// Grouped GEMMs.  bm = tile height; returns a hipError_t.
-int launch_gemm(int phase, int dtype, int bm, const GemmArgs& a, hipStream_t s);
+// Grouped GEMMs.  bm = tile height; wkn: weights in the stated [E][K][N]
+// layout (else the packed [E][N][K]); returns a hipError_t (-1: no kernel
+// for this combination).
+int launch_gemm(int phase, int dtype, int bm, bool wkn, const GemmArgs& a, hipStream_t s);
 // Both GEMMs in one launch through the h ring (bf16 weights, bm = 256); g1.C
 // and g2.A point at r.h.  Returns a hipError_t.
 int launch_gemm_ring(const GemmArgs& g1, const GemmArgs& g2, const RingArgs& r, hipStream_t s);
 // Zero n int32 words with a kernel (also inside a captured graph).
 void launch_zero(int32_t* p, int64_t n, hipStream_t s);
 // Column tiles per m-tile for a phase (depends on the kernel variant).
-int gemm_tile_n(int phase, int dtype, int bm);
+int gemm_tile_n(int phase, int dtype, int bm, bool wkn);
 // Y [T*k + S*T][d], fp32 or (y_bf16) bf16.
 void launch_combine(const void* Y, bool y_bf16, const float* w, const int32_t* token_slot,
                     void* out, int T, int d, int k, int S, bool out_bf16, hipStream_t s);

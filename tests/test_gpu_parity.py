@@ -568,28 +568,53 @@ def test_full_size_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16_r", "decode_bf16_r",
-                                  "prefill_fp8_r"])
-def test_stated_layout_weights_match_or_are_refused(name):
+                                  "skewed_bf16_r", "prefill_fp8_r"])
+def test_stated_layout_weights_match_the_oracle(name):
     # weights passed as the workloads state them ([E][d][f], [E][f][d]) with
-    # w_layout MOE_W_KN: the call either computes the layer (checked against
-    # the oracle) or refuses with MOE_ERR_UNSUPPORTED before writing anything;
-    # it never reads them as the packed layout
+    # w_layout MOE_W_KN: the GEMMs read them as k-row tiles (transposing LDS
+    # loads), no pack; the layer must match the oracle, and equal the packed
+    # layout's output bit for bit (the same products in the same order)
     cfg = REDUCED[name]
     say("stated layout", name)
+    inp = gpu_inputs(cfg)
+    ref, _, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
+    out = forward(cfg, inp, None)
+    torch.cuda.synchronize()
+    _outputs_ok(cfg, out, ref, "stated layout")
+    out32 = forward(cfg, inp, None, out_dtype=F32)
+    packed32 = _forward(cfg, inp, out_dtype=F32)
+    torch.cuda.synchronize()
+    _outputs_ok(cfg, out32, ref, "stated layout, fp32 out")
+    assert torch.equal(out32, packed32)
+
+
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("name", ["tiny_fp32", "prefill_bf16_r", "prefill_fp8_r"])
+def test_stated_layout_every_tile_height(name, block_m):
+    # every k-row tile shape equals the packed layout's kernel bit for bit
+    cfg = REDUCED[name]
+    say("stated layout bm", name, block_m)
+    inp = gpu_inputs(cfg)
+    out = forward(cfg, inp, None, out_dtype=F32, block_m=block_m)
+    ref = _forward(cfg, inp, out_dtype=F32, block_m=block_m)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_stated_layout_mxfp4_is_refused():
+    # MXFP4 weights have no stated [K][N] form (their codes are K-major by
+    # definition): MOE_ERR_UNSUPPORTED before anything is written
+    cfg = REDUCED["prefill_mxfp4_r"]
+    say("stated layout mxfp4")
     inp = gpu_inputs(cfg)
     p = B.problem_of(cfg, w_layout=B.MOE_W_KN)
     ws = poisoned_workspace(p)
     out = torch.full((cfg.T, cfg.d), 7.0, device="cuda").to(B.out_tensor(cfg).dtype)
-    try:
+    with pytest.raises(B.MoEError) as e:
         B.forward(cfg, inp, None, out=out, ws=ws)
-    except B.MoEError as e:
-        assert e.code == 2, e
-        torch.cuda.synchronize()
-        assert (out.float() == 7.0).all()
-        return
+    assert e.value.code == 2
     torch.cuda.synchronize()
-    ref, _, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
-    _outputs_ok(cfg, out, ref, "stated layout")
+    assert (out.float() == 7.0).all()
 
 
 @pytest.mark.parametrize("name", ["skewed_bf16_r", "prefill_fp8_r", "prefill_mxfp4_r",
@@ -760,6 +785,10 @@ def test_random_config_parity(cfg, block_m):
     assert np.array_equal(dbg["topk_ids"].view(cfg.T, cfg.k).cpu().numpy(), ref_ids)
     _outputs_ok(cfg, out, ref, f"fp32 out bm={block_m}")
     _outputs_ok(cfg, _forward(cfg, inp, block_m=block_m), ref, "native out")
+    if cfg.w_dtype != MXFP4:  # the stated weight layout gives the same bits
+        kn = forward(cfg, inp, None, out_dtype=F32, block_m=block_m)
+        torch.cuda.synchronize()
+        assert torch.equal(kn, out)
 
 
 # ---------------------------------------------------------------------------
