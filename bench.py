@@ -482,6 +482,38 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
 OTHER_CONFIGS = ["tiny_fp32", "decode_bf16", "skewed_bf16", "prefill_fp8"]
 
 
+def blas_calibration(reps=50):
+    """TFLOP/s of torch.matmul (hipBLASLt) on plain bf16 GEMMs: the prefill
+    layer's W1/W3 stage as one dense GEMM (T*k x d times d x 2f), its W2
+    stage (T*k x f times f x d) and 8192^3; a reference for what a vendor
+    GEMM reaches on the same shapes, without the gather, grouping or
+    SwiGLU."""
+    import torch
+
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, (m, k, n) in {"prefill_w13_dense": (32768, 2048, 4096),
+                            "prefill_w2_dense": (32768, 2048, 2048),
+                            "square_8192": (8192, 8192, 8192)}.items():
+        a = torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16)
+        b = torch.randn((k, n), generator=g, device="cuda").to(torch.bfloat16)
+        for _ in range(10):
+            c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * m * k * n / (ms * 1e-3) / 1e12
+        out[name] = {"m": m, "k": k, "n": n, "ms": ms, "tflops": tf,
+                     "frac_of_bf16_peak": tf / 2516.6}
+        del a, b, c
+    return {"blas_calibration": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,6 +535,9 @@ def main():
                          "[E][f][d]) instead of packing them once")
     ap.add_argument("--ring", action="store_true",
                     help="time moe_forward_ring (both GEMMs in one launch, h in a bounded ring)")
+    ap.add_argument("--blas-calibration", action="store_true",
+                    help="time torch.matmul (hipBLASLt) on plain bf16 GEMMs of the prefill "
+                         "W1/W3 and W2 shapes and on 8192^3, as a reference for the grouped GEMMs")
     ap.add_argument("--counter-summary", metavar="CSV",
                     help="print per-kernel mean counter values of a rocprofv3 --pmc csv (no GPU "
                          "use)")
@@ -518,6 +553,9 @@ def main():
         if not args.no_other_configs and not args.ring and args.workload == "prefill_bf16":
             wls += OTHER_CONFIGS
         print(trace_summary(args.trace_summary, args.warmup, args.steps, wls))
+        return
+    if args.blas_calibration:
+        print(json.dumps(blas_calibration()), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "

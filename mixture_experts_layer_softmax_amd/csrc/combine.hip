@@ -98,7 +98,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ 
     if (OUT_BF16) {
       uint16_t* o = static_cast<uint16_t*>(out) + static_cast<size_t>(t) * d + c;
       auto pk = [](float lo, float hi) {
-        return f32_to_bf16_rne(lo) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+        return f32x2_to_bf16x2_rne(lo, hi);
       };
       __builtin_nontemporal_store(
           u32x4{pk(a0[0], a0[1]), pk(a0[2], a0[3]), pk(a1[0], a1[1]), pk(a1[2], a1[3])},

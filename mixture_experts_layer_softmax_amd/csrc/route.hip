@@ -371,12 +371,10 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
       const int xe = mx_exponent_e4m3(m);
       if (valid && writer) {
         u32x2 c;
-        c.x = c.y = 0u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          c.x |= f32_to_e4m3(__builtin_ldexpf(v[q], -xe)) << (8 * q);
-          c.y |= f32_to_e4m3(__builtin_ldexpf(v[4 + q], -xe)) << (8 * q);
-        }
+        c.x = f32x4_to_e4m3x4(__builtin_ldexpf(v[0], -xe), __builtin_ldexpf(v[1], -xe),
+                              __builtin_ldexpf(v[2], -xe), __builtin_ldexpf(v[3], -xe));
+        c.y = f32x4_to_e4m3x4(__builtin_ldexpf(v[4], -xe), __builtin_ldexpf(v[5], -xe),
+                              __builtin_ldexpf(v[6], -xe), __builtin_ldexpf(v[7], -xe));
         *reinterpret_cast<u32x2*>(gq.q + static_cast<size_t>(t) * d + i) = c;
         if ((il & 31) == 0)
           static_cast<uint8_t*>(gq.s)[static_cast<size_t>(t) * (d / 32) + i / 32] =
@@ -397,17 +395,17 @@ __global__ __launch_bounds__(64 * TG * WS) void gate_kernel(const void* __restri
           for (int c = 0; c < 128 / KB; ++c) {
             const int col = g0 + c * KB + il;
             const u32x4 raw = qraw[r][c];
-            u32x2 cd;
-            cd.x = cd.y = 0u;
+            // (x / sc with the IEEE division: these codes are the stated
+            // recipe's, bit for bit)
+            float v8[8];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              cd.x |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[q] << 16), sc)) << (16 * q);
-              cd.x |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[q] & 0xffff0000u), sc))
-                      << (16 * q + 8);
-              cd.y |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[2 + q] << 16), sc)) << (16 * q);
-              cd.y |= f32_to_e4m3(__fdiv_rn(__uint_as_float(raw[2 + q] & 0xffff0000u), sc))
-                      << (16 * q + 8);
+            for (int q = 0; q < 4; ++q) {
+              v8[2 * q] = __fdiv_rn(__uint_as_float(raw[q] << 16), sc);
+              v8[2 * q + 1] = __fdiv_rn(__uint_as_float(raw[q] & 0xffff0000u), sc);
             }
+            u32x2 cd;
+            cd.x = f32x4_to_e4m3x4(v8[0], v8[1], v8[2], v8[3]);
+            cd.y = f32x4_to_e4m3x4(v8[4], v8[5], v8[6], v8[7]);
             *reinterpret_cast<u32x2*>(gq.q + static_cast<size_t>(t) * d + col) = cd;
           }
           if (il == 0) static_cast<float*>(gq.s)[static_cast<size_t>(t) * gq.s_stride + g0 / 128] = sc;

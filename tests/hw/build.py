@@ -4,7 +4,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PROGRAMS = ["mfma_accumulation"]
+PROGRAMS = ["mfma_accumulation", "fp8_convert"]
 
 
 def build() -> None:
