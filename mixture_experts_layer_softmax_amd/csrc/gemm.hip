@@ -301,8 +301,10 @@ struct TaskQueue {
 // map) times column tile nt -- the K loop through the LDS ring, then the
 // epilogue.  kpull() runs a few k-steps before the end (the next task's
 // queue request); pre_epi() runs between the main loop and the epilogue.
+// LIM (nonzero): the default loop runs the MFMAs of this wave's first LIM
+// fragment rows only.
 template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB_, int SCHED, bool WKN,
-          class KPull, class PreEpi>
+          int LIM = 0, class KPull, class PreEpi>
 __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const int nt,
                                           const int64_t arow_base, const int64_t crow_base,
                                           KPull&& kpull,
@@ -325,6 +327,26 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
   constexpr int HB = (BN / NH) * ES;      // bytes of one row of one half
   constexpr int HALF = KSW * HB;          // bytes of one half
   static_assert(!WKN || (HB <= 1024 && HALF % 1024 == 0 && HB % 16 == 0), "k-row DMA blocks");
+
+  // SCHED bit 4: each wave runs the task in the instantiation for the number
+  // of its fragment rows that hold a valid row (all, half or a quarter of
+  // them), so the last m-tile of an expert runs no MFMAs for most of its
+  // padding.  Every instantiation passes the same barriers.
+  if constexpr ((SCHED & 16) && LIM == 0 && TM >= 4) {
+    const int wave_row = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) / WN;
+    const int valid = __builtin_amdgcn_readfirstlane(g.tm.rows[mt]) - wave_row * WTM;
+    if (valid > 16 * (TM / 2))
+      gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_, SCHED, WKN, TM>(g, mt, nt, arow_base, crow_base,
+                                                                 kpull, pre_epi);
+    else if (valid > 16 * (TM / 4))
+      gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_, SCHED, WKN, TM / 2>(g, mt, nt, arow_base,
+                                                                     crow_base, kpull, pre_epi);
+    else
+      gemm_task<DT, PHASE, BM, BN, WM, WN, KRB_, SCHED, WKN, TM / 4>(g, mt, nt, arow_base,
+                                                                     crow_base, kpull, pre_epi);
+    return;
+  }
+  constexpr int NR = LIM ? LIM : TM;  // fragment rows whose MFMAs run
 
   // LDS: NS stages of [BM rows A | BN rows B | BM A-scales (FP8)], reused by
   // the epilogue staging; then (FP8 phase 1) the per-wave row maxima.
@@ -373,7 +395,12 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
     const int logical = lphys ^ swz_key<KRB>(r);
     const int rr = min(r, rows - 1);  // padding rows re-read a valid row
     const int64_t src = g.gather ? g.gather[row0 + rr] : static_cast<int64_t>(arow + rr);
-    oa[j] = static_cast<uint32_t>(src * g.a_row_bytes + logical * 16);
+    // a block wholly past the tile's last row reads from past the end of
+    // the buffer resource (offset 2^31 + k bytes), which fetches nothing
+    // and returns zeros: no memory traffic for the padding rows, and the
+    // same DMA count in every stage
+    oa[j] = (q * RPD < rows) ? static_cast<uint32_t>(src * g.a_row_bytes + logical * 16)
+                             : 0x80000000u;
     if (q < G::ABLK) ++my_loads;
   }
 #pragma unroll
@@ -816,21 +843,20 @@ do {                                                                            
                 Bb + swz<KRB>(wn * WTN + 16 * j + l16, kk * 4 + lg));
           }
         }
-#define MOE_BF16_ROWS(SKIP)                                                               \
-bf16x8 xf[TM];                                                                          \
-_Pragma("unroll") for (int i = 0; i < TM; ++i) xf[i] = *reinterpret_cast<const bf16x8*>( \
-    Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));                               \
-_Pragma("unroll") for (int i = 0; i < TM; ++i) {                                        \
-  if (SKIP) break;                                                                      \
-  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                        \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0); \
-}                                                                                       \
-/* issue every fragment read of the step before the MFMAs (LDS latency  */              \
-/* then overlaps the MFMAs instead of stalling each pair of fragments)  */              \
-__builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                                \
-__builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-        MOE_BF16_ROWS(false)
-#undef MOE_BF16_ROWS
+        // every fragment read of the step is issued before the MFMAs (LDS
+        // latency then overlaps the MFMAs instead of stalling each pair of
+        // fragments)
+        bf16x8 xf[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+          xf[i] = *reinterpret_cast<const bf16x8*>(Ab + swz<KRB>(wm * WTM + 16 * i + l16, kk * 4 + lg));
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR + TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NR * TN, 0);
       }
     } else if constexpr (DT == kF32) {
       if (!compute) continue;
@@ -916,7 +942,7 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
       const float* sa_st = sring + (ks / G::SGROUP) % G::SRING_BUFS * (G::SA_DMA * 256) +
                            ks % G::SGROUP;
       const float s_b0 = sb_cur0, s_b1 = sb_cur1;
-      // Software pipeline over the TM fragment rows: row i + 1's activation
+      // Software pipeline over the NR fragment rows: row i + 1's activation
       // fragment and row scale are read from LDS while row i's TN block
       // products run on the MFMA, and row i - 1's products are scaled
       // (s_x * s_w, fp32) into the accumulators behind them, so neither the
@@ -934,11 +960,11 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
       f32x4 pp[TN];
       float spg = 0.f, spu = 0.f;
 #pragma unroll
-      for (int i = 0; i <= TM; ++i) {
+      for (int i = 0; i <= NR; ++i) {
         f32x4 pc[TN];
         float scg = 0.f, scu = 0.f;
-        if (i + 1 < TM) load_row(i + 1, xf[(i + 1) & 1], sa[(i + 1) & 1]);
-        if (i < TM) {
+        if (i + 1 < NR) load_row(i + 1, xf[(i + 1) & 1], sa[(i + 1) & 1]);
+        if (i < NR) {
           scg = sa[i & 1] * s_b0;
           scu = sa[i & 1] * s_b1;
 #pragma unroll
@@ -1420,18 +1446,23 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
 #define MOE_V(DT, P, BM_, VAR, BN_, WM_, WN_, ...)                \
   if (dtype == DT && phase == P && bm == BM_ && var == VAR)        \
     return f(Variant<DT, P, BM_, BN_, WM_, WN_ __VA_OPT__(, ) __VA_ARGS__>{});
-  MOE_V(kBF16, 1, 256, 0, 256, 2, 4)
-  MOE_V(kBF16, 2, 256, 0, 256, 2, 4)
+  // SCHED bit 4: MFMAs of the padding rows skipped per wave (2.09 against
+  // 2.14 ms on the skewed layer, 17.49 against 17.54 ms on the FP8 one)
+  MOE_V(kBF16, 1, 256, 0, 256, 2, 4, 128, 16)
+  MOE_V(kBF16, 2, 256, 0, 256, 2, 4, 128, 16)
   // measured alternatives of the 256 x 256 schedule (slower, or no faster,
   // on the prefill and skewed layers): 3 = DMA interleaved with the MFMAs,
   // 4 = ping-pong of the two waves of each SIMD, 5 = the second k-step's
-  // fragments read during the first one's MFMAs
+  // fragments read during the first one's MFMAs, 6 = every fragment row's
+  // MFMAs run
   MOE_V(kBF16, 1, 256, 3, 256, 2, 4, 128, 2)
   MOE_V(kBF16, 2, 256, 3, 256, 2, 4, 128, 2)
   MOE_V(kBF16, 1, 256, 4, 256, 2, 4, 128, 1)
   MOE_V(kBF16, 2, 256, 4, 256, 2, 4, 128, 1)
   MOE_V(kBF16, 1, 256, 5, 256, 2, 4, 128, 4)
   MOE_V(kBF16, 2, 256, 5, 256, 2, 4, 128, 4)
+  MOE_V(kBF16, 1, 256, 6, 256, 2, 4)
+  MOE_V(kBF16, 2, 256, 6, 256, 2, 4)
   MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 2, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 1, 128, 1, 256, 1, 4)
@@ -1444,10 +1475,12 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kBF16, 2, 32, 0, 128, 1, 4)
   MOE_V(kBF16, 1, 16, 0, 256, 1, 4)
   MOE_V(kBF16, 2, 16, 0, 256, 1, 4)
-  MOE_V(kFP8, 1, 256, 0, 256, 2, 4)
+  MOE_V(kFP8, 1, 256, 0, 256, 2, 4, 128, 16)
   // FP8 W2 stores its fp32 Y straight from the accumulators (SCHED bit 3):
   // 5.43 against 5.57 ms on the FP8 prefill layer; on bf16 layers no gain
-  MOE_V(kFP8, 2, 256, 0, 256, 2, 4, 128, 8)
+  MOE_V(kFP8, 2, 256, 0, 256, 2, 4, 128, 24)
+  MOE_V(kFP8, 1, 256, 6, 256, 2, 4)
+  MOE_V(kFP8, 2, 256, 6, 256, 2, 4, 128, 8)
   MOE_V(kFP8, 1, 128, 0, 256, 2, 4)
   MOE_V(kFP8, 2, 128, 0, 256, 2, 4)
   MOE_V(kFP8, 1, 128, 1, 256, 2, 2)
