@@ -335,7 +335,10 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
     from mixture_experts_layer_softmax_amd.inputs import make_inputs
 
     _say(f"{cfg.name}: drawing inputs")
-    inp = make_inputs(cfg, device="cuda")
+    # (a line per 64 experts: under a counter-collecting profiler the draw
+    # of a 256-expert layer runs for minutes)
+    inp = make_inputs(cfg, device="cuda",
+                      progress=lambda n, i, ne: _say(f"{cfg.name}: {n} {i}/{ne} experts drawn"))
     t_pack = time.perf_counter()
     if args.stated_weights:  # the layouts the workload states, read without a pack
         packed = {"W1t": inp["W1"], "W3t": inp["W3"], "W2t": inp["W2"]}

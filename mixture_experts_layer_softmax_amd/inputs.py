@@ -107,7 +107,7 @@ def unpack_mxfp4(packed: torch.Tensor) -> torch.Tensor:
 
 
 def make_inputs(cfg: MoEConfig, device="cpu", seed: int | None = None,
-                experts=None) -> dict:
+                experts=None, progress=None) -> dict:
     """Draw the layer inputs of `cfg` on `device`.
 
     Returns a dict with x, gate_w, bias (or None), W1, W3, W2 and, for FP8
@@ -118,6 +118,8 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: int | None = None,
     `experts` (optional) limits the weight draw to those expert indices
     (others stay zero) -- a test
     convenience only; the draws of the listed experts do not change.
+    `progress` (optional) is called as progress(name, experts_drawn, NE)
+    after every 64 experts of each weight matrix.
     """
     seed = cfg.seed if seed is None else seed
     T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
@@ -145,6 +147,8 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: int | None = None,
             # every expert is drawn in order so that a subset draw reproduces
             # the full draw bit for bit
             w = _normal((K, N), 0.02, g, device)
+            if progress is not None and ((e + 1) % 64 == 0 or e + 1 == NE):
+                progress(name, e + 1, NE)
             if e not in wanted:
                 continue
             if cfg.w_dtype == MXFP4:
