@@ -85,11 +85,18 @@ bool supported_layout(const moe_problem& p) {
   return p.w_layout == MOE_W_NK || p.w_dtype != MOE_MXFP4;
 }
 
-// Bytes per element of Y, the expert outputs per slot: fp32, except bf16 for
-// MXFP4 weights (their 5e-2 tolerance leaves room for the rounding, and Y is
-// the largest buffer of those layers; on FP8 layers the rounding would use up
-// most of the margin the quantisation of h leaves, so they keep fp32).
-int y_bytes(const moe_problem& p) { return p.w_dtype == MOE_MXFP4 ? 2 : 4; }
+// Format of Y, the expert outputs per slot: fp32 on fp32 layers; bf16 for
+// MXFP4 weights (their 5e-2 tolerance leaves room for the rounding); on bf16
+// and FP8 layers fp16 codes under a power-of-two scale per 32 columns (one
+// exponent byte per group, in its own region).  Y is the largest buffer of
+// the layer and the combine's whole stream; an 11-bit significand keeps its
+// rounding at most 2^-12 of each term, far inside either tolerance.
+int y_format(const moe_problem& p) {
+  if (p.w_dtype == MOE_MXFP4) return moe::kYBF16;
+  if (p.w_dtype == MOE_FP8_E4M3 || p.act_dtype == MOE_BF16) return moe::kYF16E;
+  return moe::kYF32;
+}
+int y_bytes(const moe_problem& p) { return y_format(p) == moe::kYF32 ? 4 : 2; }
 
 // Floats per row of the FP8 activation scales inside the workspace (x and
 // h: one per 128 elements): padded to a multiple of 4, so that the GEMM
@@ -121,7 +128,7 @@ bool supported_shape(const moe_problem* p) {
 struct Layout {
   size_t logits, ids, w, table, counts, offsets, slot_token, slot_k, token_slot;
   size_t tm_e, tm_row0, tm_rows, tm_misc;
-  size_t xq, sx, hs, h, y;
+  size_t xq, sx, hs, h, y, ye;
   size_t ring_ctrl;  // ring layout: queue[8], l1_done[max_mtiles], l2_done[max_mtiles], err
   size_t total;
   int bm;
@@ -174,6 +181,7 @@ Layout make_layout(const moe_problem& p, bool ring = false) {
   else
     L.h = take(static_cast<size_t>(rows) * p.f * (fp8 || mx ? 1 : esize(p.act_dtype)));
   L.y = take(static_cast<size_t>(y_bytes(p)) * rows * p.d);
+  L.ye = take(y_format(p) == moe::kYF16E ? static_cast<size_t>(rows) * (p.d / 32) : 0);
   L.ring_ctrl = take(ring ? sizeof(int32_t) * ring_ctrl_words(L.max_mtiles) : 0);
   L.total = off;
   return L;
@@ -465,6 +473,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   g2.K = p->f;
   g2.N = p->d;
   g2.C = at<uint8_t>(ws, L.y);
+  g2.ce = y_format(*p) == moe::kYF16E ? at<uint8_t>(ws, L.ye) : nullptr;
   g2.sc = nullptr;
   g2.tm = tm;
   g2.n_tiles_n = static_cast<int>(ceil_div(p->d, moe::gemm_tile_n(2, gdt, L.bm, wkn)));
@@ -507,7 +516,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* gate_w,
   mark(5);
 
   // 6. combine
-  moe::launch_combine(at<uint8_t>(ws, L.y), y_bytes(*p) == 2, w, token_slot, out, T, d, k,
+  moe::launch_combine(at<uint8_t>(ws, L.y), y_format(*p), at<uint8_t>(ws, L.ye), w, token_slot,
+                      out, T, d, k,
                       p->n_shared, p->out_dtype == MOE_BF16, stream);
   mark(6);
 

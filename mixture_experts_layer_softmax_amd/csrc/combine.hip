@@ -27,10 +27,12 @@ namespace {
 // CU; the accumulation itself stays j ascending, then the shared experts.
 constexpr int kCombineGroup = 8;
 
-// Y rows are fp32, or bf16 (Y_BF16: FP8 and MXFP4 layers); either way every
-// term is widened to fp32 before its fma.
-template <bool OUT_BF16, bool Y_BF16>
+// Y rows are fp32, bf16 (MXFP4 layers) or fp16 codes with an exponent byte
+// per 32 columns (bf16 and FP8 layers); every term is widened to fp32 (code
+// * 2^x is exact) before its fma.
+template <bool OUT_BF16, int YF>
 __global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ Yv,
+                                                      const uint8_t* __restrict__ ye,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ token_slot,
                                                       void* __restrict__ out, int T, int d, int k,
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ 
       for (int u = 0; u < kCombineGroup; ++u) {
         if (j0 + u < n) {
           const size_t o = static_cast<size_t>(s_slot[j0 + u]) * d + c;
-          if constexpr (Y_BF16) {
+          if constexpr (YF == kYBF16) {
             const u32x4 raw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Yv) + o);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -66,6 +68,16 @@ __global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ 
               y0[u][2 * q + 1] = __uint_as_float(raw[q] & 0xffff0000u);
               y1[u][2 * q] = __uint_as_float(raw[2 + q] << 16);
               y1[u][2 * q + 1] = __uint_as_float(raw[2 + q] & 0xffff0000u);
+            }
+          } else if constexpr (YF == kYF16E) {
+            typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+            const h8 raw = *reinterpret_cast<const h8*>(static_cast<const uint16_t*>(Yv) + o);
+            // the 8 columns lie in one 32-column group (c is a multiple of 8)
+            const float sc = exp2_int(static_cast<int>(ye[o / 32]) - 127);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              y0[u][q] = static_cast<float>(raw[q]) * sc;
+              y1[u][q] = static_cast<float>(raw[4 + q]) * sc;
             }
           } else {
             const float* row = static_cast<const float*>(Yv) + o;
@@ -113,18 +125,23 @@ __global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ 
 
 }  // namespace
 
-void launch_combine(const void* Y, bool y_bf16, const float* w, const int32_t* token_slot,
-                    void* out, int T, int d, int k, int S, bool out_bf16, hipStream_t s) {
+void launch_combine(const void* Y, int y_format, const uint8_t* ye, const float* w,
+                    const int32_t* token_slot, void* out, int T, int d, int k, int S,
+                    bool out_bf16, hipStream_t s) {
   if (T <= 0) return;
   const int threads = std::min(1024, std::max(64, (d / 8 + 63) / 64 * 64));
-  if (out_bf16 && y_bf16)
-    combine_kernel<true, true><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
-  else if (out_bf16)
-    combine_kernel<true, false><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
-  else if (y_bf16)
-    combine_kernel<false, true><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
-  else
-    combine_kernel<false, false><<<T, threads, 0, s>>>(Y, w, token_slot, out, T, d, k, S);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(T), dim3(threads), 0, s, Y, ye, w, token_slot, out, T, d, k, S);
+  };
+  if (out_bf16) {
+    if (y_format == kYF16E) go(combine_kernel<true, kYF16E>);
+    else if (y_format == kYBF16) go(combine_kernel<true, kYBF16>);
+    else go(combine_kernel<true, kYF32>);
+  } else {
+    if (y_format == kYF16E) go(combine_kernel<false, kYF16E>);
+    else if (y_format == kYBF16) go(combine_kernel<false, kYBF16>);
+    else go(combine_kernel<false, kYF32>);
+  }
 }
 
 }  // namespace moe

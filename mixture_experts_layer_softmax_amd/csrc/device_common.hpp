@@ -38,6 +38,30 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 // encoder below on every finite input (checked on the GPU against the
 // oracle's encoder, including every rounding midpoint); a NaN input gives
 // the code of +-448.
+// Two fp32 values as an fp16 pair (low half first), each rounded to nearest
+// even by the hardware conversion.
+__device__ __forceinline__ uint32_t f32x2_to_f16x2_rne(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, h2));
+}
+
+// Exponent x of the power-of-two scale of a group of expert outputs stored
+// as fp16: with m the group's largest magnitude, m * 2^-x lies in
+// [2^14, 2^15), so the group stays inside fp16's normal range (values down
+// to 2^-29 m keep the full 11-bit significand); 0 for an all-zero group.
+// Clamped to [-126, 126] so that 2^x and 2^-x are normal floats.
+__device__ __forceinline__ int fp16_group_exponent(float m) {
+  if (!(m > 0.0f)) return 0;
+  const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xffu) - 127;  // floor(log2 m)
+  return min(126, max(-126, e - 14));
+}
+
+// 2^x as a float, for |x| <= 126.
+__device__ __forceinline__ float exp2_int(int x) {
+  return __uint_as_float(static_cast<uint32_t>(x + 127) << 23);
+}
+
 __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
   auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
   int r = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);

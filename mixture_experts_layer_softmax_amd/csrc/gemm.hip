@@ -100,10 +100,13 @@ struct Geo {
   // streams better than one of 8 (one refills while the other starts a task)
   static constexpr int NS_CAP = BM <= 32 ? ((MX && BM == 16) ? 4 : 8) : 6;
   static constexpr int NS = NS0 > NS_CAP ? NS_CAP : NS0;
-  // phase-2 output element: Y is fp32, except bf16 (RNE) for MXFP4 weights,
-  // whose 5e-2 tolerance leaves room for the rounding (the FP8 layer's
-  // measured error does not: it keeps fp32)
-  static constexpr int YES = (DT == kMX4) ? 2 : 4;
+  // phase-2 output element: Y is fp32 on fp32 layers, bf16 (RNE) on MXFP4
+  // layers, whose 5e-2 tolerance leaves room for that rounding, and on bf16
+  // and FP8 layers fp16 codes under a power-of-two scale per 32 columns (an
+  // 11-bit significand: its rounding adds at most 2^-12 of each term)
+  static constexpr int YES = (DT == kF32) ? 4 : 2;
+  static constexpr bool YF16 = DT == kBF16 || DT == kFP8;
+  static_assert(PHASE == 1 || !YF16 || (BN / WN) % 32 == 0, "fp16 Y groups of 32 inside a wave");
   static constexpr int EPI =  // output staging, one pass per wave row
       (BM / WM) * ((PHASE == 1) ? BN / 2 : BN) * ((PHASE == 1) ? ES : YES);
   static constexpr int RING = NS * STAGE;
@@ -580,7 +583,7 @@ do {                                                                            
     wait_lgkmcnt0();
   }
 
-  constexpr int LOOP = SCHED & 7;  // main-loop schedule; bit 3: direct Y stores
+  constexpr int LOOP = SCHED & 7;  // main-loop schedule
   if constexpr (LOOP == 4) {
     // Two MFMA k-steps per stage (128-byte rows, two stages), the second
     // k-step's fragments read while the first one's MFMAs run: row by row
@@ -1032,28 +1035,6 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
         if (lg == 0) red[wn * BM + wm * WTM + 16 * i + l16] = m;
       }
     }
-    // fp32 Y straight from the accumulators (SCHED bit 3): each lane holds
-    // four consecutive columns of one row, so a store writes 16 rows x 64
-    // bytes; no staging through LDS and no barrier
-    constexpr bool kDirectY = (SCHED & 8) && PHASE == 2 && G::YES == 4;
-    if constexpr (kDirectY) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int lr = wm * WTM + 16 * i + l16;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t col = col0 + wn * WTN + 16 * j + 4 * lg;
-          if (lr < rows && col < N) {
-            f32x4* dst = reinterpret_cast<f32x4*>(g.C + (static_cast<int64_t>(crow + lr) * N + col) * 4);
-            if (g.stream_c)
-              __builtin_nontemporal_store(acc[i][j], dst);
-            else
-              *dst = acc[i][j];
-          }
-        }
-      }
-      return;
-    }
     __syncthreads();  // every wave is done with the ring (and the row maxima are in)
 
     for (int pass = 0; pass < PASSES; ++pass) {
@@ -1067,13 +1048,43 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
             for (int j = 0; j < TN; ++j)
               *reinterpret_cast<f32x4*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 4)) =
                   acc[i][j];
-          } else if constexpr (PHASE == 2) {
+          } else if constexpr (PHASE == 2 && MX) {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
               u32x2 v;
               v.x = f32x2_to_bf16x2_rne(acc[i][j][0], acc[i][j][1]);
               v.y = f32x2_to_bf16x2_rne(acc[i][j][2], acc[i][j][3]);
               *reinterpret_cast<u32x2*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 2)) = v;
+            }
+          } else if constexpr (PHASE == 2) {
+            // fp16 Y under a power-of-two scale per 32 columns of the row
+            // (two 16-column fragments, held by the four lanes of this row):
+            // the group amax sets the exponent, then fp16 codes of Y * 2^-x
+#pragma unroll
+            for (int gq = 0; gq < TN / 2; ++gq) {
+              float m = 0.f;
+#pragma unroll
+              for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) m = fmaxf(m, fabsf(acc[i][2 * gq + pp][q4]));
+              m = fmaxf(m, __shfl_xor(m, 16, 64));
+              m = fmaxf(m, __shfl_xor(m, 32, 64));
+              const int x = fp16_group_exponent(m);
+              const float rs = exp2_int(-x);
+#pragma unroll
+              for (int pp = 0; pp < 2; ++pp) {
+                const int j = 2 * gq + pp;
+                u32x2 v;
+                v.x = f32x2_to_f16x2_rne(acc[i][j][0] * rs, acc[i][j][1] * rs);
+                v.y = f32x2_to_f16x2_rne(acc[i][j][2] * rs, acc[i][j][3] * rs);
+                *reinterpret_cast<u32x2*>(stage + st_off(r, (wn * WTN + 16 * j + 4 * lg) * 2)) = v;
+              }
+              // (one byte per row and group, straight from the lanes: staging
+              // them through LDS measured slower on the FP8 layer)
+              const int64_t gcol = col0 + wn * WTN + 32 * gq;
+              if (lg == 0 && lr < rows && gcol < N)
+                g.ce[static_cast<int64_t>(crow + lr) * (N / 32) + gcol / 32] =
+                    static_cast<uint8_t>(x + 127);
             }
           } else if constexpr (MX) {
             // h = SiLU(gate) * up; each block of 32 h columns (two 16-column
@@ -1476,11 +1487,9 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kBF16, 1, 16, 0, 256, 1, 4)
   MOE_V(kBF16, 2, 16, 0, 256, 1, 4)
   MOE_V(kFP8, 1, 256, 0, 256, 2, 4, 128, 16)
-  // FP8 W2 stores its fp32 Y straight from the accumulators (SCHED bit 3):
-  // 5.43 against 5.57 ms on the FP8 prefill layer; on bf16 layers no gain
-  MOE_V(kFP8, 2, 256, 0, 256, 2, 4, 128, 24)
+  MOE_V(kFP8, 2, 256, 0, 256, 2, 4, 128, 16)
   MOE_V(kFP8, 1, 256, 6, 256, 2, 4)
-  MOE_V(kFP8, 2, 256, 6, 256, 2, 4, 128, 8)
+  MOE_V(kFP8, 2, 256, 6, 256, 2, 4)
   MOE_V(kFP8, 1, 128, 0, 256, 2, 4)
   MOE_V(kFP8, 2, 128, 0, 256, 2, 4)
   MOE_V(kFP8, 1, 128, 1, 256, 2, 2)
@@ -1534,7 +1543,7 @@ int dispatch_kn(int phase, int dtype, int bm, F&& f) {
   MOE_KN(kBF16, 1, 16, 256, 1, 4)
   MOE_KN(kBF16, 2, 16, 256, 1, 4)
   MOE_KN(kFP8, 1, 256, 256, 2, 4)
-  MOE_KN(kFP8, 2, 256, 256, 2, 4, 8)
+  MOE_KN(kFP8, 2, 256, 256, 2, 4)
   MOE_KN(kFP8, 1, 128, 256, 2, 4)
   MOE_KN(kFP8, 2, 128, 256, 2, 4)
   MOE_KN(kFP8, 1, 64, 256, 1, 4)

@@ -57,8 +57,10 @@ struct GemmArgs {
   int64_t K;              // contraction length (elements)
   int64_t N;              // output columns: f (phase 1) or d (phase 2)
   // outputs
-  uint8_t* C;             // h [slots][f] (phase 1) or Y [slots][d] (phase 2: fp32, or
-                          // bf16 for MXFP4 weights)
+  uint8_t* C;             // h [slots][f] (phase 1) or Y [slots][d] (phase 2: fp32 for fp32
+                          // layers, bf16 for MXFP4, else fp16 codes under the scales in ce)
+  uint8_t* ce;            // phase 2, fp16 Y: exponent byte x + 127 per 32 columns
+                          // [slots][d/32]; Y = code * 2^x
   float* sc;              // phase 1 h scales: FP8 [slots][sc_stride]; MX E8M0 bytes [slots][f/32]
   int sc_stride;          // FP8: floats per h scale row, a multiple of 4
   TileMap tm;
@@ -129,9 +131,12 @@ int launch_gemm_ring(const GemmArgs& g1, const GemmArgs& g2, const RingArgs& r, 
 void launch_zero(int32_t* p, int64_t n, hipStream_t s);
 // Column tiles per m-tile for a phase (depends on the kernel variant).
 int gemm_tile_n(int phase, int dtype, int bm, bool wkn);
-// Y [T*k + S*T][d], fp32 or (y_bf16) bf16.
-void launch_combine(const void* Y, bool y_bf16, const float* w, const int32_t* token_slot,
-                    void* out, int T, int d, int k, int S, bool out_bf16, hipStream_t s);
+// Formats of Y [T*k + S*T][d]: fp32, bf16, or fp16 codes with one exponent
+// byte x + 127 per 32 columns in ye [T*k + S*T][d/32] (Y = code * 2^x).
+enum YFormat { kYF32 = 0, kYBF16 = 1, kYF16E = 2 };
+void launch_combine(const void* Y, int y_format, const uint8_t* ye, const float* w,
+                    const int32_t* token_slot, void* out, int T, int d, int k, int S,
+                    bool out_bf16, hipStream_t s);
 void launch_pack(int E, int64_t K, int64_t N, int elem_bytes, const void* src, void* dst,
                  hipStream_t s);
 
