@@ -152,6 +152,25 @@ def test_forward_every_tile_height(name, block_m):
     _outputs_ok(cfg, out, ref, f"bm={block_m}")
 
 
+@pytest.mark.parametrize("log2_scale", [12, -12])
+@pytest.mark.parametrize("name", ["prefill_bf16_r", "prefill_fp8_r"])
+def test_expert_outputs_far_outside_fp16_range(name, log2_scale):
+    # x times 2^s (exact in bf16) scales h and the expert outputs Y by about
+    # 2^2s: near 2^24 their magnitudes lie far above fp16's largest finite
+    # value, near 2^-24 far below its smallest normal one.  Y is stored as
+    # fp16 codes under a power-of-two scale per 32 columns, which must keep
+    # both within the layer's bar (relative to the output RMS).
+    cfg = REDUCED[name]
+    say("fp16 Y range", name, log2_scale)
+    inp = gpu_inputs(cfg)
+    inp["x"] = inp["x"] * (2.0 ** log2_scale)
+    ref, _, _ = oracle_forward_rows(cfg, inp, np.arange(cfg.T))
+    amax = float(np.abs(ref).max())
+    assert (amax > 2.0 ** 20) if log2_scale > 0 else (amax < 2.0 ** -14), amax  # the premise
+    out32 = _forward(cfg, inp, out_dtype=F32)
+    _outputs_ok(cfg, out32, ref, f"x * 2^{log2_scale}, fp32 out")
+
+
 @pytest.mark.parametrize("E,K,N,dt", [(3, 130, 70, torch.uint8), (2, 64, 4100, torch.int16),
                                       (1, 1000, 33, torch.int32), (5, 1, 1, torch.int16),
                                       (4, 7168, 256, torch.int16)])
