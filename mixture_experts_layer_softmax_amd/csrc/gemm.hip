@@ -9,7 +9,9 @@
 // is applied in registers and h is rounded once to the activation format
 // (bf16 RNE, fp32, or FP8 with a fresh 1x128 scale: the epilogue role
 // "SwiGLU + amax + quantise" on that page, section 2.1).
-// Phase 2 (W2): h rows of an m-tile times the expert's down weights, fp32 Y.
+// Phase 2 (W2): h rows of an m-tile times the expert's down weights: Y per
+// slot, fp32 on fp32 layers, bf16 on MXFP4 layers, else fp16 codes under a
+// power-of-two scale per 32 columns.
 //
 // Scheduling: a persistent grid sized from occupancy pulls (m-tile, n-tile)
 // tasks from integer atomic counters -- a work-conserving device-side tile
@@ -22,7 +24,7 @@
 //
 // Operand pipeline: an NS-stage LDS ring.  Each stage holds KRB bytes of the
 // contraction axis for the BM activation rows and the BN weight rows, filled
-// by direct global->LDS loads (global_load_lds_dwordx4: lane L of a wave
+// by direct global->LDS loads (buffer_load_dwordx4 ... lds: lane L of a wave
 // writes 16 bytes at the wave's LDS base + 16 L) issued NS-1 stages ahead, so
 // up to (NS-1) stages of both operands are in flight per CU without passing
 // through VGPRs.  Each wave waits only for its own loads of the stage it is
