@@ -585,7 +585,7 @@ do {                                                                            
     wait_lgkmcnt0();
   }
 
-  constexpr int LOOP = SCHED & 7;  // main-loop schedule
+  constexpr int LOOP = SCHED & 7;  // main-loop schedule; bit 3: fp16 Y stored from registers
   if constexpr (LOOP == 4) {
     // Two MFMA k-steps per stage (128-byte rows, two stages), the second
     // k-step's fragments read while the first one's MFMAs run: row by row
@@ -1037,6 +1037,48 @@ _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                
         if (lg == 0) red[wn * BM + wm * WTM + 16 * i + l16] = m;
       }
     }
+    // SCHED bit 3, fp16 Y: stored straight from the accumulators, without
+    // staging or barriers -- each lane holds four consecutive columns (8
+    // bytes) of one row, so one store writes 16 rows x 32 bytes
+    if constexpr ((SCHED & 8) && PHASE == 2 && G::YF16) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (wm * WTM + 16 * i >= rows) break;  // padding rows are not stored
+        const int lr = wm * WTM + 16 * i + l16;
+#pragma unroll
+        for (int gq = 0; gq < TN / 2; ++gq) {
+          float m = 0.f;
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) m = fmaxf(m, fabsf(acc[i][2 * gq + pp][q4]));
+          m = fmaxf(m, __shfl_xor(m, 16, 64));
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          const int x = fp16_group_exponent(m);
+          const float rs = exp2_int(-x);
+          const int64_t gcol = col0 + wn * WTN + 32 * gq;
+          if (lr < rows && gcol < N) {
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const int j = 2 * gq + pp;
+              u32x2 v;
+              v.x = f32x2_to_f16x2_rne(acc[i][j][0] * rs, acc[i][j][1] * rs);
+              v.y = f32x2_to_f16x2_rne(acc[i][j][2] * rs, acc[i][j][3] * rs);
+              u32x2* dst = reinterpret_cast<u32x2*>(
+                  g.C + (static_cast<int64_t>(crow + lr) * N + gcol + 16 * pp + 4 * lg) * 2);
+              if (g.stream_c)
+                __builtin_nontemporal_store(v, dst);
+              else
+                *dst = v;
+            }
+            if (lg == 0)
+              g.ce[static_cast<int64_t>(crow + lr) * (N / 32) + gcol / 32] =
+                  static_cast<uint8_t>(x + 127);
+          }
+        }
+      }
+      return;
+    }
     __syncthreads();  // every wave is done with the ring (and the row maxima are in)
 
     for (int pass = 0; pass < PASSES; ++pass) {
@@ -1460,14 +1502,16 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   if (dtype == DT && phase == P && bm == BM_ && var == VAR)        \
     return f(Variant<DT, P, BM_, BN_, WM_, WN_ __VA_OPT__(, ) __VA_ARGS__>{});
   // SCHED bit 4: MFMAs of the padding rows skipped per wave (2.09 against
-  // 2.14 ms on the skewed layer, 17.49 against 17.54 ms on the FP8 one)
+  // 2.14 ms on the skewed layer, 17.49 against 17.54 ms on the FP8 one);
+  // bit 3: W2 stores its fp16 Y from registers (W2 0.682 against 0.696 ms
+  // on the skewed layer, 0.292 against 0.2975 on the prefill one)
   MOE_V(kBF16, 1, 256, 0, 256, 2, 4, 128, 16)
-  MOE_V(kBF16, 2, 256, 0, 256, 2, 4, 128, 16)
+  MOE_V(kBF16, 2, 256, 0, 256, 2, 4, 128, 24)
   // measured alternatives of the 256 x 256 schedule (slower, or no faster,
   // on the prefill and skewed layers): 3 = DMA interleaved with the MFMAs,
   // 4 = ping-pong of the two waves of each SIMD, 5 = the second k-step's
   // fragments read during the first one's MFMAs, 6 = every fragment row's
-  // MFMAs run
+  // MFMAs run, 7 = W2's Y staged through LDS
   MOE_V(kBF16, 1, 256, 3, 256, 2, 4, 128, 2)
   MOE_V(kBF16, 2, 256, 3, 256, 2, 4, 128, 2)
   MOE_V(kBF16, 1, 256, 4, 256, 2, 4, 128, 1)
@@ -1476,6 +1520,7 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kBF16, 2, 256, 5, 256, 2, 4, 128, 4)
   MOE_V(kBF16, 1, 256, 6, 256, 2, 4)
   MOE_V(kBF16, 2, 256, 6, 256, 2, 4)
+  MOE_V(kBF16, 2, 256, 7, 256, 2, 4, 128, 16)
   MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 2, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 1, 128, 1, 256, 1, 4)
@@ -1489,9 +1534,10 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kBF16, 1, 16, 0, 256, 1, 4)
   MOE_V(kBF16, 2, 16, 0, 256, 1, 4)
   MOE_V(kFP8, 1, 256, 0, 256, 2, 4, 128, 16)
-  MOE_V(kFP8, 2, 256, 0, 256, 2, 4, 128, 16)
+  MOE_V(kFP8, 2, 256, 0, 256, 2, 4, 128, 24)
   MOE_V(kFP8, 1, 256, 6, 256, 2, 4)
   MOE_V(kFP8, 2, 256, 6, 256, 2, 4)
+  MOE_V(kFP8, 2, 256, 7, 256, 2, 4, 128, 16)
   MOE_V(kFP8, 1, 128, 0, 256, 2, 4)
   MOE_V(kFP8, 2, 128, 0, 256, 2, 4)
   MOE_V(kFP8, 1, 128, 1, 256, 2, 2)
