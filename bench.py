@@ -158,7 +158,9 @@ def _stage_work(cfg, counts):
     n = cfg.T * (cfg.k + cfg.n_shared)
     w13 = dict(flops=4.0 * n * cfg.d * cfg.f,
                bytes=hit * 2.0 * cfg.d * cfg.f * es + cfg.T * cfg.d * ae + n * cfg.f * he)
-    ye = 2.0 if cfg.w_dtype == 3 else 4.0  # Y: bf16 on MXFP4 layers, else fp32
+    # Y: fp32 on fp32 layers, bf16 on MXFP4 layers, else fp16 codes with one
+    # exponent byte per 32 columns
+    ye = {0: 4.0, 1: 2.0 + 1 / 32, 2: 2.0 + 1 / 32, 3: 2.0}[cfg.w_dtype]
     w2 = dict(flops=2.0 * n * cfg.d * cfg.f,
               bytes=hit * 1.0 * cfg.d * cfg.f * es + n * cfg.f * he + n * cfg.d * ye)
     return {"gemm_w13_swiglu": w13, "gemm_w2": w2, "hit_experts": hit}
