@@ -28,7 +28,11 @@ sys.path.insert(0, ROOT)
 # fp8 rate (the scaled MFMA with one FP8 operand), so MXFP4 layers use it too
 PEAK_TFLOPS = {0: 157.3, 1: 2516.6, 2: 5033.2, 3: 5033.2}
 PEAK_HBM_GBPS = 8000.0
-STAGES = ["gate", "quant_x", "permute", "gemm_w13_swiglu", "gemm_w2", "combine"]
+# stage name -> the pair of moe_debug stage events around it (event 1, between
+# the gate and its activation quantisation, is not recorded: the quantisation
+# runs inside the gate kernel, and an event there only adds its own cost)
+STAGES = {"gate": (0, 2), "permute": (2, 3), "gemm_w13_swiglu": (3, 4), "gemm_w2": (4, 5),
+          "combine": (5, 6)}
 
 
 def _hip():
@@ -208,6 +212,12 @@ def _cpu_baseline(cfg, inp, out_gpu, out32_gpu, target_s):
     n = int(min(cfg.T, max(n0, n0 * target_s / max(t_probe, 1e-3))))
     rows = np.sort(rng.choice(cfg.T, size=n, replace=False))
     ref, secs = run(rows)
+    if secs < 0.5 * target_s and n < cfg.T:
+        # the probe overstates the per-token cost when each expert's fixed
+        # cost dominates a few tokens: size the sample again from this run
+        n = int(min(cfg.T, n * target_s / max(secs, 1e-3)))
+        rows = np.sort(rng.choice(cfg.T, size=n, replace=False))
+        ref, secs = run(rows)
     sel = torch.as_tensor(rows, device=out_gpu.device)
     got = out_gpu[sel].double().cpu().numpy()
     rms = math.sqrt(float(np.mean(ref ** 2))) or 1.0
@@ -327,9 +337,12 @@ def _say(msg):
 
 
 def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
-    """Time `steps` whole-layer forwards of cfg after `warmup` untimed ones;
-    returns the per-workload record (tokens/s, roofline of the dominant GEMM
-    launch, stage breakdown, CPU-oracle baseline and parity sample)."""
+    """Time `steps` whole-layer forwards of cfg after `warmup` untimed ones.
+    Returns the per-workload record (tokens/s, roofline of the dominant GEMM
+    launch, stage breakdown) and a function that later adds the CPU-oracle
+    baseline and parity sample to it (no GPU work) and frees the workload's
+    device memory: the GPU phases of several workloads can then run back to
+    back, with no host-only stretch between them."""
     import numpy as np
     import torch
 
@@ -401,11 +414,11 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
     # per-stage breakdown (untimed): every stage boundary recorded
     nbreak = min(steps, 10)
     for i in range(nbreak):
-        step({"stage_events": evs[i]})
+        step({"stage_events": [None if j == 1 else v for j, v in enumerate(evs[i])]})
     torch.cuda.synchronize()
     stage_ms = {}
-    for s_, name in enumerate(STAGES, start=1):
-        stage_ms[name] = float(np.mean([_elapsed(hip, e[s_ - 1], e[s_]) for e in evs[:nbreak]]))
+    for name, (a, b) in STAGES.items():
+        stage_ms[name] = float(np.mean([_elapsed(hip, e[a], e[b]) for e in evs[:nbreak]]))
     gpu_ms = _elapsed(hip, evs[0][0], evs[nbreak - 1][-1]) / nbreak
     per_step = np.array([_elapsed(hip, e[0], e[-1]) for e in evs[:nbreak]])
     step_stats = {"median": float(np.median(per_step)), "min": float(per_step.min()),
@@ -461,11 +474,6 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
         step(None, out32, p32)
         torch.cuda.synchronize()
 
-    cpu = parity = None
-    if not args.no_cpu_baseline:
-        _say(f"{cfg.name}: CPU oracle baseline (~{cpu_seconds:.0f} s)")
-        cpu, parity = _cpu_baseline(cfg, inp, out, out32, cpu_seconds)
-
     dtype = {0: "f32", 1: "bf16", 2: "fp8e4m3", 3: "mxfp4xmxfp8"}[cfg.w_dtype]
     rec = {
         "value": value, "unit": "tokens/s", "steps": steps, "warmup": warmup,
@@ -473,17 +481,28 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
                    "top_k": cfg.k, "n_shared": cfg.n_shared, "parallelism": "single GPU",
                    "gemms": "one launch, h ring" if args.ring else "two launches"},
-        "roofline": roof, "cpu_baseline": cpu, "stages_ms": stage_ms, "layer": layer,
-        "sustained_clock_mhz": sustained, "parity_sample": parity,
+        "roofline": roof, "cpu_baseline": None, "stages_ms": stage_ms, "layer": layer,
+        "sustained_clock_mhz": sustained, "parity_sample": None,
         "weight_pack_ms": None if args.stated_weights else pack_s * 1e3,
         "weights": "stated [K][N] layout, no pack" if args.stated_weights else "packed [N][K]",
     }
-    del inp, packed, ws, out, out32
-    _free(torch)
-    return rec
+    del packed, ws
+    held = {"inp": inp, "out": out, "out32": out32}
+
+    def finish():
+        if not args.no_cpu_baseline:
+            _say(f"{cfg.name}: CPU oracle baseline (~{cpu_seconds:.0f} s)")
+            rec["cpu_baseline"], rec["parity_sample"] = _cpu_baseline(
+                cfg, held["inp"], held["out"], held["out32"], cpu_seconds)
+        held.clear()
+        _free(torch)
+        return rec
+
+    return rec, finish
 
 
-# the other stated workloads, measured after the headline one in a default run
+# the other stated workloads of a default run; their GPU phases run after the
+# headline one's (see main)
 OTHER_CONFIGS = ["tiny_fp32", "decode_bf16", "skewed_bf16", "prefill_fp8"]
 
 
@@ -533,7 +552,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="measure only --workload (by default the other stated workloads "
-                         "follow the headline one, each in a block of its own)")
+                         "are measured too, after the headline one, each in a block of "
+                         "its own)")
     ap.add_argument("--block-m", type=int, default=0, help="expert tile height (0 = auto)")
     ap.add_argument("--stated-weights", action="store_true",
                     help="pass the weights in the layouts the workloads state ([E][d][f], "
@@ -556,7 +576,7 @@ def main():
     if args.trace_summary:
         wls = [args.workload]
         if not args.no_other_configs and not args.ring and args.workload == "prefill_bf16":
-            wls += OTHER_CONFIGS
+            wls += OTHER_CONFIGS  # the order main() runs their GPU phases in
         print(trace_summary(args.trace_summary, args.warmup, args.steps, wls))
         return
     if args.blas_calibration:
@@ -577,15 +597,26 @@ def main():
     B.load()
     hip = _hip()
     copy_gbps = _copy_gbps(torch)
-    head = measure(cfg, args, args.steps, args.warmup, args.cpu_seconds, hip, copy_gbps)
-
-    others = {}
+    # GPU phases first, back to back, the headline workload first; then the
+    # CPU-oracle baselines, which use no GPU.  The shader clock a workload
+    # runs at depends on what ran before it (it climbs over the first ~50 ms
+    # of a heavy load and sits lower after the FP8 layer's run), so the
+    # headline layer runs on a GPU that nothing else has loaded in this
+    # process, and every workload gets exactly `warmup` untimed steps of its
+    # own before its `steps` timed ones.
+    head, head_finish = measure(cfg, args, args.steps, args.warmup, args.cpu_seconds, hip,
+                                copy_gbps)
+    pending = []
     if not args.no_other_configs and not args.ring and args.workload == "prefill_bf16":
         for name in OTHER_CONFIGS:
-            rec = measure(CONFIGS[name], args, args.steps, args.warmup, args.other_cpu_seconds,
-                          hip, copy_gbps)
-            rec.pop("layer", None)
-            others[name] = rec
+            pending.append((name, *measure(CONFIGS[name], args, args.steps, args.warmup,
+                                           args.other_cpu_seconds, hip, copy_gbps)))
+    head_finish()
+    others = {}
+    for name, rec, finish in pending:
+        finish()
+        rec.pop("layer", None)
+        others[name] = rec
 
     device = _device_info()
     device["sustained_clock_mhz"] = head.pop("sustained_clock_mhz")
