@@ -4,7 +4,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PROGRAMS = ["mfma_accumulation", "fp8_convert", "gemm_loop_bench", "mfma_rate"]
+PROGRAMS = ["mfma_accumulation", "fp8_convert", "gemm_loop_bench", "mfma_rate", "stream_rate"]
 
 
 def build() -> None:
