@@ -1610,6 +1610,8 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kBF16, 1, 256, 8, 256, 2, 4, 128, 24)
   MOE_V(kBF16, 2, 256, 7, 256, 2, 4, 128, 16)
   // 9 = the activation rows in a three-slot ring, requested two stages ahead
+  // (2-5 % fewer shader clocks per launch, but the GEMM then holds a clock
+  // lower by about as much: no faster)
   MOE_V(kBF16, 1, 256, 9, 256, 2, 4, 128, 48)
   MOE_V(kBF16, 2, 256, 9, 256, 2, 4, 128, 56)
   MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
