@@ -508,22 +508,6 @@ __device__ __forceinline__ void gemm_task(const GemmArgs& g, const int mt, const
     return BM * KRB + h * HALF + kn_off<ES, HB>(k, c0 * ES + colbyte);
   };
 
-  // SCHED bit 5 (bf16, two stages): the activation rows get a ring of
-  // three slots and the weight rows one of two, filling the 160 KB of LDS:
-  // the (gathered) activation rows of stage ks + 2 are requested during
-  // stage ks, a stage earlier than the weight rows of stage ks + 1
-  constexpr bool AAHEAD = (SCHED & 32) != 0;
-  static_assert(!AAHEAD || (DT == kBF16 && NS == 2 && !WKN && (SCHED & 7) == 0 &&
-                            3 * BM * KRB + 2 * BN * KRBW <= kLdsBytes &&
-                            G::EPI <= 3 * BM * KRB),
-                "three-slot activation ring: bf16, two stages, default loop");
-  auto a_slot = [&](int ks) { return lds + (ks % 3) * (BM * KRB); };
-  auto b_slot = [&](int ks) { return lds + 3 * BM * KRB + (ks & 1) * (BN * KRBW); };
-  int my_a_loads = 0;  // activation DMAs this wave issues per stage
-#pragma unroll
-  for (int j = 0; j < G::AW; ++j)
-    if (wave + NW * j < G::ABLK) ++my_a_loads;
-
 // DMA of stage KS: the activation rows (and FP8 row scales) when DO_A, the
 // weight rows when DO_B
 #define MOE_ISSUE_PART(KS, DO_A, DO_B)                                                   \
@@ -531,10 +515,9 @@ do {                                                                            
   uint8_t* st_ = lds + ((KS) % NS) * G::STAGE;                                         \
   const uint32_t ko_ = static_cast<uint32_t>(KS) * KRB;                                \
   if (DO_A) {                                                                          \
-    uint8_t* sa_ = AAHEAD ? a_slot(KS) : st_;                                          \
     _Pragma("unroll") for (int j = 0; j < G::AW; ++j) {                                \
       const int q = wave + NW * j;                                                     \
-      if (G::ABLK % NW == 0 || q < G::ABLK) dma_a(oa[j] + ko_, sa_ + q * 1024);          \
+      if (G::ABLK % NW == 0 || q < G::ABLK) dma_a(oa[j] + ko_, st_ + q * 1024);          \
     }                                                                                  \
     if (DT == kFP8 && scale_dma && (KS) % G::SGROUP == 0)                              \
       dma16b(rsa, sa_off + (KS) * 4,                                                   \
@@ -542,11 +525,10 @@ do {                                                                            
   }                                                                                    \
   if (DO_B) {                                                                          \
     const uint32_t kw_ = static_cast<uint32_t>(KS) * w_kstride;                        \
-    uint8_t* sb_ = AAHEAD ? b_slot(KS) : st_ + BM * KRB;                                \
     _Pragma("unroll") for (int j = 0; j < G::BW; ++j) {                                \
       const int q = wave + NW * j;                                                     \
       if (G::BBLK % NW == 0 || q < G::BBLK)                                            \
-        dma_b((up_mask >> j) & 1u, ob[j] + kw_, sb_ + q * 1024);                         \
+        dma_b((up_mask >> j) & 1u, ob[j] + kw_, st_ + BM * KRB + q * 1024);              \
     }                                                                                  \
     if (MX) {                                                                          \
       _Pragma("unroll") for (int u = 0; u < G::SCW; ++u) {                             \
@@ -594,9 +576,6 @@ do {                                                                            
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < ksteps) MOE_ISSUE(p);
-  if constexpr (AAHEAD) {
-    if (1 < ksteps) MOE_ISSUE_PART(1, true, false);  // issued after stage 0's weights
-  }
   if constexpr (DT == kFP8) {
     // (the previous task's reads of these columns ended before its epilogue
     // barrier; the first stage barrier below publishes the new ones)
@@ -827,36 +806,22 @@ do {                                                                            
         (DT == kFP8 && scale_dma && ahead > 0)
             ? (ks + ahead) / G::SGROUP - ks / G::SGROUP
             : 0;
-    if constexpr (AAHEAD) {
-      // issued after this stage's weight rows: the activation rows of stage
-      // ks + 1 (when there is one), which may stay in flight
-      if (ks + 1 < ksteps) wait_vmcnt(my_a_loads);
-      else wait_vmcnt(0);
-    } else {
-      wait_vmcnt(ahead * my_loads + groups_ahead);
-    }
+    wait_vmcnt(ahead * my_loads + groups_ahead);
     ring_barrier();
     if (ks == k_pull) kpull();
     // bf16 stages hold two MFMA k-steps: the weight rows of the next stage
     // are requested after the first one, which spreads the DMA's LDS writes
     // over the stage instead of piling them onto its first fragment reads
-    // (three-slot activation ring: the weight rows of stage ks + 1 first,
-    // then, after the first k-step, the activation rows of stage ks + 2)
     constexpr bool kSplitDma = (DT == kBF16) && (KRB / 64 == 2);
     const bool refill = ks + NS - 1 < ksteps;
-    const bool refill_a2 = AAHEAD && ks + 2 < ksteps;
-    if constexpr (AAHEAD) {
-      if (refill) MOE_ISSUE_PART(ks + 1, false, true);
-    } else {
-      if (refill) MOE_ISSUE_PART(ks + NS - 1, true, !kSplitDma);
-    }
+    if (refill) MOE_ISSUE_PART(ks + NS - 1, true, !kSplitDma);
     float sb_cur0 = 0.f, sb_cur1 = 0.f;  // FP8 weight block scales of this k-step
     if constexpr (DT == kFP8) {
       sb_cur0 = wsc[wsc_col * kWscMax + ks];
       if (PHASE == 1) sb_cur1 = wsc[kWscMax + ks];
     }
-    const uint8_t* Ab = AAHEAD ? a_slot(ks) : lds + (ks % NS) * G::STAGE;
-    const uint8_t* Bb = AAHEAD ? b_slot(ks) : Ab + BM * KRB;
+    const uint8_t* Ab = lds + (ks % NS) * G::STAGE;
+    const uint8_t* Bb = Ab + BM * KRB;
     const uint8_t* Sb = Bb + BN * KRBW;  // per-stage scale dwords
     // A wave whose rows are all padding skips the step; a partly valid
     // wave computes its padding rows too (their results are never stored),
@@ -865,11 +830,7 @@ do {                                                                            
     if constexpr (DT == kBF16) {
 #pragma unroll
       for (int kk = 0; kk < KRB / 64; ++kk) {
-        if constexpr (AAHEAD) {
-          if (kk == 1 && refill_a2) MOE_ISSUE_PART(ks + 2, true, false);
-        } else {
-          if (kSplitDma && kk == 1 && refill) MOE_ISSUE_PART(ks + NS - 1, false, true);
-        }
+        if (kSplitDma && kk == 1 && refill) MOE_ISSUE_PART(ks + NS - 1, false, true);
         if (!compute) continue;
         bf16x8 wf[TN];
 #pragma unroll
@@ -1312,9 +1273,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs g) 
   // the task hand-over slot lives in the last bytes of the ring: it is
   // written after every wave is done with the ring and read before the
   // first DMA of the task can reach that stage slot
-  // (three-slot activation ring: the end of the second weight slot, which
-  // the task's first stage barrier precedes the refill of)
-  int& s_task = *reinterpret_cast<int*>(lds + ((SCHED & 32) ? kLdsBytes : G::RING) - 16);
+  int& s_task = *reinterpret_cast<int*>(lds + G::RING - 16);
 
   const int tid = threadIdx.x;
   const uint64_t clk0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
@@ -1547,9 +1506,7 @@ template <int DT, int PHASE, int BM, int BN, int WM, int WN, int KRB = (DT == kF
           int SCHED = 0, bool WKN = false>
 struct Variant {
   static constexpr int kThreads = WM * WN * 64;
-  static constexpr int lds_bytes() {
-    return (SCHED & 32) ? kLdsBytes : Geo<DT, PHASE, BM, BN, WM, WN, KRB>::LDS;
-  }
+  static constexpr int lds_bytes() { return Geo<DT, PHASE, BM, BN, WM, WN, KRB>::LDS; }
   static int launch(const GemmArgs& a, hipStream_t s) {
     auto kern = grouped_gemm_kernel<DT, PHASE, BM, BN, WM, WN, KRB, SCHED, WKN>;
     static int grid = 0;
@@ -1609,11 +1566,6 @@ int dispatch_var(int phase, int dtype, int bm, int var, F&& f) {
   MOE_V(kBF16, 2, 256, 6, 256, 2, 4)
   MOE_V(kBF16, 1, 256, 8, 256, 2, 4, 128, 24)
   MOE_V(kBF16, 2, 256, 7, 256, 2, 4, 128, 16)
-  // 9 = the activation rows in a three-slot ring, requested two stages ahead
-  // (2-5 % fewer shader clocks per launch, but the GEMM then holds a clock
-  // lower by about as much: no faster)
-  MOE_V(kBF16, 1, 256, 9, 256, 2, 4, 128, 48)
-  MOE_V(kBF16, 2, 256, 9, 256, 2, 4, 128, 56)
   MOE_V(kBF16, 1, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 2, 128, 0, 128, 2, 2)
   MOE_V(kBF16, 1, 128, 1, 256, 1, 4)
