@@ -340,9 +340,10 @@ def measure(cfg, args, steps, warmup, cpu_seconds, hip, copy_gbps):
     """Time `steps` whole-layer forwards of cfg after `warmup` untimed ones.
     Returns the per-workload record (tokens/s, roofline of the dominant GEMM
     launch, stage breakdown) and a function that later adds the CPU-oracle
-    baseline and parity sample to it (no GPU work) and frees the workload's
-    device memory: the GPU phases of several workloads can then run back to
-    back, with no host-only stretch between them."""
+    baseline and parity sample to it (it launches no kernel of the library;
+    it copies the rows it needs to the host) and frees the workload's device
+    memory: the GPU phases of several workloads can then run back to back,
+    with no host-only stretch between them."""
     import numpy as np
     import torch
 
@@ -598,7 +599,7 @@ def main():
     hip = _hip()
     copy_gbps = _copy_gbps(torch)
     # GPU phases first, back to back, the headline workload first; then the
-    # CPU-oracle baselines, which use no GPU.  The shader clock a workload
+    # CPU-oracle baselines, which launch no kernels.  The shader clock a workload
     # runs at depends on what ran before it (it climbs over the first ~50 ms
     # of a heavy load and sits lower after the FP8 layer's run), so the
     # headline layer runs on a GPU that nothing else has loaded in this
